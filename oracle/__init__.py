@@ -1,0 +1,1 @@
+"""fp64 CPU oracle (test infrastructure only; see oracle.py)."""

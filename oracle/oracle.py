@@ -1,0 +1,262 @@
+"""fp64 CPU oracle for the Mamba-2 selective SSM recurrence -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The GPU product path never touches it and
+it shares no code with the HIP library.
+
+The heavy loops live in ``ssm_oracle.c`` (plain sequential C, fp64, OpenMP over
+independent (batch, head) or (batch, group) units); this file compiles it with
+gcc, marshals numpy arrays, and holds the few scalar helpers that the pages
+state as small examples:
+
+* ``checkpoint_budget`` -- "Nemotron 3 Ultra: replaying a rounded state",
+  section "An error budget for checkpoint writes": after each checkpoint write
+  the allowance is the previous one shrunk by L**n (n tokens since the last
+  write) plus one write allowance delta.
+* ``grid_schedule_run`` -- same page, section "Fewer writes can leave a larger
+  error": the scalar update s' = a*s + u with round-half-even writes onto the
+  integer grid at the end of every chunk of the schedule.
+* ``state_bytes`` / ``kv_bytes`` -- same page, section "Counting the state and
+  attention cache": payload counts of the recurrent state and of the KV cache.
+* ``replay_additive`` -- same page, section "Recovering the state by replay":
+  the s' = s + u example of replaying the pending buffer from a checkpoint.
+
+Parity of every function here is pinned by ``tests/test_oracle_*.py`` against
+closed forms, a textbook filter (scipy.signal.lfilter), central finite
+differences, brute force, and the pages' worked values under ``tests/golden``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from fractions import Fraction
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ssm_oracle.c with gcc (fp64, no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            i64, vp, u64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64
+            lib.oracle_fwd.argtypes = [i64] * 7 + [vp] * 10
+            lib.oracle_fwd.restype = None
+            lib.oracle_bwd.argtypes = [i64] * 6 + [vp] * 16
+            lib.oracle_bwd.restype = None
+            lib.oracle_decode_step.argtypes = [i64] * 5 + [vp] * 8
+            lib.oracle_decode_step.restype = None
+            lib.oracle_splitmix64_output.argtypes = [u64, u64]
+            lib.oracle_splitmix64_output.restype = u64
+            lib.oracle_hash32.argtypes = [u64, u64, u64]
+            lib.oracle_hash32.restype = ctypes.c_uint32
+            lib.oracle_sr16_one.argtypes = [ctypes.c_float, ctypes.c_uint32]
+            lib.oracle_sr16_one.restype = ctypes.c_uint16
+            lib.oracle_sr16.argtypes = [vp, vp, i64, u64, u64, u64]
+            lib.oracle_sr16.restype = None
+            lib.oracle_half_to_double_array.argtypes = [vp, vp, i64]
+            lib.oracle_half_to_double_array.restype = None
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _f32(a):
+    """Contiguous float32 numpy array (the SR16 rule reads float32 values)."""
+    if hasattr(a, "detach"):  # torch tensor: bf16 -> f32 is exact
+        a = a.detach().to("cpu").float().contiguous().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _f64(a):
+    """Exact widening to a contiguous float64 numpy array (bf16/fp16/fp32 in)."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: bf16 -> f64 is exact
+        a = a.detach().to("cpu").double().contiguous().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(x, B, C, dt, A, D, h0=None, chunk=None, want_chunk_states=False):
+    """Sequential forward.  x [Bsz,T,H,P], B/C [Bsz,T,G,N], dt [Bsz,T,H], A/D [H].
+
+    Returns dict with y [Bsz,T,H,P], h_final [Bsz,H,P,N] and, when
+    ``want_chunk_states``, chunk_states [Bsz,H,nc,P,N] (state entering each
+    chunk of ``chunk`` tokens).  All float64.
+    """
+    x, B, C, dt, A, D = (_f64(v) for v in (x, B, C, dt, A, D))
+    h0 = _f64(h0)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    L = int(chunk) if chunk else T
+    assert L >= 1 and H % G == 0
+    nc = (T + L - 1) // L
+    y = np.empty((Bsz, T, H, P), np.float64)
+    hf = np.empty((Bsz, H, P, N), np.float64)
+    cs = np.empty((Bsz, H, nc, P, N), np.float64) if want_chunk_states else None
+    _load().oracle_fwd(Bsz, T, H, P, N, G, L, _p(x), _p(B), _p(C), _p(dt), _p(A), _p(D),
+                       _p(h0), _p(y), _p(hf), _p(cs))
+    out = {"y": y, "h_final": hf}
+    if want_chunk_states:
+        out["chunk_states"] = cs
+    return out
+
+
+def bwd(x, B, C, dt, A, D, dy, h0=None, dh_final=None):
+    """Reverse sweep; returns dict dx, dB, dC, ddt, dA, dD, dh0 (float64)."""
+    x, B, C, dt, A, D, dy = (_f64(v) for v in (x, B, C, dt, A, D, dy))
+    h0, dh_final = _f64(h0), _f64(dh_final)
+    Bsz, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    out = {
+        "dx": np.empty((Bsz, T, H, P), np.float64),
+        "dB": np.empty((Bsz, T, G, N), np.float64),
+        "dC": np.empty((Bsz, T, G, N), np.float64),
+        "ddt": np.empty((Bsz, T, H), np.float64),
+        "dA": np.empty((H,), np.float64),
+        "dD": np.empty((H,), np.float64),
+        "dh0": np.empty((Bsz, H, P, N), np.float64),
+    }
+    _load().oracle_bwd(Bsz, T, H, P, N, G, _p(x), _p(B), _p(C), _p(dt), _p(A), _p(D),
+                       _p(h0), _p(dy), _p(dh_final), _p(out["dx"]), _p(out["dB"]),
+                       _p(out["dC"]), _p(out["ddt"]), _p(out["dA"]), _p(out["dD"]),
+                       _p(out["dh0"]))
+    return out
+
+
+def decode_step(state, x, B, C, dt, A, D):
+    """One token on a float64 state [Bsz,H,P,N] (updated in place); returns y [Bsz,H,P]."""
+    assert state.dtype == np.float64 and state.flags["C_CONTIGUOUS"]
+    x, B, C, dt, A, D = (_f64(v) for v in (x, B, C, dt, A, D))
+    Bsz, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    y = np.empty((Bsz, H, P), np.float64)
+    _load().oracle_decode_step(Bsz, H, P, N, G, _p(state), _p(x), _p(B), _p(C), _p(dt),
+                               _p(A), _p(D), _p(y))
+    return y
+
+
+def replay(ckpt, x, B, C, dt, A, D, t0, r):
+    """Run r tokens (t0 .. t0+r-1 of full-length inputs) from a saved state.
+
+    This is the forward from a given state: the retained prepared inputs are
+    applied again in order ("Recovering the state by replay").  Returns dict
+    with y [Bsz,r,H,P] and h_final [Bsz,H,P,N].
+    """
+    sl = slice(t0, t0 + r)
+    return fwd(_f64(x)[:, sl], _f64(B)[:, sl], _f64(C)[:, sl], _f64(dt)[:, sl], A, D,
+               h0=ckpt)
+
+
+# ----------------------------------------------------------------------------
+# counter-based entropy and stochastic rounding to binary16
+# ----------------------------------------------------------------------------
+
+def splitmix64_output(seed: int, k: int) -> int:
+    return int(_load().oracle_splitmix64_output(seed & (2**64 - 1), k & (2**64 - 1)))
+
+
+def hash32(seed: int, ckpt: int, elem: int) -> int:
+    return int(_load().oracle_hash32(seed & (2**64 - 1), ckpt, elem))
+
+
+def sr16_one(v: float, u: int) -> int:
+    return int(_load().oracle_sr16_one(ctypes.c_float(v), ctypes.c_uint32(u)))
+
+
+def sr16(v, seed: int, ckpt: int, elem_offset: int = 0):
+    """SR16 bits (uint16 array, same shape) of float32 values v."""
+    v = _f32(v)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_sr16(_p(v), _p(out), v.size, seed & (2**64 - 1), ckpt, elem_offset)
+    return out
+
+
+def half_bits_to_double(bits):
+    bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(bits.shape, np.float64)
+    _load().oracle_half_to_double_array(_p(bits), _p(out), bits.size)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# scalar helpers from the TorchLean page's small examples (exact rationals)
+# ----------------------------------------------------------------------------
+
+def checkpoint_budget(L, delta, e0, chunk_lengths):
+    """Worst-case allowance after each checkpoint write: E <- L**n * E + delta."""
+    e = Fraction(e0)
+    out = []
+    for n in chunk_lengths:
+        e = Fraction(L) ** n * e + Fraction(delta)
+        out.append(e)
+    return out
+
+
+def _round_half_even(v: Fraction) -> Fraction:
+    fl = v.numerator // v.denominator
+    rem = v - fl
+    if rem > Fraction(1, 2):
+        return Fraction(fl + 1)
+    if rem < Fraction(1, 2):
+        return Fraction(fl)
+    return Fraction(fl if fl % 2 == 0 else fl + 1)
+
+
+def grid_schedule_run(a, s0, chunks):
+    """s' = a*s + u over each chunk, then a nearest-even write onto the integers."""
+    s = Fraction(s0)
+    for chunk in chunks:
+        for u in chunk:
+            s = Fraction(a) * s + Fraction(u)
+        s = _round_half_even(s)
+    return s
+
+
+def replay_additive(checkpoint, pending, suffix=()):
+    """Replay for the transition s' = s + u: the observed state, then the suffix."""
+    s = checkpoint
+    for u in pending:
+        s = s + u
+    observed = s
+    for u in suffix:
+        s = s + u
+    return observed, s
+
+
+def state_bytes(blocks, heads, value_dim, state_dim, bytes_per_entry):
+    return blocks * heads * value_dim * state_dim * bytes_per_entry
+
+
+def kv_bytes(attn_blocks, tokens, kv_heads, width, bytes_per_entry):
+    """Keys and values (two tensors) for every attention block and token."""
+    return attn_blocks * tokens * 2 * kv_heads * width * bytes_per_entry
