@@ -1,0 +1,347 @@
+// abi.cpp -- the extern "C" surface declared in include/ssm.h: argument
+// validation (all of it before the first enqueue), workspace carving, and
+// dispatch to the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <initializer_list>
+
+#include "../../include/ssm.h"
+#include "launch.hpp"
+
+using namespace ssm;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+size_t esize(ssm_dtype t) { return t == SSM_F32 ? 4 : 2; }
+
+// Alignment contract: state-shaped float arrays are read as float4 (16 B);
+// B and C rows are read 4 elements at a time (4 * element size); on the MFMA
+// path x, y, dy, dx rows are read 16 B at a time; everything else is scalar.
+bool check_align(std::initializer_list<const void *> vec16, std::initializer_list<const void *> bc,
+                 std::initializer_list<const void *> rows, std::initializer_list<const void *> scal,
+                 ssm_dtype t, bool mfma) {
+    for (const void *p : vec16)
+        if (p && !aligned(p, 16)) return false;
+    for (const void *p : bc)
+        if (p && !aligned(p, mfma ? 16 : 4 * esize(t))) return false;
+    for (const void *p : rows)
+        if (p && !aligned(p, mfma ? 16 : esize(t))) return false;
+    for (const void *p : scal)
+        if (p && !aligned(p, 4)) return false;
+    return true;
+}
+
+bool valid_dtype(ssm_dtype t) { return t == SSM_F32 || t == SSM_BF16; }
+
+// Dims every call shares.  seqlen/batch may be zero (no tokens / no sequences).
+ssm_status check_dims(const ssm_dims *d, bool need_chunk) {
+    if (d == nullptr) return SSM_ERR_NULL;
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+        d->ngroups < 1)
+        return SSM_ERR_DIMS;
+    if (d->nheads % d->ngroups != 0) return SSM_ERR_DIMS;
+    if (need_chunk && d->chunk < 1) return SSM_ERR_DIMS;
+    if (d->batch * d->nheads > (int64_t(1) << 31) - 1) return SSM_ERR_DIMS;
+    if (d->nheads > 65535 || d->headdim > 65535) return SSM_ERR_DIMS;
+    return SSM_OK;
+}
+
+// Token-serial kernels: dstate in {16,32,64,128,256}; a 256-thread workgroup
+// holds 8 rows per thread, i.e. headdim <= 8 * 256 / (dstate / 4).
+bool serial_supported(const ssm_dims *d) {
+    const int64_t N = d->dstate;
+    if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return false;
+    return d->headdim <= 8 * 256 / (N / 4);
+}
+
+bool mfma_path(const ssm_dims *d, ssm_dtype t) {
+#ifdef SSM_WITH_MFMA
+    return t == SSM_BF16 && d->headdim == 64 && d->dstate == 128 && d->chunk % 64 == 0 &&
+           d->nheads <= 4096;
+#else
+    (void)d;
+    (void)t;
+    return false;
+#endif
+}
+
+int64_t nchunks_of(const ssm_dims *d) { return (d->seqlen + d->chunk - 1) / d->chunk; }
+
+struct Carve {
+    char *base;
+    size_t off = 0;
+    template <typename T> T *take(size_t count) {
+        T *p = reinterpret_cast<T *>(base + off);
+        off += round_up(count * sizeof(T));
+        return p;
+    }
+};
+
+size_t bwd_ws_bytes(const ssm_dims *d, ssm_dtype t) {
+    const size_t B = d->batch, T = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate;
+    const size_t nc = nchunks_of(d);
+    if (mfma_path(d, t)) {
+        return round_up(B * H * nc * P * N * sizeof(float)) + round_up(B * T * H * sizeof(float)) +
+               round_up(B * H * nc * 4 * sizeof(float)) + 2 * round_up(B * H * nc * sizeof(double));
+    }
+    const size_t L = d->chunk < d->seqlen ? d->chunk : (d->seqlen > 0 ? d->seqlen : 1);
+    return round_up(B * H * (L + 1) * P * N * sizeof(float)) +
+           2 * round_up(B * T * H * N * sizeof(float)) + 2 * round_up(B * H * sizeof(double));
+}
+
+size_t replay_ws_bytes(const ssm_dims *d, int64_t r) {
+    return 2 * round_up(static_cast<size_t>(r) * d->batch * d->nheads * 4 * sizeof(float));
+}
+
+hipError_t fill(float *p, int64_t n, hipStream_t s) { return launch_fill(p, n, 0.f, s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *ssm_status_string(ssm_status s) {
+    switch (s) {
+        case SSM_OK: return "SSM_OK";
+        case SSM_ERR_NULL: return "SSM_ERR_NULL: a required pointer is NULL";
+        case SSM_ERR_DIMS: return "SSM_ERR_DIMS: invalid dimensions";
+        case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: no kernel for these dimensions";
+        case SSM_ERR_DTYPE: return "SSM_ERR_DTYPE: unknown dtype";
+        case SSM_ERR_ALIGN: return "SSM_ERR_ALIGN: pointer not aligned as required";
+        case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
+        case SSM_ERR_HIP: return "SSM_ERR_HIP: HIP launch failed";
+    }
+    return "unknown ssm_status";
+}
+
+int ssm_uses_mfma_path(const ssm_dims *d, ssm_dtype dtype) {
+    if (check_dims(d, true) != SSM_OK) return 0;
+    return mfma_path(d, dtype) ? 1 : 0;
+}
+
+size_t ssm_workspace_bytes(const ssm_dims *d, ssm_dtype dtype, int which, int64_t r) {
+    if (!valid_dtype(dtype)) return static_cast<size_t>(-1);
+    if (which == SSM_WS_FWD) {
+        if (check_dims(d, true) != SSM_OK) return static_cast<size_t>(-1);
+        if (!mfma_path(d, dtype) && !serial_supported(d)) return static_cast<size_t>(-1);
+        return 0;
+    }
+    if (which == SSM_WS_BWD) {
+        if (check_dims(d, true) != SSM_OK) return static_cast<size_t>(-1);
+        if (!mfma_path(d, dtype) && !serial_supported(d)) return static_cast<size_t>(-1);
+        return bwd_ws_bytes(d, dtype);
+    }
+    if (which == SSM_WS_REPLAY) {
+        if (check_dims(d, false) != SSM_OK || r < 0 || !serial_supported(d))
+            return static_cast<size_t>(-1);
+        return replay_ws_bytes(d, r);
+    }
+    return static_cast<size_t>(-1);
+}
+
+ssm_status ssm_fwd_chunked(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                           const void *C, const float *dt, const float *A, const float *D,
+                           const float *h0, void *y, float *h_final, float *chunk_states,
+                           void *workspace, size_t ws_bytes, ssm_stream stream) {
+    ssm_status st = check_dims(d, true);
+    if (st != SSM_OK) return st;
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    const bool mfma = mfma_path(d, dtype);
+    if (!mfma && !serial_supported(d)) return SSM_ERR_UNSUPPORTED;
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if (tokens && (!x || !B || !C || !dt || !y)) return SSM_ERR_NULL;
+    if (!A || !D) return SSM_ERR_NULL;
+    if (!check_align({h0, h_final, chunk_states}, {B, C}, {x, y}, {dt, A, D}, dtype, mfma))
+        return SSM_ERR_ALIGN;
+    (void)workspace;
+    (void)ws_bytes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (d->batch == 0) return SSM_OK;
+    const int64_t PN = d->headdim * d->dstate;
+    if (d->seqlen == 0) {  // no tokens: the final state is the initial state
+        if (h_final) {
+            hipError_t e = h0 ? launch_copy(h_final, h0, d->batch * d->nheads * PN, s)
+                              : fill(h_final, d->batch * d->nheads * PN, s);
+            if (e != hipSuccess) return SSM_ERR_HIP;
+        }
+        return SSM_OK;
+    }
+    hipError_t e;
+    if (mfma) {
+        SsdFwdArgs a{};
+        a.Bsz = d->batch; a.T = d->seqlen; a.H = static_cast<int>(d->nheads);
+        a.G = static_cast<int>(d->ngroups); a.L = d->chunk; a.nchunks = nchunks_of(d);
+        a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.D = D; a.h0 = h0; a.y = y;
+        a.h_final = h_final; a.chunk_states = chunk_states;
+#ifdef SSM_WITH_MFMA
+        e = launch_ssd_fwd(a, s);
+#else
+        e = hipErrorNotSupported;
+#endif
+    } else {
+        ScanArgs a{};
+        a.Bsz = d->batch; a.T = d->seqlen; a.H = static_cast<int>(d->nheads);
+        a.P = static_cast<int>(d->headdim); a.N = static_cast<int>(d->dstate);
+        a.G = static_cast<int>(d->ngroups); a.t0 = 0; a.r = d->seqlen; a.L = d->chunk;
+        a.nchunks = nchunks_of(d); a.ckpt = h0; a.live = nullptr; a.state_out = h_final;
+        a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.D = D; a.y = y;
+        a.chunk_states = chunk_states;
+        e = launch_scan(a, dtype == SSM_BF16, false, s);
+    }
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                   const void *C, const float *dt, const float *A, const float *D,
+                   const float *chunk_states, const void *dy, const float *dh_final, void *dx,
+                   float *dB, float *dC, float *ddt, float *dA, float *dD, float *dh0,
+                   void *workspace, size_t ws_bytes, ssm_stream stream) {
+    ssm_status st = check_dims(d, true);
+    if (st != SSM_OK) return st;
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    const bool mfma = mfma_path(d, dtype);
+    if (!mfma && !serial_supported(d)) return SSM_ERR_UNSUPPORTED;
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    if (tokens && (!x || !B || !C || !dt || !chunk_states || !dy || !dx || !dB || !dC || !ddt))
+        return SSM_ERR_NULL;
+    if (!A || !D || !dA || !dD) return SSM_ERR_NULL;
+    if (!check_align({chunk_states, dh_final, dh0, workspace}, {B, C, dB, dC}, {x, dy, dx},
+                     {dt, A, D, ddt, dA, dD}, dtype, mfma))
+        return SSM_ERR_ALIGN;
+    const size_t need = tokens ? bwd_ws_bytes(d, dtype) : 0;
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return SSM_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t PN = d->headdim * d->dstate;
+    if (!tokens) {  // no tokens: zero parameter gradients, dh0 = dh_final
+        if (fill(dA, d->nheads, s) != hipSuccess || fill(dD, d->nheads, s) != hipSuccess)
+            return SSM_ERR_HIP;
+        if (dh0 && d->batch > 0) {
+            hipError_t e = dh_final ? launch_copy(dh0, dh_final, d->batch * d->nheads * PN, s)
+                                    : fill(dh0, d->batch * d->nheads * PN, s);
+            if (e != hipSuccess) return SSM_ERR_HIP;
+        }
+        return SSM_OK;
+    }
+    Carve cv{static_cast<char *>(workspace)};
+    hipError_t e;
+    const int64_t nc = nchunks_of(d);
+    if (mfma) {
+        SsdBwdArgs a{};
+        a.Bsz = d->batch; a.T = d->seqlen; a.H = static_cast<int>(d->nheads);
+        a.G = static_cast<int>(d->ngroups); a.L = d->chunk; a.nchunks = nc;
+        a.x = x; a.B = B; a.C = C; a.dy = dy; a.dt = dt; a.A = A; a.D = D;
+        a.chunk_states = chunk_states; a.dh_final = dh_final; a.dx = dx; a.dB = dB; a.dC = dC;
+        a.ddt = ddt; a.dA = dA; a.dD = dD; a.dh0 = dh0;
+        a.dstates = cv.take<float>(d->batch * d->nheads * nc * PN);
+        a.dlam = cv.take<float>(d->batch * d->seqlen * d->nheads);
+        a.lam_end = cv.take<float>(d->batch * d->nheads * nc * 4);
+        a.pA = cv.take<double>(d->batch * d->nheads * nc);
+        a.pD = cv.take<double>(d->batch * d->nheads * nc);
+#ifdef SSM_WITH_MFMA
+        e = launch_ssd_bwd(a, s);
+#else
+        e = hipErrorNotSupported;
+#endif
+    } else {
+        ScanBwdArgs a{};
+        a.Bsz = d->batch; a.T = d->seqlen; a.H = static_cast<int>(d->nheads);
+        a.P = static_cast<int>(d->headdim); a.N = static_cast<int>(d->dstate);
+        a.G = static_cast<int>(d->ngroups); a.L = d->chunk; a.nchunks = nc;
+        a.x = x; a.B = B; a.C = C; a.dy = dy; a.dt = dt; a.A = A; a.D = D;
+        a.chunk_states = chunk_states; a.dh_final = dh_final; a.dx = dx; a.dB = dB; a.dC = dC;
+        a.ddt = ddt; a.dA = dA; a.dD = dD; a.dh0 = dh0;
+        // the sweep rebuilds the states of one saved chunk at a time
+        const int64_t Lslab = d->chunk < d->seqlen ? d->chunk : d->seqlen;
+        a.slab_stride = (Lslab + 1) * PN;
+        a.slab = cv.take<float>(d->batch * d->nheads * a.slab_stride);
+        a.dB_part = cv.take<float>(d->batch * d->seqlen * d->nheads * d->dstate);
+        a.dC_part = cv.take<float>(d->batch * d->seqlen * d->nheads * d->dstate);
+        a.dA_part = cv.take<double>(d->batch * d->nheads);
+        a.dD_part = cv.take<double>(d->batch * d->nheads);
+        e = launch_scan_bwd(a, dtype == SSM_BF16, s);
+    }
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_decode_step(const ssm_dims *d, ssm_dtype dtype, float *state, const void *x,
+                           const void *B, const void *C, const float *dt, const float *A,
+                           const float *D, void *y, ssm_stream stream) {
+    ssm_status st = check_dims(d, false);
+    if (st != SSM_OK) return st;
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (!serial_supported(d)) return SSM_ERR_UNSUPPORTED;
+    if (d->batch > 0 && (!state || !x || !B || !C || !dt || !y)) return SSM_ERR_NULL;
+    if (!A || !D) return SSM_ERR_NULL;
+    if (!check_align({state}, {B, C}, {x, y}, {dt, A, D}, dtype, false)) return SSM_ERR_ALIGN;
+    if (d->batch == 0) return SSM_OK;
+    DecodeArgs a{};
+    a.Bsz = d->batch; a.H = static_cast<int>(d->nheads); a.P = static_cast<int>(d->headdim);
+    a.N = static_cast<int>(d->dstate); a.G = static_cast<int>(d->ngroups);
+    a.state = state; a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.D = D; a.y = y;
+    return launch_decode(a, dtype == SSM_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSM_OK
+               : SSM_ERR_HIP;
+}
+
+ssm_status ssm_checkpoint_sr16(const float *state, uint16_t *out, uint64_t n_elems,
+                               uint64_t seed, uint64_t ckpt_index, uint64_t elem_offset,
+                               ssm_stream stream) {
+    if (n_elems == 0) return SSM_OK;
+    if (!state || !out) return SSM_ERR_NULL;
+    if (!aligned(state, 4) || !aligned(out, 2)) return SSM_ERR_ALIGN;
+    const char *a0 = reinterpret_cast<const char *>(state);
+    const char *b0 = reinterpret_cast<const char *>(out);
+    if (a0 < b0 + n_elems * 2 && b0 < a0 + n_elems * 4) return SSM_ERR_DIMS;  // aliasing
+    Sr16Args a{state, out, n_elems, seed, ckpt_index, elem_offset};
+    return launch_sr16(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_replay(const ssm_dims *d, ssm_dtype dtype, const void *ckpt, ssm_dtype ckpt_dtype,
+                      float *state_out, const void *x, const void *B, const void *C,
+                      const float *dt, const float *A, const float *D, int64_t t0, int64_t r,
+                      void *y, const float *live_ckpt, float *drift_max, float *drift_mean,
+                      void *workspace, size_t ws_bytes, ssm_stream stream) {
+    ssm_status st = check_dims(d, false);
+    if (st != SSM_OK) return st;
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (ckpt_dtype != SSM_F32 && ckpt_dtype != SSM_F16) return SSM_ERR_DTYPE;
+    if (!serial_supported(d)) return SSM_ERR_UNSUPPORTED;
+    if (t0 < 0 || r < 0 || t0 + r > d->seqlen) return SSM_ERR_DIMS;
+    if (d->batch > 0 && (!ckpt || !state_out)) return SSM_ERR_NULL;
+    if (d->batch > 0 && r > 0 && (!x || !B || !C || !dt)) return SSM_ERR_NULL;
+    if (!A || !D) return SSM_ERR_NULL;
+    if (live_ckpt && r > 0 && (!drift_max || !drift_mean)) return SSM_ERR_NULL;
+    if (!check_align({ckpt, state_out, live_ckpt, workspace}, {B, C}, {x, y},
+                     {dt, A, D, drift_max, drift_mean}, dtype, false))
+        return SSM_ERR_ALIGN;
+    const size_t need = (live_ckpt && r > 0) ? replay_ws_bytes(d, r) : 0;
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (d->batch == 0) return SSM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Carve cv{static_cast<char *>(workspace)};
+    ScanArgs a{};
+    a.Bsz = d->batch; a.T = d->seqlen; a.H = static_cast<int>(d->nheads);
+    a.P = static_cast<int>(d->headdim); a.N = static_cast<int>(d->dstate);
+    a.G = static_cast<int>(d->ngroups); a.t0 = t0; a.r = r; a.L = 1; a.nchunks = 0;
+    a.ckpt = ckpt; a.live = (r > 0) ? live_ckpt : nullptr; a.state_out = state_out;
+    a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.D = D; a.y = y; a.chunk_states = nullptr;
+    const int64_t nwaves = d->batch * d->nheads * 4;
+    if (a.live) {
+        a.part_max = cv.take<float>(r * nwaves);
+        a.part_sum = cv.take<float>(r * nwaves);
+    }
+    hipError_t e = launch_scan(a, dtype == SSM_BF16, ckpt_dtype == SSM_F16, s);
+    if (e == hipSuccess && a.live) {
+        const double cnt = static_cast<double>(d->batch) * d->nheads * d->headdim * d->dstate;
+        e = launch_drift_reduce(a.part_max, a.part_sum, nwaves, r, 1.0 / cnt, drift_max,
+                                drift_mean, s);
+    }
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// launch.hpp -- argument blocks and host launchers of the gfx950 kernels
+// (internal to the library; the public surface is include/ssm.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+struct DecodeArgs {
+    int64_t Bsz;
+    int H, P, N, G;
+    float *state;
+    const void *x, *B, *C;
+    const float *dt, *A, *D;
+    void *y;
+};
+
+struct ScanArgs {
+    int64_t Bsz, T;      // T: token stride of x/B/C/dt/y (the full sequence length)
+    int H, P, N, G;
+    int64_t t0, r;       // tokens t0 .. t0+r-1
+    int64_t L, nchunks;  // chunk_states cadence (relative to t0)
+    const void *ckpt;    // initial state (float or binary16 bits) or nullptr = zero
+    const float *live;   // lockstep live copy or nullptr
+    float *state_out;
+    const void *x, *B, *C;
+    const float *dt, *A, *D;
+    void *y;
+    float *chunk_states;
+    float *part_max, *part_sum;  // [r][Bsz*H*4] per-wave drift partials
+};
+
+struct ScanBwdArgs {
+    int64_t Bsz, T;
+    int H, P, N, G;
+    int64_t L, nchunks;
+    const void *x, *B, *C, *dy;
+    const float *dt, *A, *D, *chunk_states, *dh_final;
+    void *dx;
+    float *dB, *dC, *ddt, *dA, *dD, *dh0;
+    // workspace
+    float *slab;            // [Bsz*H][slab_stride]: states of one chunk per head
+    int64_t slab_stride;    // (min(L, T) + 1) * P * N
+    float *dB_part, *dC_part;  // [Bsz, T, H, N]
+    double *dA_part, *dD_part;  // [Bsz*H]
+};
+
+struct Sr16Args {
+    const float *in;
+    uint16_t *out;
+    uint64_t n, seed, ckpt, offset;
+};
+
+// Chunked MFMA path (bf16 operands, P = 64, N = 128, chunk % 64 == 0).
+struct SsdFwdArgs {
+    int64_t Bsz, T;
+    int H, G;
+    int64_t L, nchunks;
+    const void *x, *B, *C;
+    const float *dt, *A, *D, *h0;
+    void *y;
+    float *h_final, *chunk_states;
+};
+
+struct SsdBwdArgs {
+    int64_t Bsz, T;
+    int H, G;
+    int64_t L, nchunks;
+    const void *x, *B, *C, *dy;
+    const float *dt, *A, *D, *chunk_states, *dh_final;
+    void *dx;
+    float *dB, *dC, *ddt, *dA, *dD, *dh0;
+    // workspace
+    float *dstates;   // [Bsz, H, nchunks, 64, 128]: gradient on the state leaving chunk c
+    float *dlam;      // [Bsz, T, H] d loss / d (within-chunk cumulative log-retention)
+    float *lam_end;   // [Bsz, H, nchunks, 4] per-tile partials of the chunk-end term
+    double *pA, *pD;  // [Bsz, H, nchunks] per-chunk partials of dA, dD
+};
+
+hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);
+hipError_t launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_scan(const ScanArgs &a, bool bf16, bool ckpt_f16, hipStream_t s);
+hipError_t launch_drift_reduce(const float *pm, const float *ps, int64_t nwaves, int64_t r,
+                               double inv_count, float *dmax, float *dmean, hipStream_t s);
+hipError_t launch_scan_bwd(const ScanBwdArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_sr16(const Sr16Args &a, hipStream_t s);
+hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s);
+hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s);
+
+}  // namespace ssm

@@ -1,0 +1,524 @@
+// recurrence.hip -- token-serial kernels of the selective SSM recurrence on gfx950:
+//   * decode step (one token, state streamed from HBM and written back in place)
+//   * replay / sequential scan (state held in registers across tokens; optional
+//     y, chunk-state saves, and a lockstep "live" copy with per-step drift)
+//   * exact-fp32 reverse sweep (the backward for dims or dtypes the chunked
+//     MFMA kernels do not serve)
+//
+// The per-token update is the coordinate formula of theorem updateHead_apply
+// ("Nemotron 3 Ultra: replaying a rounded state", section "The Mamba state
+// update"): s = exp(dt*A) * s + x[p] * (B[n] * dt), and the output reads the
+// updated state (section "Recovering the state by replay", the example whose
+// output is 12).  Decode and replay call the same row_step() with the same lane
+// mapping and the same reduction tree, so one replayed token equals one decode
+// call bit for bit (every rounding is pinned with explicit fmaf / __fmul_rn).
+//
+// Thread mapping (both kernels): a state row of N floats is covered by
+// LPR = N/4 lanes holding 4 consecutive coordinates each (16-byte accesses);
+// a 256-thread workgroup covers 256/LPR rows per pass and one (batch, head).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssm {
+
+// Update 4 consecutive coordinates of one row and return their part of C.s.
+__device__ __forceinline__ float row_step(float4 &s, float a, float xp, const float4 &bdt,
+                                          const float4 &c) {
+    s.x = fmaf(a, s.x, __fmul_rn(xp, bdt.x));
+    s.y = fmaf(a, s.y, __fmul_rn(xp, bdt.y));
+    s.z = fmaf(a, s.z, __fmul_rn(xp, bdt.z));
+    s.w = fmaf(a, s.w, __fmul_rn(xp, bdt.w));
+    float acc = __fmul_rn(c.x, s.x);
+    acc = fmaf(c.y, s.y, acc);
+    acc = fmaf(c.z, s.z, acc);
+    acc = fmaf(c.w, s.w, acc);
+    return acc;
+}
+
+// Same update without the read (for the lockstep live copy).
+__device__ __forceinline__ void row_update(float4 &s, float a, float xp, const float4 &bdt) {
+    s.x = fmaf(a, s.x, __fmul_rn(xp, bdt.x));
+    s.y = fmaf(a, s.y, __fmul_rn(xp, bdt.y));
+    s.z = fmaf(a, s.z, __fmul_rn(xp, bdt.z));
+    s.w = fmaf(a, s.w, __fmul_rn(xp, bdt.w));
+}
+
+// Sum over the LPR lanes of one row (fixed xor tree).
+template <int LPR>
+__device__ __forceinline__ float row_reduce(float acc) {
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    return acc;
+}
+
+__device__ __forceinline__ float retention(float dtv, float Ah) { return expf(__fmul_rn(dtv, Ah)); }
+
+__device__ __forceinline__ float4 scale4(const float4 &v, float s) {
+    return make_float4(__fmul_rn(v.x, s), __fmul_rn(v.y, s), __fmul_rn(v.z, s), __fmul_rn(v.w, s));
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one (batch, head) per workgroup, MAXR row passes unrolled so all
+// state loads are in flight before the arithmetic.
+// ---------------------------------------------------------------------------
+template <int N, int MAXR, typename T>
+__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+    constexpr int LPR = N / 4;
+    constexpr int RPW = 256 / LPR;
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
+    const int tid = threadIdx.x;
+    const int n0 = (tid % LPR) * 4;
+    const int r0 = tid / LPR;
+    const T *x = static_cast<const T *>(a.x);
+    const T *Bm = static_cast<const T *>(a.B);
+    const T *Cm = static_cast<const T *>(a.C);
+    float *st = a.state + static_cast<int64_t>(bh) * a.P * N;
+
+    float4 s[MAXR];
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+        const int p = r0 + i * RPW;
+        if (p < a.P) s[i] = *reinterpret_cast<const float4 *>(st + static_cast<int64_t>(p) * N + n0);
+    }
+    const float dtv = a.dt[bh];
+    const float av = retention(dtv, a.A[h]);
+    const float Dh = a.D[h];
+    const int64_t bgN = (static_cast<int64_t>(b) * a.G + g) * N + n0;
+    const float4 bdt = scale4(IO<T>::ld4(Bm, bgN), dtv);
+    const float4 c = IO<T>::ld4(Cm, bgN);
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+        const int p = r0 + i * RPW;
+        if (p < a.P) {
+            const float xp = IO<T>::ld(x, static_cast<int64_t>(bh) * a.P + p);
+            float acc = row_step(s[i], av, xp, bdt, c);
+            acc = row_reduce<LPR>(acc);
+            *reinterpret_cast<float4 *>(st + static_cast<int64_t>(p) * N + n0) = s[i];
+            if ((tid % LPR) == 0)
+                IO<T>::st(static_cast<T *>(a.y), static_cast<int64_t>(bh) * a.P + p,
+                          fmaf(Dh, xp, acc));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Token-serial scan / replay: state in registers across r tokens.
+// ---------------------------------------------------------------------------
+template <int N, int MAXR, typename T, typename CK, bool LIVE>
+__global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
+    constexpr int LPR = N / 4;
+    constexpr int RPW = 256 / LPR;
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
+    const int tid = threadIdx.x;
+    const int n0 = (tid % LPR) * 4;
+    const int r0 = tid / LPR;
+    const int64_t PN = static_cast<int64_t>(a.P) * N;
+    const T *x = static_cast<const T *>(a.x);
+    const T *Bm = static_cast<const T *>(a.B);
+    const T *Cm = static_cast<const T *>(a.C);
+    T *y = static_cast<T *>(a.y);
+
+    float4 s[MAXR];
+    float4 l[LIVE ? MAXR : 1];
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+        const int p = r0 + i * RPW;
+        s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (LIVE) l[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p < a.P) {
+            const int64_t off = bh * PN + static_cast<int64_t>(p) * N + n0;
+            if (a.ckpt != nullptr) {
+                const CK *ck = static_cast<const CK *>(a.ckpt);
+                if constexpr (sizeof(CK) == 4) {
+                    s[i] = *reinterpret_cast<const float4 *>(ck + off);
+                } else {
+                    const _Float16 *hk = reinterpret_cast<const _Float16 *>(ck + off);
+                    s[i] = make_float4(static_cast<float>(hk[0]), static_cast<float>(hk[1]),
+                                       static_cast<float>(hk[2]), static_cast<float>(hk[3]));
+                }
+            }
+            if constexpr (LIVE) l[i] = *reinterpret_cast<const float4 *>(a.live + off);
+        }
+    }
+    const float Ah = a.A[h];
+    const float Dh = a.D[h];
+    const int wave = tid / 64, lane = tid % 64;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+
+    for (int64_t k = 0; k < a.r; ++k) {
+        const int64_t t = a.t0 + k;
+        if (a.chunk_states != nullptr && (k % a.L) == 0) {
+            float *cs = a.chunk_states + (bh * a.nchunks + k / a.L) * PN;
+#pragma unroll
+            for (int i = 0; i < MAXR; ++i) {
+                const int p = r0 + i * RPW;
+                if (p < a.P) *reinterpret_cast<float4 *>(cs + static_cast<int64_t>(p) * N + n0) = s[i];
+            }
+        }
+        const int64_t bt = static_cast<int64_t>(b) * a.T + t;
+        const float dtv = a.dt[bt * a.H + h];
+        const float av = retention(dtv, Ah);
+        const int64_t bgN = (bt * a.G + g) * N + n0;
+        const float4 bdt = scale4(IO<T>::ld4(Bm, bgN), dtv);
+        const float4 c = IO<T>::ld4(Cm, bgN);
+        const int64_t xrow = (bt * a.H + h) * a.P;
+        float dmax = 0.f, dsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i) {
+            const int p = r0 + i * RPW;
+            if (p < a.P) {
+                const float xp = IO<T>::ld(x, xrow + p);
+                float acc = row_step(s[i], av, xp, bdt, c);
+                acc = row_reduce<LPR>(acc);
+                if (y != nullptr && (tid % LPR) == 0) IO<T>::st(y, xrow + p, fmaf(Dh, xp, acc));
+                if constexpr (LIVE) {
+                    row_update(l[i], av, xp, bdt);
+                    const float d0 = fabsf(s[i].x - l[i].x), d1 = fabsf(s[i].y - l[i].y);
+                    const float d2 = fabsf(s[i].z - l[i].z), d3 = fabsf(s[i].w - l[i].w);
+                    dmax = fmaxf(dmax, fmaxf(fmaxf(d0, d1), fmaxf(d2, d3)));
+                    dsum += (d0 + d1) + (d2 + d3);
+                }
+            }
+        }
+        if constexpr (LIVE) {
+            dmax = wave_max(dmax);
+            dsum = wave_sum(dsum);
+            if (lane == 0) {
+                const int64_t w = static_cast<int64_t>(bh) * 4 + wave;
+                a.part_max[k * nwaves + w] = dmax;
+                a.part_sum[k * nwaves + w] = dsum;
+            }
+        }
+    }
+    if (a.state_out != nullptr) {
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i) {
+            const int p = r0 + i * RPW;
+            if (p < a.P)
+                *reinterpret_cast<float4 *>(a.state_out + bh * PN + static_cast<int64_t>(p) * N + n0) = s[i];
+        }
+    }
+}
+
+// Fixed-order reduction of the per-wave drift partials: one thread per step.
+__global__ void drift_reduce_kernel(const float *part_max, const float *part_sum, int64_t nwaves,
+                                    int64_t r, double inv_count, float *drift_max,
+                                    float *drift_mean) {
+    const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (k >= r) return;
+    float m = 0.f;
+    double s = 0.0;
+    for (int64_t w = 0; w < nwaves; ++w) {
+        m = fmaxf(m, part_max[k * nwaves + w]);
+        s += static_cast<double>(part_sum[k * nwaves + w]);
+    }
+    drift_max[k] = m;
+    drift_mean[k] = static_cast<float>(s * inv_count);
+}
+
+// ---------------------------------------------------------------------------
+// Exact-fp32 reverse sweep, one (batch, head) per workgroup.  Per token, from
+// the last to the first ("Nemotron Kernels: From Inference To
+// Backpropagation", Kernel 1 backward: output path plus future path; branch
+// contributions add):
+//   gs += dy (outer) C;  dC_t += dy . s_t;  dx = D dy + dt (gs B);
+//   dB_t += dt (gs^T x);  ddt = x.(gs B) + a A <gs, s_{t-1}>;
+//   dA += a dt <gs, s_{t-1}>;  dD += dy . x;  gs *= a.
+// States of one chunk are rebuilt from chunk_states into a workspace slab.
+// dB/dC go to per-head partials that a second kernel sums over the group in
+// ascending head order.
+// ---------------------------------------------------------------------------
+template <int N, int MAXR, typename T>
+__global__ void __launch_bounds__(256) scan_bwd_kernel(ScanBwdArgs a) {
+    constexpr int LPR = N / 4;
+    constexpr int RPW = 256 / LPR;
+    __shared__ float red_c[RPW * N];
+    __shared__ float red_b[RPW * N];
+    __shared__ float red_w[3][4];
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
+    const int tid = threadIdx.x;
+    const int n0 = (tid % LPR) * 4;
+    const int r0 = tid / LPR;
+    const int wave = tid / 64, lane = tid % 64;
+    const int64_t PN = static_cast<int64_t>(a.P) * N;
+    const T *x = static_cast<const T *>(a.x);
+    const T *Bm = static_cast<const T *>(a.B);
+    const T *Cm = static_cast<const T *>(a.C);
+    const T *dy = static_cast<const T *>(a.dy);
+    T *dx = static_cast<T *>(a.dx);
+    float *slab = a.slab + static_cast<int64_t>(bh) * a.slab_stride;
+    const float Ah = a.A[h], Dh = a.D[h];
+
+    float4 gs[MAXR];
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+        const int p = r0 + i * RPW;
+        gs[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p < a.P && a.dh_final != nullptr)
+            gs[i] = *reinterpret_cast<const float4 *>(a.dh_final + bh * PN + static_cast<int64_t>(p) * N + n0);
+    }
+    double dA_acc = 0.0, dD_acc = 0.0;  // used by thread 0 only
+
+    for (int64_t c = a.nchunks - 1; c >= 0; --c) {
+        const int64_t tlo = c * a.L;
+        const int64_t thi = (tlo + a.L < a.T) ? tlo + a.L : a.T;
+        // rebuild the chunk's states: slab[k] = state after token tlo+k-1
+        float4 s[MAXR];
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i) {
+            const int p = r0 + i * RPW;
+            if (p < a.P) {
+                const int64_t off = static_cast<int64_t>(p) * N + n0;
+                s[i] = *reinterpret_cast<const float4 *>(a.chunk_states + (bh * a.nchunks + c) * PN + off);
+                *reinterpret_cast<float4 *>(slab + off) = s[i];
+            }
+        }
+        for (int64_t t = tlo; t < thi; ++t) {
+            const int64_t bt = static_cast<int64_t>(b) * a.T + t;
+            const float dtv = a.dt[bt * a.H + h];
+            const float av = retention(dtv, Ah);
+            const float4 bdt = scale4(IO<T>::ld4(Bm, (bt * a.G + g) * N + n0), dtv);
+#pragma unroll
+            for (int i = 0; i < MAXR; ++i) {
+                const int p = r0 + i * RPW;
+                if (p < a.P) {
+                    row_update(s[i], av, IO<T>::ld(x, (bt * a.H + h) * a.P + p), bdt);
+                    *reinterpret_cast<float4 *>(slab + (t - tlo + 1) * PN + static_cast<int64_t>(p) * N + n0) = s[i];
+                }
+            }
+        }
+        // reverse walk over the chunk (each thread reads only what it wrote)
+        for (int64_t t = thi - 1; t >= tlo; --t) {
+            const int64_t bt = static_cast<int64_t>(b) * a.T + t;
+            const float dtv = a.dt[bt * a.H + h];
+            const float av = retention(dtv, Ah);
+            const int64_t bgN = (bt * a.G + g) * N + n0;
+            const float4 bn = IO<T>::ld4(Bm, bgN);
+            const float4 cn = IO<T>::ld4(Cm, bgN);
+            const int64_t xrow = (bt * a.H + h) * a.P;
+            float4 pc = make_float4(0.f, 0.f, 0.f, 0.f);  // sum_p dy_p s_t[p, n]
+            float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);  // sum_p gs[p, n] x_p
+            float wsum = 0.f, rsum = 0.f, dsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < MAXR; ++i) {
+                const int p = r0 + i * RPW;
+                if (p < a.P) {
+                    const int64_t off = static_cast<int64_t>(p) * N + n0;
+                    const float4 st = *reinterpret_cast<const float4 *>(slab + (t - tlo + 1) * PN + off);
+                    const float4 sp = *reinterpret_cast<const float4 *>(slab + (t - tlo) * PN + off);
+                    const float dyp = IO<T>::ld(dy, xrow + p);
+                    const float xp = IO<T>::ld(x, xrow + p);
+                    gs[i].x = fmaf(dyp, cn.x, gs[i].x);
+                    gs[i].y = fmaf(dyp, cn.y, gs[i].y);
+                    gs[i].z = fmaf(dyp, cn.z, gs[i].z);
+                    gs[i].w = fmaf(dyp, cn.w, gs[i].w);
+                    pc.x = fmaf(dyp, st.x, pc.x);
+                    pc.y = fmaf(dyp, st.y, pc.y);
+                    pc.z = fmaf(dyp, st.z, pc.z);
+                    pc.w = fmaf(dyp, st.w, pc.w);
+                    pb.x = fmaf(gs[i].x, xp, pb.x);
+                    pb.y = fmaf(gs[i].y, xp, pb.y);
+                    pb.z = fmaf(gs[i].z, xp, pb.z);
+                    pb.w = fmaf(gs[i].w, xp, pb.w);
+                    float gb = gs[i].x * bn.x + gs[i].y * bn.y + gs[i].z * bn.z + gs[i].w * bn.w;
+                    gb = row_reduce<LPR>(gb);
+                    if ((tid % LPR) == 0) {
+                        IO<T>::st(dx, xrow + p, fmaf(Dh, dyp, dtv * gb));
+                        wsum = fmaf(xp, gb, wsum);
+                        dsum = fmaf(dyp, xp, dsum);
+                    }
+                    rsum += gs[i].x * sp.x + gs[i].y * sp.y + gs[i].z * sp.z + gs[i].w * sp.w;
+                }
+            }
+            // cross-row sums for dC / dB (fixed order over row groups)
+            *reinterpret_cast<float4 *>(&red_c[r0 * N + n0]) = pc;
+            *reinterpret_cast<float4 *>(&red_b[r0 * N + n0]) = pb;
+            wsum = wave_sum(wsum);
+            rsum = wave_sum(rsum);
+            dsum = wave_sum(dsum);
+            if (lane == 0) {
+                red_w[0][wave] = wsum;
+                red_w[1][wave] = rsum;
+                red_w[2][wave] = dsum;
+            }
+            __syncthreads();
+            if (tid < N) {
+                float sc = 0.f, sb = 0.f;
+                for (int r = 0; r < RPW; ++r) {
+                    sc += red_c[r * N + tid];
+                    sb += red_b[r * N + tid];
+                }
+                const int64_t o = (bt * a.H + h) * N + tid;
+                a.dC_part[o] = sc;
+                a.dB_part[o] = dtv * sb;
+            }
+            if (tid == 0) {
+                const float W = (red_w[0][0] + red_w[0][1]) + (red_w[0][2] + red_w[0][3]);
+                const float R = (red_w[1][0] + red_w[1][1]) + (red_w[1][2] + red_w[1][3]);
+                const float S = (red_w[2][0] + red_w[2][1]) + (red_w[2][2] + red_w[2][3]);
+                a.ddt[bt * a.H + h] = W + R * av * Ah;
+                dA_acc += static_cast<double>(R) * av * dtv;
+                dD_acc += static_cast<double>(S);
+            }
+#pragma unroll
+            for (int i = 0; i < MAXR; ++i) {
+                gs[i].x *= av;
+                gs[i].y *= av;
+                gs[i].z *= av;
+                gs[i].w *= av;
+            }
+            __syncthreads();
+        }
+    }
+    if (a.dh0 != nullptr) {
+#pragma unroll
+        for (int i = 0; i < MAXR; ++i) {
+            const int p = r0 + i * RPW;
+            if (p < a.P)
+                *reinterpret_cast<float4 *>(a.dh0 + bh * PN + static_cast<int64_t>(p) * N + n0) = gs[i];
+        }
+    }
+    if (tid == 0) {
+        a.dA_part[bh] = dA_acc;
+        a.dD_part[bh] = dD_acc;
+    }
+}
+
+// dB/dC of a group = sum of the per-head partials in ascending head order.
+__global__ void group_sum_kernel(const float *part_b, const float *part_c, float *dB, float *dC,
+                                 int64_t BT, int H, int G, int N) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = BT * G * N;
+    if (i >= total) return;
+    const int n = static_cast<int>(i % N);
+    const int64_t bg = i / N;
+    const int g = static_cast<int>(bg % G);
+    const int64_t bt = bg / G;
+    const int hpg = H / G;
+    float sb = 0.f, sc = 0.f;
+    for (int k = 0; k < hpg; ++k) {
+        const int64_t o = (bt * H + g * hpg + k) * N + n;
+        sb += part_b[o];
+        sc += part_c[o];
+    }
+    dB[i] = sb;
+    dC[i] = sc;
+}
+
+// dA[h], dD[h] = sums over batch of per-(batch, head) fp64 partials.
+__global__ void head_param_sum_kernel(const double *pa, const double *pd, float *dA, float *dD,
+                                      int Bsz, int H) {
+    const int h = blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    double sa = 0.0, sd = 0.0;
+    for (int b = 0; b < Bsz; ++b) {
+        sa += pa[static_cast<int64_t>(b) * H + h];
+        sd += pd[static_cast<int64_t>(b) * H + h];
+    }
+    dA[h] = static_cast<float>(sa);
+    dD[h] = static_cast<float>(sd);
+}
+
+__global__ void fill_kernel(float *p, int64_t n, float v) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+__global__ void copy_kernel(float *dst, const float *src, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    fill_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+hipError_t launch_copy(float *dst, const float *src, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    copy_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(dst, src, n);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.Bsz * a.H)), block(256);
+    switch (a.N) {
+        case 16: decode_kernel<16, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 32: decode_kernel<32, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 64: decode_kernel<64, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 128: decode_kernel<128, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 256: decode_kernel<256, 8, T><<<grid, block, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s) {
+    return bf16 ? launch_decode_t<bf16_t>(a, s) : launch_decode_t<float>(a, s);
+}
+
+template <typename T, typename CK, bool LIVE>
+static hipError_t launch_scan_tcl(const ScanArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.Bsz * a.H)), block(256);
+    switch (a.N) {
+        case 16: scan_kernel<16, 8, T, CK, LIVE><<<grid, block, 0, s>>>(a); break;
+        case 32: scan_kernel<32, 8, T, CK, LIVE><<<grid, block, 0, s>>>(a); break;
+        case 64: scan_kernel<64, 8, T, CK, LIVE><<<grid, block, 0, s>>>(a); break;
+        case 128: scan_kernel<128, 8, T, CK, LIVE><<<grid, block, 0, s>>>(a); break;
+        case 256: scan_kernel<256, 8, T, CK, LIVE><<<grid, block, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename CK>
+static hipError_t launch_scan_tc(const ScanArgs &a, hipStream_t s) {
+    return a.live ? launch_scan_tcl<T, CK, true>(a, s) : launch_scan_tcl<T, CK, false>(a, s);
+}
+
+hipError_t launch_scan(const ScanArgs &a, bool bf16, bool ckpt_f16, hipStream_t s) {
+    if (bf16) return ckpt_f16 ? launch_scan_tc<bf16_t, uint16_t>(a, s) : launch_scan_tc<bf16_t, float>(a, s);
+    return ckpt_f16 ? launch_scan_tc<float, uint16_t>(a, s) : launch_scan_tc<float, float>(a, s);
+}
+
+hipError_t launch_drift_reduce(const float *pm, const float *ps, int64_t nwaves, int64_t r,
+                               double inv_count, float *dmax, float *dmean, hipStream_t s) {
+    const unsigned blocks = static_cast<unsigned>((r + 255) / 256);
+    drift_reduce_kernel<<<blocks, 256, 0, s>>>(pm, ps, nwaves, r, inv_count, dmax, dmean);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_scan_bwd_t(const ScanBwdArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.Bsz * a.H)), block(256);
+    switch (a.N) {
+        case 16: scan_bwd_kernel<16, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 32: scan_bwd_kernel<32, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 64: scan_bwd_kernel<64, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 128: scan_bwd_kernel<128, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 256: scan_bwd_kernel<256, 8, T><<<grid, block, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = a.Bsz * a.T * a.G * a.N;
+    group_sum_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, s>>>(
+        a.dB_part, a.dC_part, a.dB, a.dC, a.Bsz * a.T, a.H, a.G, a.N);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    head_param_sum_kernel<<<static_cast<unsigned>((a.H + 255) / 256), 256, 0, s>>>(
+        a.dA_part, a.dD_part, a.dA, a.dD, a.Bsz, a.H);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd(const ScanBwdArgs &a, bool bf16, hipStream_t s) {
+    return bf16 ? launch_scan_bwd_t<bf16_t>(a, s) : launch_scan_bwd_t<float>(a, s);
+}
+
+}  // namespace ssm

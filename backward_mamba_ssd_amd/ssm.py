@@ -1,0 +1,236 @@
+"""ctypes binding of the C-ABI library ``libssm_mi355x.so`` (see include/ssm.h).
+
+The functions carry the C names.  They only marshal arguments: read shapes off
+torch tensors, allocate outputs and workspace with torch on the tensors'
+device, pass raw device pointers and the current HIP stream, and raise
+``SsmError`` on a non-zero status.  Every step of the computation runs in the
+library's gfx950 kernels; there is no other code path.  If the library is not
+built the import of this module fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
+
+SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
+SSM_WS_FWD, SSM_WS_BWD, SSM_WS_REPLAY = 0, 1, 2
+_SIZE_MAX = ctypes.c_size_t(-1).value
+
+EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_decode_step", "ssm_checkpoint_sr16",
+           "ssm_replay", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path")
+
+
+class ssm_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk")]
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i64, u64, i32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_uint64,
+                             ctypes.c_int)
+    D = ctypes.POINTER(ssm_dims)
+    lib.ssm_status_string.argtypes = [i32]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_workspace_bytes.argtypes = [D, i32, i32, i64]
+    lib.ssm_workspace_bytes.restype = sz
+    lib.ssm_uses_mfma_path.argtypes = [D, i32]
+    lib.ssm_uses_mfma_path.restype = i32
+    lib.ssm_fwd_chunked.argtypes = [D, i32] + [vp] * 10 + [vp, sz, vp]
+    lib.ssm_fwd_chunked.restype = i32
+    lib.ssm_bwd.argtypes = [D, i32] + [vp] * 16 + [vp, sz, vp]
+    lib.ssm_bwd.restype = i32
+    lib.ssm_decode_step.argtypes = [D, i32] + [vp] * 8 + [vp]
+    lib.ssm_decode_step.restype = i32
+    lib.ssm_checkpoint_sr16.argtypes = [vp, vp, u64, u64, u64, u64, vp]
+    lib.ssm_checkpoint_sr16.restype = i32
+    lib.ssm_replay.argtypes = ([D, i32, vp, i32, vp] + [vp] * 6 + [i64, i64] + [vp] * 4
+                               + [vp, sz, vp])
+    lib.ssm_replay.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.ssm_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise SsmError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t or None
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"unsupported storage dtype {t.dtype}")
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk=1):
+    return ssm_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
+
+
+def dims_of(x, B, chunk):
+    b, t, h, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    return make_dims(b, t, h, p, n, g, chunk)
+
+
+def ssm_workspace_bytes(dims, dtype_code, which, r=0):
+    v = _lib.ssm_workspace_bytes(ctypes.byref(dims), int(dtype_code), int(which), int(r))
+    if v == _SIZE_MAX:
+        raise SsmError(3, "ssm_workspace_bytes")
+    return int(v)
+
+
+def ssm_uses_mfma_path(dims, dtype_code):
+    return bool(_lib.ssm_uses_mfma_path(ctypes.byref(dims), int(dtype_code)))
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() >= nbytes:
+        return ws, int(ws.numel())
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def ssm_fwd_chunked(x, B, C, dt, A, D, h0=None, chunk=256, h_final=True, chunk_states=True,
+                    y=None, workspace=None, stream=None):
+    """Chunked prefill forward.  Returns (y, h_final or None, chunk_states or None)."""
+    dims = dims_of(x, B, chunk)
+    code = _dtype_code(x)
+    dev = x.device
+    b, t, h, p = x.shape
+    n = B.shape[3]
+    nc = (t + chunk - 1) // chunk
+    if y is None:
+        y = torch.empty_like(x)
+    hf = (torch.empty((b, h, p, n), dtype=torch.float32, device=dev) if h_final is True
+          else (h_final if isinstance(h_final, torch.Tensor) else None))
+    cs = (torch.empty((b, h, nc, p, n), dtype=torch.float32, device=dev) if chunk_states is True
+          else (chunk_states if isinstance(chunk_states, torch.Tensor) else None))
+    ws, wsb = _workspace(ssm_workspace_bytes(dims, code, SSM_WS_FWD), dev, workspace)
+    st = _lib.ssm_fwd_chunked(ctypes.byref(dims), code, _ptr(x), _ptr(B), _ptr(C), _ptr(dt),
+                              _ptr(A), _ptr(D), _ptr(h0), _ptr(y), _ptr(hf), _ptr(cs), _ptr(ws),
+                              wsb, _stream(stream))
+    _check(st, "ssm_fwd_chunked")
+    return y, hf, cs
+
+
+def ssm_bwd(x, B, C, dt, A, D, chunk_states, dy, dh_final=None, chunk=256, dh0=True, out=None,
+            workspace=None, stream=None):
+    """Backward.  Returns dict dx, dB, dC, ddt, dA, dD, dh0 (dh0 None if not asked)."""
+    dims = dims_of(x, B, chunk)
+    code = _dtype_code(x)
+    dev = x.device
+    b, t, h, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    f32 = dict(dtype=torch.float32, device=dev)
+    if out is None:
+        out = {
+            "dx": torch.empty_like(x),
+            "dB": torch.empty((b, t, g, n), **f32),
+            "dC": torch.empty((b, t, g, n), **f32),
+            "ddt": torch.empty((b, t, h), **f32),
+            "dA": torch.empty((h,), **f32),
+            "dD": torch.empty((h,), **f32),
+            "dh0": torch.empty((b, h, p, n), **f32) if dh0 else None,
+        }
+    ws, wsb = _workspace(ssm_workspace_bytes(dims, code, SSM_WS_BWD), dev, workspace)
+    st = _lib.ssm_bwd(ctypes.byref(dims), code, _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
+                      _ptr(D), _ptr(chunk_states), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]),
+                      _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+                      _ptr(out["dD"]), _ptr(out.get("dh0")), _ptr(ws), wsb, _stream(stream))
+    _check(st, "ssm_bwd")
+    return out
+
+
+def ssm_decode_step(state, x, B, C, dt, A, D, y=None, stream=None):
+    """In-place one-token update of state [b,h,p,n]; returns y [b,h,p]."""
+    b, h, p, n = state.shape
+    g = B.shape[1]
+    dims = make_dims(b, 1, h, p, n, g, 1)
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    st = _lib.ssm_decode_step(ctypes.byref(dims), code, _ptr(state), _ptr(x), _ptr(B), _ptr(C),
+                              _ptr(dt), _ptr(A), _ptr(D), _ptr(y), _stream(stream))
+    _check(st, "ssm_decode_step")
+    return y
+
+
+def ssm_checkpoint_sr16(state, seed, ckpt_index, elem_offset=0, out=None, stream=None):
+    """SR16 bits of a float32 state (returned as an int16 tensor holding the bits)."""
+    if out is None:
+        out = torch.empty(state.shape, dtype=torch.int16, device=state.device)
+    st = _lib.ssm_checkpoint_sr16(_ptr(state), _ptr(out), state.numel(), seed & (2**64 - 1),
+                                  int(ckpt_index), int(elem_offset), _stream(stream))
+    _check(st, "ssm_checkpoint_sr16")
+    return out
+
+
+def ssm_replay(ckpt, x, B, C, dt, A, D, t0, r, state_out=None, y=None, live=None,
+               workspace=None, stream=None):
+    """Replay tokens t0..t0+r-1 from ckpt (float32 state, or int16 SR16 bits).
+
+    Returns dict with state (float32), and when ``live`` is given drift_max and
+    drift_mean [r].  ``y`` (full-length output tensor) is written if given.
+    """
+    b, t, h, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    dims = make_dims(b, t, h, p, n, g, 1)
+    code = _dtype_code(x)
+    ck_code = SSM_F32 if ckpt.dtype == torch.float32 else SSM_F16
+    if state_out is None:
+        state_out = torch.empty((b, h, p, n), dtype=torch.float32, device=x.device)
+    dmax = dmean = None
+    ws, wsb = None, 0
+    if live is not None and r > 0:
+        dmax = torch.empty(r, dtype=torch.float32, device=x.device)
+        dmean = torch.empty(r, dtype=torch.float32, device=x.device)
+        ws, wsb = _workspace(ssm_workspace_bytes(dims, code, SSM_WS_REPLAY, r), x.device,
+                             workspace)
+    st = _lib.ssm_replay(ctypes.byref(dims), code, _ptr(ckpt), ck_code, _ptr(state_out), _ptr(x),
+                         _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), int(t0), int(r), _ptr(y),
+                         _ptr(live), _ptr(dmax), _ptr(dmean), _ptr(ws), wsb, _stream(stream))
+    _check(st, "ssm_replay")
+    return {"state": state_out, "drift_max": dmax, "drift_mean": dmean}

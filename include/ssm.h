@@ -1,0 +1,184 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) Mamba-2 selective state-space library.
+ *
+ * The recurrence, per batch b, head h and group g = h / (nheads/ngroups):
+ *     a_t      = exp(dt[b,t,h] * A[h])
+ *     s[p][n]  = a_t * s[p][n] + x[b,t,h,p] * (B[b,t,g,n] * dt[b,t,h])
+ *     y[b,t,h,p] = sum_n C[b,t,g,n] * s[p][n] + D[h] * x[b,t,h,p]
+ * "Nemotron 3 Ultra: replaying a rounded state" (TorchLean Verified Examples),
+ * section "The Mamba state update" (theorem updateHead_apply: per-coordinate
+ * update with the head's group B and a per-head rate), and section "Recovering
+ * the state by replay" (the output reads the updated state).
+ *
+ * Conventions shared by every call
+ *  - Layouts are dense row-major:
+ *      x, y, dy, dx   [batch, seqlen, nheads, headdim]           (dtype)
+ *      B, C           [batch, seqlen, ngroups, dstate]           (dtype)
+ *      dB, dC         [batch, seqlen, ngroups, dstate]           float
+ *      dt, ddt        [batch, seqlen, nheads]                    float (dt > 0)
+ *      A, D, dA, dD   [nheads]                                   float
+ *      states         [batch, nheads, headdim, dstate]           float
+ *      chunk_states   [batch, nheads, nchunks, headdim, dstate]  float,
+ *                     nchunks = ceil(seqlen/chunk); entry c is the state
+ *                     ENTERING chunk c (entry 0 is the initial state).
+ *  - `dtype` (SSM_F32 or SSM_BF16) is the storage type of x, B, C, dy, y, dx.
+ *  - All pointers are device pointers (HBM) owned by the caller.  Alignment:
+ *    state-shaped float arrays (states, chunk_states, h0, h_final, dh_final,
+ *    dh0, checkpoints) and the workspace: 16 bytes; B, C, dB, dC: 16 bytes on
+ *    the MFMA path, else 4 elements; x, y, dy, dx: 16 bytes on the MFMA path,
+ *    else one element; dt, A, D, ddt, dA, dD, drift arrays: 4 bytes.
+ *    The library never allocates and never synchronises; all work is enqueued
+ *    on `stream` (a hipStream_t; NULL means the null stream).
+ *  - Outputs are overwritten, never accumulated.
+ *  - Every argument is validated before anything is enqueued; on any error
+ *    nothing is written ("detected before any work", as in "Reverse-mode
+ *    automatic differentiation" (OneModel docs), section 2 "The engine").
+ *  - Calls are stateless and reentrant; calls on different streams that
+ *    write the same buffers race.
+ *  - Results are deterministic: no floating-point atomics; every reduction
+ *    has a fixed order.
+ */
+#ifndef SSM_MI355X_H
+#define SSM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSM_ERR_DIMS = 2,        /* non-positive dim, nheads % ngroups != 0, ... */
+    SSM_ERR_UNSUPPORTED = 3, /* a (headdim, dstate, chunk) with no kernel */
+    SSM_ERR_DTYPE = 4,       /* unknown dtype */
+    SSM_ERR_ALIGN = 5,       /* a pointer is not aligned as required */
+    SSM_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+    SSM_ERR_HIP = 7          /* a HIP launch reported an error */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1, SSM_F16 = 2 } ssm_dtype;
+
+typedef struct {
+    int64_t batch;
+    int64_t seqlen;
+    int64_t nheads;
+    int64_t headdim;  /* P: value channels per head */
+    int64_t dstate;   /* N: state coordinates */
+    int64_t ngroups;  /* heads h in [g*nheads/ngroups, (g+1)*nheads/ngroups) share B, C */
+    int64_t chunk;    /* L: chunk length (state save interval) */
+} ssm_dims;
+
+typedef void *ssm_stream; /* hipStream_t */
+
+/* Workspace kinds for ssm_workspace_bytes. */
+enum { SSM_WS_FWD = 0, SSM_WS_BWD = 1, SSM_WS_REPLAY = 2 };
+
+/* Bytes of device workspace a call needs (0 is a valid answer).  `r` is the
+ * replay length for SSM_WS_REPLAY and ignored otherwise.  Returns (size_t)-1
+ * for invalid or unsupported dims. */
+size_t ssm_workspace_bytes(const ssm_dims *d, ssm_dtype dtype, int which, int64_t r);
+
+/* Static human-readable name of a status code. */
+const char *ssm_status_string(ssm_status s);
+
+/* 1 when the chunked MFMA kernels serve these dims and dtype (bf16 operands,
+ * headdim 64, dstate 128, chunk a multiple of 64); otherwise the exact-fp32
+ * sequential kernels run.  Purely informational. */
+int ssm_uses_mfma_path(const ssm_dims *d, ssm_dtype dtype);
+
+/*
+ * Chunked prefill forward.  "Nemotron Kernels: From Inference To
+ * Backpropagation", Kernel 1: the prefill scan walks the whole sequence and
+ * returns the outputs and the final state.
+ *   h0            initial state or NULL (zero)
+ *   y             outputs (dtype)
+ *   h_final       final state or NULL
+ *   chunk_states  states entering each chunk or NULL (needed by ssm_bwd)
+ *   workspace     ssm_workspace_bytes(d, dtype, SSM_WS_FWD, 0) bytes
+ */
+ssm_status ssm_fwd_chunked(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                           const void *C, const float *dt, const float *A, const float *D,
+                           const float *h0, void *y, float *h_final, float *chunk_states,
+                           void *workspace, size_t ws_bytes, ssm_stream stream);
+
+/*
+ * Reverse-mode backward.  Same page, Kernel 1 "Backpropagation: What Mamba2
+ * Backward Must Do": a reverse walk over the tokens in which the state
+ * gradient is the output path plus the future recurrent path, and shared B/C
+ * receive the sum over every head and channel of their group.  The loss seen
+ * by the backward is sum(dy*y) + sum(dh_final*h_final).
+ *   chunk_states  from ssm_fwd_chunked with the same dims (entry 0 = h0); the
+ *                 backward recomputes everything else from them
+ *   dh_final      gradient on the final state or NULL (zero)
+ *   dx            (dtype); dB, dC summed over the group's heads; ddt w.r.t.
+ *                 the dt input; dA, dD summed over batch and tokens;
+ *   dh0           gradient on the initial state, or NULL
+ *   workspace     ssm_workspace_bytes(d, dtype, SSM_WS_BWD, 0) bytes
+ */
+ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                   const void *C, const float *dt, const float *A, const float *D,
+                   const float *chunk_states, const void *dy, const float *dh_final, void *dx,
+                   float *dB, float *dC, float *ddt, float *dA, float *dD, float *dh0,
+                   void *workspace, size_t ws_bytes, ssm_stream stream);
+
+/*
+ * One-token decode state update, in place.  Same page, Kernel 1: decode
+ * evaluates the same recurrence for one step.  `d->seqlen` and `d->chunk` are
+ * ignored.  Shapes: state [batch,nheads,headdim,dstate] float (in/out),
+ * x [batch,nheads,headdim], B, C [batch,ngroups,dstate], dt [batch,nheads],
+ * y [batch,nheads,headdim] (dtype).  Bit-identical to one step of ssm_replay.
+ */
+ssm_status ssm_decode_step(const ssm_dims *d, ssm_dtype dtype, float *state, const void *x,
+                           const void *B, const void *C, const float *dt, const float *A,
+                           const float *D, void *y, ssm_stream stream);
+
+/*
+ * FP16 stochastically rounded checkpoint of a float32 state.  "Nemotron 3
+ * Ultra: replaying a rounded state", sections "Stochastic rounding and the
+ * mean state" (round up when the entropy residue is below the discarded
+ * remainder) and "Recovering the state by replay" (a random step keeps its
+ * random choices, so the entropy is a pure function of a key).
+ * Element i of `state` (n_elems of them) is rounded with the entropy word
+ *   u = high32( SM(SM(seed, ckpt_index), elem_offset + i) )
+ * where SM(s, k) is output k (0-based) of a SplitMix64 stream seeded with s.
+ * With R = floor(remainder * 2^32), the magnitude goes to the upper binary16
+ * neighbour iff u < R.  Magnitudes reaching 65536 become infinity; NaN keeps
+ * its sign as 0x7E00.  `out` receives binary16 bits and must not alias state.
+ */
+ssm_status ssm_checkpoint_sr16(const float *state, uint16_t *out, uint64_t n_elems,
+                               uint64_t seed, uint64_t ckpt_index, uint64_t elem_offset,
+                               ssm_stream stream);
+
+/*
+ * Replay r retained tokens from a checkpoint.  Same page, section
+ * "Recovering the state by replay": re-applying the retained prepared inputs
+ * in order from a saved state recovers the current state.
+ *   ckpt        [batch,nheads,headdim,dstate], float (ckpt_dtype SSM_F32) or
+ *               binary16 bits (SSM_F16, widened exactly)
+ *   state_out   state after the r tokens (float); may alias ckpt if SSM_F32
+ *   x, B, C, dt full-length inputs ([batch, seqlen, ...]); tokens
+ *               t0 .. t0+r-1 are replayed (t0 + r <= seqlen)
+ *   y           NULL, or [batch,seqlen,nheads,headdim] (dtype): the outputs of
+ *               the replayed tokens are written at t0 .. t0+r-1
+ *   live_ckpt   NULL, or a float state advanced in lockstep with the same
+ *               inputs (not written); then drift_max[k] and drift_mean[k]
+ *               (k = 0..r-1) receive max and mean over all elements of
+ *               |replayed - live| after token t0+k
+ *   workspace   ssm_workspace_bytes(d, dtype, SSM_WS_REPLAY, r) bytes (0 when
+ *               live_ckpt is NULL)
+ * The step arithmetic is the one of ssm_decode_step, bit for bit.
+ */
+ssm_status ssm_replay(const ssm_dims *d, ssm_dtype dtype, const void *ckpt, ssm_dtype ckpt_dtype,
+                      float *state_out, const void *x, const void *B, const void *C,
+                      const float *dt, const float *A, const float *D, int64_t t0, int64_t r,
+                      void *y, const float *live_ckpt, float *drift_max, float *drift_mean,
+                      void *workspace, size_t ws_bytes, ssm_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_MI355X_H */

@@ -1,0 +1,136 @@
+"""Host-only checks of the C-ABI library (no GPU needed, nothing enqueued).
+
+- the built library loads and exports every function declared in include/ssm.h;
+- invalid calls are rejected with the documented status before any work
+  ("Reverse-mode automatic differentiation" (OneModel docs), section 2: errors
+  are detected before any work) -- every case here fails validation, so no
+  kernel is ever launched;
+- workspace sizing and the MFMA-path predicate are pure host logic.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+ssm = pytest.importorskip("backward_mamba_ssd_amd.ssm")
+
+OK, NULL, DIMS, UNSUP, DTYPE, ALIGN, WS, HIP = range(8)
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("ssm_fwd_chunked", "ssm_decode_step", "ssm_bwd", "ssm_checkpoint_sr16",
+              "ssm_replay"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ssm.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(ssm.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings():
+    for code in range(8):
+        assert ssm.status_string(code).startswith("SSM_")
+
+
+def dims(**kw):
+    base = dict(batch=2, seqlen=100, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=64)
+    base.update(kw)
+    return ssm.make_dims(**base)
+
+
+def fwd(d, dtype=ssm.SSM_BF16, x=FAKE, B=FAKE, C=FAKE, dt=FAKE, A=FAKE, D=FAKE, h0=None, y=FAKE,
+        hf=None, cs=None):
+    L = ssm.lib()
+    dp = ctypes.byref(d) if d is not None else None
+    return L.ssm_fwd_chunked(dp, dtype, x, B, C, dt, A, D, h0, y, hf, cs, None, 0, None)
+
+
+def bwd(d, ws=None, wsb=0, **over):
+    L = ssm.lib()
+    a = dict(x=FAKE, B=FAKE, C=FAKE, dt=FAKE, A=FAKE, D=FAKE, cs=FAKE, dy=FAKE, dhf=None, dx=FAKE,
+             dB=FAKE, dC=FAKE, ddt=FAKE, dA=FAKE, dD=FAKE, dh0=None)
+    a.update(over)
+    return L.ssm_bwd(ctypes.byref(d), ssm.SSM_BF16, a["x"], a["B"], a["C"], a["dt"], a["A"],
+                     a["D"], a["cs"], a["dy"], a["dhf"], a["dx"], a["dB"], a["dC"], a["ddt"],
+                     a["dA"], a["dD"], a["dh0"], ws, wsb, None)
+
+
+def test_fwd_validation():
+    assert fwd(None) == NULL
+    assert fwd(dims(nheads=6, ngroups=4)) == DIMS
+    assert fwd(dims(chunk=0)) == DIMS
+    assert fwd(dims(headdim=0)) == DIMS
+    assert fwd(dims(batch=-1)) == DIMS
+    assert fwd(dims(), dtype=7) == DTYPE
+    assert fwd(dims(dstate=100)) == UNSUP
+    assert fwd(dims(), x=None) == NULL
+    assert fwd(dims(), y=FAKE + 1) == ALIGN
+    assert fwd(dims(), h0=FAKE + 8) == ALIGN
+    assert fwd(dims(), A=None) == NULL
+
+
+def test_bwd_validation():
+    d = dims()
+    need = ssm.ssm_workspace_bytes(d, ssm.SSM_BF16, ssm.SSM_WS_BWD)
+    assert need > 0
+    assert bwd(d) == WS
+    assert bwd(d, ws=FAKE, wsb=need - 1) == WS
+    assert bwd(d, ws=FAKE, wsb=need, cs=None) == NULL
+    assert bwd(d, ws=FAKE + 8, wsb=need) == ALIGN
+    assert bwd(dims(nheads=3, ngroups=2), ws=FAKE, wsb=need) == DIMS
+
+
+def test_decode_replay_sr16_validation():
+    L = ssm.lib()
+    d = dims(seqlen=1)
+    args = [FAKE] * 8
+    assert L.ssm_decode_step(ctypes.byref(d), ssm.SSM_BF16, None, *args[1:], None) == NULL
+    assert L.ssm_decode_step(ctypes.byref(dims(dstate=48)), ssm.SSM_BF16, *args, None) == UNSUP
+    assert L.ssm_checkpoint_sr16(None, FAKE, 10, 0, 0, 0, None) == NULL
+    assert L.ssm_checkpoint_sr16(FAKE, FAKE + 1, 10, 0, 0, 0, None) == ALIGN
+    assert L.ssm_checkpoint_sr16(FAKE, FAKE + 16, 10, 0, 0, 0, None) == DIMS  # aliasing
+    assert L.ssm_checkpoint_sr16(None, None, 0, 0, 0, 0, None) == OK  # empty: no-op
+    rd = dims(seqlen=50)
+    common = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+
+    def rep(t0, r, live=None, dm=None, dn=None, ws=None, wsb=0, ckd=ssm.SSM_F32):
+        return L.ssm_replay(ctypes.byref(rd), ssm.SSM_BF16, FAKE, ckd, FAKE, *common, t0, r, None,
+                            live, dm, dn, ws, wsb, None)
+
+    assert rep(40, 11) == DIMS
+    assert rep(-1, 5) == DIMS
+    assert rep(0, 5, ckd=ssm.SSM_BF16) == DTYPE
+    assert rep(0, 5, live=FAKE) == NULL
+    assert rep(0, 5, live=FAKE, dm=FAKE, dn=FAKE) == WS
+    need = ssm.ssm_workspace_bytes(rd, ssm.SSM_BF16, ssm.SSM_WS_REPLAY, 5)
+    assert need >= 2 * 5 * (2 * 4 * 4) * 4  # two [r][batch*heads*4] float arrays
+
+
+def test_empty_batch_is_a_noop():
+    # batch 0: valid, nothing to do, returns OK without touching any pointer
+    assert fwd(dims(batch=0), x=None, B=None, C=None, dt=None, y=None) == OK
+
+
+def test_workspace_and_path_predicates():
+    d = dims(batch=4, seqlen=4096, nheads=256, ngroups=8, chunk=256)
+    assert ssm.ssm_workspace_bytes(d, ssm.SSM_BF16, ssm.SSM_WS_FWD) == 0
+    assert ssm.ssm_workspace_bytes(d, ssm.SSM_BF16, ssm.SSM_WS_BWD) > 0
+    with pytest.raises(ssm.SsmError):
+        ssm.ssm_workspace_bytes(dims(dstate=48), ssm.SSM_BF16, ssm.SSM_WS_FWD)
+    assert not ssm.ssm_uses_mfma_path(dims(headdim=8, dstate=16), ssm.SSM_F32)
+    assert not ssm.ssm_uses_mfma_path(d, ssm.SSM_F32)
