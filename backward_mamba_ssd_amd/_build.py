@@ -34,9 +34,12 @@ def sources():
 
 def _defines():
     have = {os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "*.hip"))}
-    if {"ssd_fwd.hip", "ssd_bwd.hip"} <= have:
-        return ["-DSSM_WITH_MFMA"]
-    return []
+    defs = []
+    if "ssd_fwd.hip" in have:
+        defs.append("-DSSM_WITH_MFMA_FWD")
+    if "ssd_bwd.hip" in have:
+        defs.append("-DSSM_WITH_MFMA_BWD")
+    return defs
 
 
 def _compile(src, defs, verbose):

@@ -60,16 +60,31 @@ bool serial_supported(const ssm_dims *d) {
     return d->headdim <= 8 * 256 / (N / 4);
 }
 
-bool mfma_path(const ssm_dims *d, ssm_dtype t) {
-#ifdef SSM_WITH_MFMA
-    return t == SSM_BF16 && d->headdim == 64 && d->dstate == 128 && d->chunk % 64 == 0 &&
-           d->nheads <= 4096;
+bool mfma_shape(const ssm_dims *d, ssm_dtype t) {
+    return t == SSM_BF16 && d->headdim == 64 && d->dstate == 128 && d->chunk % 64 == 0;
+}
+
+bool mfma_fwd_path(const ssm_dims *d, ssm_dtype t) {
+#ifdef SSM_WITH_MFMA_FWD
+    return mfma_shape(d, t);
 #else
     (void)d;
     (void)t;
     return false;
 #endif
 }
+
+bool mfma_bwd_path(const ssm_dims *d, ssm_dtype t) {
+#ifdef SSM_WITH_MFMA_BWD
+    return mfma_shape(d, t);
+#else
+    (void)d;
+    (void)t;
+    return false;
+#endif
+}
+
+bool mfma_path(const ssm_dims *d, ssm_dtype t) { return mfma_fwd_path(d, t) && mfma_bwd_path(d, t); }
 
 int64_t nchunks_of(const ssm_dims *d) { return (d->seqlen + d->chunk - 1) / d->chunk; }
 
@@ -86,7 +101,7 @@ struct Carve {
 size_t bwd_ws_bytes(const ssm_dims *d, ssm_dtype t) {
     const size_t B = d->batch, T = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate;
     const size_t nc = nchunks_of(d);
-    if (mfma_path(d, t)) {
+    if (mfma_bwd_path(d, t)) {
         return round_up(B * H * nc * P * N * sizeof(float)) + round_up(B * T * H * sizeof(float)) +
                round_up(B * H * nc * 4 * sizeof(float)) + 2 * round_up(B * H * nc * sizeof(double));
     }
@@ -128,12 +143,12 @@ size_t ssm_workspace_bytes(const ssm_dims *d, ssm_dtype dtype, int which, int64_
     if (!valid_dtype(dtype)) return static_cast<size_t>(-1);
     if (which == SSM_WS_FWD) {
         if (check_dims(d, true) != SSM_OK) return static_cast<size_t>(-1);
-        if (!mfma_path(d, dtype) && !serial_supported(d)) return static_cast<size_t>(-1);
+        if (!mfma_fwd_path(d, dtype) && !serial_supported(d)) return static_cast<size_t>(-1);
         return 0;
     }
     if (which == SSM_WS_BWD) {
         if (check_dims(d, true) != SSM_OK) return static_cast<size_t>(-1);
-        if (!mfma_path(d, dtype) && !serial_supported(d)) return static_cast<size_t>(-1);
+        if (!mfma_bwd_path(d, dtype) && !serial_supported(d)) return static_cast<size_t>(-1);
         return bwd_ws_bytes(d, dtype);
     }
     if (which == SSM_WS_REPLAY) {
@@ -151,7 +166,7 @@ ssm_status ssm_fwd_chunked(const ssm_dims *d, ssm_dtype dtype, const void *x, co
     ssm_status st = check_dims(d, true);
     if (st != SSM_OK) return st;
     if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
-    const bool mfma = mfma_path(d, dtype);
+    const bool mfma = mfma_fwd_path(d, dtype);
     if (!mfma && !serial_supported(d)) return SSM_ERR_UNSUPPORTED;
     const bool tokens = d->batch > 0 && d->seqlen > 0;
     if (tokens && (!x || !B || !C || !dt || !y)) return SSM_ERR_NULL;
@@ -178,7 +193,7 @@ ssm_status ssm_fwd_chunked(const ssm_dims *d, ssm_dtype dtype, const void *x, co
         a.G = static_cast<int>(d->ngroups); a.L = d->chunk; a.nchunks = nchunks_of(d);
         a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.D = D; a.h0 = h0; a.y = y;
         a.h_final = h_final; a.chunk_states = chunk_states;
-#ifdef SSM_WITH_MFMA
+#ifdef SSM_WITH_MFMA_FWD
         e = launch_ssd_fwd(a, s);
 #else
         e = hipErrorNotSupported;
@@ -204,7 +219,7 @@ ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void
     ssm_status st = check_dims(d, true);
     if (st != SSM_OK) return st;
     if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
-    const bool mfma = mfma_path(d, dtype);
+    const bool mfma = mfma_bwd_path(d, dtype);
     if (!mfma && !serial_supported(d)) return SSM_ERR_UNSUPPORTED;
     const bool tokens = d->batch > 0 && d->seqlen > 0;
     if (tokens && (!x || !B || !C || !dt || !chunk_states || !dy || !dx || !dB || !dC || !ddt))
@@ -242,7 +257,7 @@ ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void
         a.lam_end = cv.take<float>(d->batch * d->nheads * nc * 4);
         a.pA = cv.take<double>(d->batch * d->nheads * nc);
         a.pD = cv.take<double>(d->batch * d->nheads * nc);
-#ifdef SSM_WITH_MFMA
+#ifdef SSM_WITH_MFMA_BWD
         e = launch_ssd_bwd(a, s);
 #else
         e = hipErrorNotSupported;

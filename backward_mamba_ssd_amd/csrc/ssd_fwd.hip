@@ -1,0 +1,287 @@
+// ssd_fwd.hip -- chunked forward of the selective SSM recurrence on gfx950 MFMA.
+//
+// Specialised for the Nemotron 3 Ultra head shape (headdim P = 64, dstate
+// N = 128; "Nemotron 3 Ultra: replaying a rounded state", section "Counting
+// the state and attention cache") with bf16 x, B, C and an fp32 state.
+//
+// Chunk algebra (exact rearrangement of the recurrence of theorem
+// updateHead_apply, same page, "The Mamba state update"; the pages give no
+// chunked form, this is derived).  For one (batch, head) and a block of
+// Ls = 64 tokens entering with state H (P x N), let a_j = dt_j * A,
+// Lam_i = a_0 + ... + a_i (inclusive, local to the block), then
+//   h_i  = exp(Lam_i) H + sum_{j<=i} exp(Lam_i - Lam_j) dt_j x_j B_j^T
+//   y_i  = C_i . h_i + D x_i
+//        = exp(Lam_i) (H C_i) + sum_{j<=i} [(C_i.B_j) exp(Lam_i-Lam_j) dt_j] x_j + D x_i
+//   H'   = exp(Lam_63) H + sum_j [exp(Lam_63 - Lam_j) dt_j] x_j B_j^T
+// Every exponent is <= 0, so no factor exceeds 1.  The three products
+//   G^T = B C^T (Gram of the group's B and C, causal half, masked and decayed),
+//   Y^T = H C^T (scaled by exp(Lam)) + X^T Gm^T,
+//   H'^T = exp(Lam_63) H^T + Bs^T X   (Bs = B scaled per token)
+// run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the state lives in
+// the accumulators of the workgroup for the whole sequence (the inter-block
+// pass is the serial loop itself), so HBM sees each input once, y once, and
+// the state once per saved chunk.  chunk_states[c] (state entering chunk c)
+// is stored whenever a block starts a chunk of L tokens (L % 64 == 0).
+//
+// One 256-thread workgroup (4 waves) per (batch, head); workgroup ids are
+// remapped so the heads of one group run on the same XCD and share B/C in
+// that XCD's L2.
+//
+// MFMA operand convention ("NT" tiles): both operands are row-major [16 x K]
+// bf16 tiles in LDS, K contiguous.  Lane l supplies row l%16, elements
+// 8*(l/16) .. 8*(l/16)+7 of each 32-wide K step; the accumulator lane holds
+// D[m = 4*(l/16) + v][n = l%16] for v = 0..3, where D = A_tile * B_tile^T.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kP = 64;    // value channels per head
+constexpr int kN = 128;   // state coordinates
+constexpr int kLs = 64;   // tokens per block
+constexpr int kS128 = kN + 8;   // LDS row stride (elements) of 128-wide rows
+constexpr int kS64 = kLs + 8;   // LDS row stride (elements) of 64-wide rows
+
+struct FwdSmem {
+    bf16_t C[kLs * kS128];    // [tok][n]
+    bf16_t B[kLs * kS128];    // [tok][n]; after the Gram product: H in bf16, [p][n]
+    bf16_t BsT[kN * kS64];    // [n][tok] = B[tok][n] * exp(Lam_63 - Lam_tok) * dt_tok
+    bf16_t XT[kP * kS64];     // [p][tok]
+    bf16_t Gm[kLs * kS64];    // [i][j] = (C_i.B_j) exp(Lam_i - Lam_j) dt_j for j <= i, else 0
+    float lam[2][kLs];        // double-buffered by block parity
+    float dt[2][kLs];
+};
+
+__device__ __forceinline__ f32x4 mma16(const bf16_t *a, const bf16_t *b, f32x4 acc) {
+    const bf16x8 av = *reinterpret_cast<const bf16x8 *>(a);
+    const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+    // dispatch places workgroup i on XCD i % 8; give each XCD a contiguous
+    // range of (batch, head) ids so whole groups share one L2
+    if ((n & 7) != 0) return i;
+    return (i & 7) * (n >> 3) + (i >> 3);
+}
+
+__global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    FwdSmem &sm = *reinterpret_cast<FwdSmem *>(smem_raw);
+
+    const int nwg = gridDim.x;
+    const int bh = xcd_remap(blockIdx.x, nwg);
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15;          // operand row within a 16-row tile
+    const int lk = (lane >> 4) * 8;    // operand k offset within a 32-wide step
+    const int lq = (lane >> 4) * 4;    // accumulator row offset
+    const int64_t T = a.T;
+    const float Ah = a.A[h], Dh = a.D[h];
+    const bf16_t *x = static_cast<const bf16_t *>(a.x);
+    const bf16_t *Bm = static_cast<const bf16_t *>(a.B);
+    const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
+    bf16_t *y = static_cast<bf16_t *>(a.y);
+
+    // state H^T in accumulators: wave w owns n-tiles 2w, 2w+1 and all 4 p-tiles;
+    // tile q: nt = 2w + q/4, pt = q%4; element v: n = 16nt + lq + v, p = 16pt + lr
+    f32x4 H[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+        if (a.h0 != nullptr) {
+            const float4 v = *reinterpret_cast<const float4 *>(a.h0 + (static_cast<int64_t>(bh) * kP + p) * kN + n);
+            H[q] = f32x4{v.x, v.y, v.z, v.w};
+        } else {
+            H[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // cooperative load mapping
+    const int xt0 = 2 * (tid >> 3), xp0 = (tid & 7) * 8;   // x: 2 tokens x 8 channels
+    const int bt0 = 4 * (tid >> 4), bn0 = (tid & 15) * 8;  // B, C: 4 tokens x 8 coords
+    u16x8 xr[2], br[4], cr[4];
+    float dtr = 0.f;
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    auto prefetch = [&](int64_t t0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t t = t0 + xt0 + i;
+            xr[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(x + ((b * T + t) * a.H + h) * kP + xp0) : z8;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = t0 + bt0 + i;
+            const int64_t off = ((b * T + t) * a.G + g) * kN + bn0;
+            br[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(Bm + off) : z8;
+            cr[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(Cm + off) : z8;
+        }
+        if (tid < kLs) {
+            const int64_t t = t0 + tid;
+            dtr = (t < T) ? a.dt[(b * T + t) * a.H + h] : 0.f;
+        }
+    };
+
+    const int64_t nblk = (T + kLs - 1) / kLs;
+    prefetch(0);
+    for (int64_t s = 0; s < nblk; ++s) {
+        const int64_t t0 = s * kLs;
+        const int buf = static_cast<int>(s & 1);
+        // (1) cumulative log-retention of the block (one wave, one token per lane)
+        if (wave == 0) {
+            float v = dtr * Ah;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(v, off, 64);
+                if (lane >= off) v += o;
+            }
+            sm.lam[buf][lane] = v;
+            sm.dt[buf][lane] = dtr;
+        }
+        __syncthreads();
+        const float *lam = sm.lam[buf];
+        const float *dts = sm.dt[buf];
+        const float lam_end = lam[kLs - 1];
+        // (2) stage the block in LDS
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u16x8 *>(&sm.C[(bt0 + i) * kS128 + bn0]) = cr[i];
+            *reinterpret_cast<u16x8 *>(&sm.B[(bt0 + i) * kS128 + bn0]) = br[i];
+        }
+        {
+            float coef[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) coef[i] = __expf(lam_end - lam[bt0 + i]) * dts[bt0 + i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                u16x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(bf16_to_f32(br[i][e]) * coef[i]);
+                *reinterpret_cast<u16x4 *>(&sm.BsT[(bn0 + e) * kS64 + bt0]) = v;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t pr = static_cast<uint32_t>(xr[0][e]) | (static_cast<uint32_t>(xr[1][e]) << 16);
+                *reinterpret_cast<uint32_t *>(&sm.XT[(xp0 + e) * kS64 + xt0]) = pr;
+            }
+        }
+        // state entering a chunk of L tokens
+        if (a.chunk_states != nullptr && (t0 % a.L) == 0) {
+            float *cs = a.chunk_states + (static_cast<int64_t>(bh) * a.nchunks + t0 / a.L) * (kP * kN);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+                *reinterpret_cast<float4 *>(cs + p * kN + n) = make_float4(H[q][0], H[q][1], H[q][2], H[q][3]);
+            }
+        }
+        if (s + 1 < nblk) prefetch(t0 + kLs);
+        __syncthreads();
+
+        // (3) masked, decayed Gram rows of this wave: i in [16w, 16w+16)
+        {
+            const int i = 16 * wave + lr;
+            const float lam_i = lam[i];
+            for (int jt = 0; jt < 4; ++jt) {
+                u16x4 out = {0, 0, 0, 0};
+                if (jt <= wave) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        acc = mma16(&sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk],
+                                    &sm.C[i * kS128 + 32 * kk + lk], acc);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int j = 16 * jt + lq + v;
+                        const float gm = (j <= i) ? acc[v] * __expf(lam_i - lam[j]) * dts[j] : 0.f;
+                        out[v] = f32_to_bf16(gm);
+                    }
+                }
+                *reinterpret_cast<u16x4 *>(&sm.Gm[i * kS64 + 16 * jt + lq]) = out;
+            }
+        }
+        __syncthreads();
+        // (4) H in bf16 over the consumed B rows: [p][n]
+        bf16_t *Hb = sm.B;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+            u16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = f32_to_bf16(H[q][e]);
+            *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = v;
+        }
+        __syncthreads();
+        // (5) outputs: Y^T rows p in [16w, 16w+16), 16 tokens at a time
+        {
+            const int prow = 16 * wave + lr;
+            for (int tt = 0; tt < 4; ++tt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    acc = mma16(&Hb[prow * kS128 + 32 * kk + lk],
+                                &sm.C[(16 * tt + lr) * kS128 + 32 * kk + lk], acc);
+                const int tok = 16 * tt + lr;
+                const float el = __expf(lam[tok]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] *= el;
+                for (int kk = 0; kk <= tt / 2; ++kk)
+                    acc = mma16(&sm.XT[prow * kS64 + 32 * kk + lk],
+                                &sm.Gm[(16 * tt + lr) * kS64 + 32 * kk + lk], acc);
+                const int64_t t = t0 + tok;
+                if (t < T) {
+                    const int64_t off = ((b * T + t) * a.H + h) * kP + 16 * wave + lq;
+                    const u16x4 xv = *reinterpret_cast<const u16x4 *>(x + off);
+                    u16x4 yv;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) yv[v] = f32_to_bf16(fmaf(Dh, bf16_to_f32(xv[v]), acc[v]));
+                    *reinterpret_cast<u16x4 *>(y + off) = yv;
+                }
+            }
+        }
+        // (6) state update H^T = exp(Lam_63) H^T + Bs^T X
+        {
+            const float el = __expf(lam_end);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int nt = 2 * wave + q / 4, pt = q % 4;
+                f32x4 acc = H[q];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] *= el;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc = mma16(&sm.BsT[(16 * nt + lr) * kS64 + 32 * kk + lk],
+                                &sm.XT[(16 * pt + lr) * kS64 + 32 * kk + lk], acc);
+                H[q] = acc;
+            }
+        }
+    }
+    if (a.h_final != nullptr) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+            *reinterpret_cast<float4 *>(a.h_final + (static_cast<int64_t>(bh) * kP + p) * kN + n) =
+                make_float4(H[q][0], H[q][1], H[q][2], H[q][3]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s) {
+    const size_t smem = sizeof(FwdSmem);
+    static bool configured = false;
+    if (!configured) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ssd_fwd_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(smem));
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    const unsigned grid = static_cast<unsigned>(a.Bsz * a.H);
+    ssd_fwd_kernel<<<grid, 256, smem, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

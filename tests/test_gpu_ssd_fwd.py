@@ -1,0 +1,91 @@
+"""GPU parity of the chunked MFMA forward (bf16 x/B/C, headdim 64, dstate 128).
+
+Tolerance 2e-2 scaled error (bf16 MFMA operands, fp32 accumulation) on y,
+h_final and chunk_states.  Sizes span several 64-token blocks, partial chunks
+and ragged tails; the full prefill workload (batch 4, 256 heads, T = 4096,
+chunk 256) is checked on whole (batch, group) units, which the oracle computes
+exactly on their own since groups never interact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from backward_mamba_ssd_amd import inputs
+from oracle import oracle
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+dev = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    from backward_mamba_ssd_amd import ssm as m
+    return m
+
+
+def _uses_mfma(ssm, pr, L):
+    d = ssm.dims_of(pr["x"], pr["B"], L)
+    return ssm.lib().ssm_uses_mfma_path(__import__("ctypes").byref(d), ssm.SSM_BF16)
+
+
+@pytest.mark.parametrize("t,L,h0", [(64, 64, "zero"), (200, 64, "randn"), (320, 128, "zero"),
+                                    (513, 256, "randn"), (37, 64, "randn"), (1000, 192, "zero")])
+def test_forward_matches_oracle(ssm, t, L, h0):
+    b, h, p, n, g = 2, 8, 64, 128, 2
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 100 + t, dev, h0=h0)
+    y, hf, cs = ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                                    h0=pr["h0"], chunk=L)
+    ref = oracle.fwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], h0=pr["h0"],
+                     chunk=L, want_chunk_states=True)
+    torch.cuda.synchronize()
+    assert_close("y", y, ref["y"], 2e-2)
+    assert_close("h_final", hf, ref["h_final"], 2e-2)
+    assert_close("chunk_states", cs, ref["chunk_states"], 2e-2)
+
+
+def test_chunk_size_only_moves_the_saved_states(ssm):
+    b, t, h, p, n, g = 1, 512, 4, 64, 128, 1
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 7, dev)
+    outs = {L: ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                                   chunk=L) for L in (64, 128, 256)}
+    for L in (128, 256):
+        assert torch.equal(outs[L][0], outs[64][0])
+        assert torch.equal(outs[L][1], outs[64][1])
+        assert torch.equal(outs[L][2], outs[64][2][:, :, ::L // 64])
+
+
+def test_prefill_equals_repeated_decode(ssm):
+    """Nemotron Kernels: From Inference To Backpropagation, Kernel 1: the
+    full-sequence scan and repeated one-token decode must agree."""
+    b, t, h, p, n, g = 2, 96, 4, 64, 128, 2
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 9, dev, h0="randn")
+    y, hf, _ = ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                                   h0=pr["h0"], chunk=64)
+    st = pr["h0"].clone()
+    ys = []
+    for k in range(t):
+        ys.append(ssm.ssm_decode_step(st, pr["x"][:, k].contiguous(), pr["B"][:, k].contiguous(),
+                                      pr["C"][:, k].contiguous(), pr["dt"][:, k].contiguous(),
+                                      pr["A"], pr["D"]))
+    torch.cuda.synchronize()
+    assert_close("y vs decode", y, torch.stack(ys, 1), 2e-2)
+    assert_close("h_final vs decode", hf, st, 2e-2)
+
+
+def test_full_prefill_workload_sampled_groups(ssm):
+    w = inputs.WORKLOADS["prefill_b4_t4096"]
+    pr = inputs.make_workload_problem(w, dev, with_dy=False)
+    y, hf, cs = ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                                    chunk=w.chunk)
+    torch.cuda.synchronize()
+    hpg = w.nheads // w.ngroups
+    for (bb, gg) in ((0, 0), (3, 7), (1, 4)):
+        hs = slice(gg * hpg, (gg + 1) * hpg)
+        print(f"group b={bb} g={gg}", flush=True)
+        ref = oracle.fwd(pr["x"][bb:bb + 1, :, hs], pr["B"][bb:bb + 1, :, gg:gg + 1],
+                         pr["C"][bb:bb + 1, :, gg:gg + 1], pr["dt"][bb:bb + 1, :, hs],
+                         pr["A"][hs], pr["D"][hs], chunk=w.chunk, want_chunk_states=True)
+        assert_close("y", y[bb:bb + 1, :, hs], ref["y"], 2e-2)
+        assert_close("h_final", hf[bb:bb + 1, hs], ref["h_final"], 2e-2)
+        assert_close("chunk_states", cs[bb:bb + 1, hs], ref["chunk_states"], 2e-2)
