@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <atomic>
 #include <initializer_list>
 
 #include "../../include/ssm.h"
@@ -102,8 +103,9 @@ size_t bwd_ws_bytes(const ssm_dims *d, ssm_dtype t) {
     const size_t B = d->batch, T = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate;
     const size_t nc = nchunks_of(d);
     if (mfma_bwd_path(d, t)) {
-        return round_up(B * H * nc * P * N * sizeof(float)) + round_up(B * T * H * sizeof(float)) +
-               round_up(B * H * nc * 4 * sizeof(float)) + 2 * round_up(B * H * nc * sizeof(double));
+        const size_t nb = d->chunk / 64;
+        return round_up(B * H * nc * P * N * sizeof(float)) +
+               2 * round_up(B * H * nc * nb * sizeof(double));
     }
     const size_t L = d->chunk < d->seqlen ? d->chunk : (d->seqlen > 0 ? d->seqlen : 1);
     return round_up(B * H * (L + 1) * P * N * sizeof(float)) +
@@ -116,9 +118,16 @@ size_t replay_ws_bytes(const ssm_dims *d, int64_t r) {
 
 hipError_t fill(float *p, int64_t n, hipStream_t s) { return launch_fill(p, n, 0.f, s); }
 
+std::atomic<void *> g_prof_begin{nullptr}, g_prof_end{nullptr};
+
 }  // namespace
 
 extern "C" {
+
+void ssm_profile_next_bwd_block(void *begin, void *end) {
+    g_prof_end.store(end);
+    g_prof_begin.store(begin);
+}
 
 const char *ssm_status_string(ssm_status s) {
     switch (s) {
@@ -252,11 +261,11 @@ ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void
         a.x = x; a.B = B; a.C = C; a.dy = dy; a.dt = dt; a.A = A; a.D = D;
         a.chunk_states = chunk_states; a.dh_final = dh_final; a.dx = dx; a.dB = dB; a.dC = dC;
         a.ddt = ddt; a.dA = dA; a.dD = dD; a.dh0 = dh0;
+        a.ev_begin = static_cast<hipEvent_t>(g_prof_begin.exchange(nullptr));
+        a.ev_end = static_cast<hipEvent_t>(g_prof_end.exchange(nullptr));
         a.dstates = cv.take<float>(d->batch * d->nheads * nc * PN);
-        a.dlam = cv.take<float>(d->batch * d->seqlen * d->nheads);
-        a.lam_end = cv.take<float>(d->batch * d->nheads * nc * 4);
-        a.pA = cv.take<double>(d->batch * d->nheads * nc);
-        a.pD = cv.take<double>(d->batch * d->nheads * nc);
+        a.pA = cv.take<double>(d->batch * d->nheads * nc * (d->chunk / 64));
+        a.pD = cv.take<double>(d->batch * d->nheads * nc * (d->chunk / 64));
 #ifdef SSM_WITH_MFMA_BWD
         e = launch_ssd_bwd(a, s);
 #else

@@ -71,11 +71,10 @@ struct SsdBwdArgs {
     const float *dt, *A, *D, *chunk_states, *dh_final;
     void *dx;
     float *dB, *dC, *ddt, *dA, *dD, *dh0;
+    hipEvent_t ev_begin, ev_end;  // optional: recorded around the per-block kernel
     // workspace
     float *dstates;   // [Bsz, H, nchunks, 64, 128]: gradient on the state leaving chunk c
-    float *dlam;      // [Bsz, T, H] d loss / d (within-chunk cumulative log-retention)
-    float *lam_end;   // [Bsz, H, nchunks, 4] per-tile partials of the chunk-end term
-    double *pA, *pD;  // [Bsz, H, nchunks] per-chunk partials of dA, dD
+    double *pA, *pD;  // [Bsz, H, nchunks, chunk/64] per-block partials of dA, dD
 };
 
 hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);

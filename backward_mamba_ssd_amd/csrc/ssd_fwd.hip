@@ -27,21 +27,13 @@
 // remapped so the heads of one group run on the same XCD and share B/C in
 // that XCD's L2.
 //
-// MFMA operand convention ("NT" tiles): both operands are row-major [16 x K]
-// bf16 tiles in LDS, K contiguous.  Lane l supplies row l%16, elements
-// 8*(l/16) .. 8*(l/16)+7 of each 32-wide K step; the accumulator lane holds
-// D[m = 4*(l/16) + v][n = l%16] for v = 0..3, where D = A_tile * B_tile^T.
+// MFMA tiles follow the "NT" convention of ssd_common.hpp.
 #include "common.hpp"
 #include "launch.hpp"
+#include "ssd_common.hpp"
 
 namespace ssm {
 namespace {
-
-constexpr int kP = 64;    // value channels per head
-constexpr int kN = 128;   // state coordinates
-constexpr int kLs = 64;   // tokens per block
-constexpr int kS128 = kN + 8;   // LDS row stride (elements) of 128-wide rows
-constexpr int kS64 = kLs + 8;   // LDS row stride (elements) of 64-wide rows
 
 struct FwdSmem {
     bf16_t C[kLs * kS128];    // [tok][n]
@@ -52,19 +44,6 @@ struct FwdSmem {
     float lam[2][kLs];        // double-buffered by block parity
     float dt[2][kLs];
 };
-
-__device__ __forceinline__ f32x4 mma16(const bf16_t *a, const bf16_t *b, f32x4 acc) {
-    const bf16x8 av = *reinterpret_cast<const bf16x8 *>(a);
-    const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-}
-
-__device__ __forceinline__ int xcd_remap(int i, int n) {
-    // dispatch places workgroup i on XCD i % 8; give each XCD a contiguous
-    // range of (batch, head) ids so whole groups share one L2
-    if ((n & 7) != 0) return i;
-    return (i & 7) * (n >> 3) + (i >> 3);
-}
 
 __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -131,13 +110,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         const int buf = static_cast<int>(s & 1);
         // (1) cumulative log-retention of the block (one wave, one token per lane)
         if (wave == 0) {
-            float v = dtr * Ah;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(v, off, 64);
-                if (lane >= off) v += o;
-            }
-            sm.lam[buf][lane] = v;
+            sm.lam[buf][lane] = wave_prefix_sum(dtr * Ah, lane);
             sm.dt[buf][lane] = dtr;
         }
         __syncthreads();

@@ -22,7 +22,8 @@ SSM_WS_FWD, SSM_WS_BWD, SSM_WS_REPLAY = 0, 1, 2
 _SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_decode_step", "ssm_checkpoint_sr16",
-           "ssm_replay", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path")
+           "ssm_replay", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path",
+           "ssm_profile_next_bwd_block")
 
 
 class ssm_dims(ctypes.Structure):
@@ -61,6 +62,8 @@ def _load():
     lib.ssm_replay.argtypes = ([D, i32, vp, i32, vp] + [vp] * 6 + [i64, i64] + [vp] * 4
                                + [vp, sz, vp])
     lib.ssm_replay.restype = i32
+    lib.ssm_profile_next_bwd_block.argtypes = [vp, vp]
+    lib.ssm_profile_next_bwd_block.restype = None
     return lib
 
 
@@ -119,6 +122,17 @@ def ssm_workspace_bytes(dims, dtype_code, which, r=0):
     if v == _SIZE_MAX:
         raise SsmError(3, "ssm_workspace_bytes")
     return int(v)
+
+
+def ssm_profile_next_bwd_block(begin_event, end_event):
+    """Arm the timing hook: the next MFMA-path ssm_bwd records these
+    torch.cuda.Event objects around its per-block kernel."""
+    def h(ev):
+        if ev is None:
+            return None
+        ev.record()  # materialise the underlying hipEvent_t; re-recorded by the library
+        return ctypes.c_void_p(ev.cuda_event)
+    _lib.ssm_profile_next_bwd_block(h(begin_event), h(end_event))
 
 
 def ssm_uses_mfma_path(dims, dtype_code):

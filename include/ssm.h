@@ -177,6 +177,16 @@ ssm_status ssm_replay(const ssm_dims *d, ssm_dtype dtype, const void *ckpt, ssm_
                       void *y, const float *live_ckpt, float *drift_max, float *drift_mean,
                       void *workspace, size_t ws_bytes, ssm_stream stream);
 
+/*
+ * Benchmark timing hook (no counterpart on the pages).  `begin` and `end` are
+ * hipEvent_t handles, or NULL to disarm.  The next ssm_bwd call that runs the
+ * chunked MFMA path records `begin` on its stream immediately before its
+ * per-block backward kernel and `end` immediately after it, then disarms the
+ * hook; every other call ignores it.  The hook is process-global: arm it from
+ * one thread around one call.  Nothing else changes in the call.
+ */
+void ssm_profile_next_bwd_block(void *begin, void *end);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,117 @@
+"""GPU parity of the chunked MFMA backward (bf16 x/B/C/dy, headdim 64, dstate 128).
+
+Tolerance 2e-2 scaled error on dx, dB, dC, ddt, dA, dD, dh0 (bf16 MFMA
+operands, fp32 accumulation, fp64 final dA/dD sums).  Small problems span
+several 64-token blocks, partial chunks and ragged tails; the full prefill
+workload (batch 4, 256 heads, T = 4096) is checked on one whole group over all
+batches (so dA/dD of its heads are complete); the long-context workload
+(T = 131,072, 512 saved chunk states per head) is checked per head over the
+full length and on all heads of a group over the final 1024 tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from backward_mamba_ssd_amd import inputs
+from oracle import oracle
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+dev = torch.device("cuda:0")
+GRADS = ("dx", "dB", "dC", "ddt", "dA", "dD", "dh0")
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    from backward_mamba_ssd_amd import ssm as m
+    return m
+
+
+def _run(ssm, pr, L):
+    y, hf, cs = ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                                    h0=pr["h0"], chunk=L)
+    g = ssm.ssm_bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], cs, pr["dy"],
+                    dh_final=pr["dh_final"], chunk=L)
+    return y, hf, cs, g
+
+
+@pytest.mark.parametrize("t,L,h0,dhf", [(64, 64, "zero", False), (200, 64, "randn", True),
+                                        (320, 128, "zero", True), (513, 256, "randn", False),
+                                        (37, 64, "randn", True), (700, 192, "zero", True)])
+def test_backward_matches_oracle(ssm, t, L, h0, dhf):
+    b, h, p, n, g = 2, 8, 64, 128, 2
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 300 + t, dev, h0=h0, dh_final=dhf)
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
+    _, _, _, gr = _run(ssm, pr, L)
+    ref = oracle.bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], pr["dy"],
+                     h0=pr["h0"], dh_final=pr["dh_final"])
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert_close(k, gr[k], ref[k], 2e-2)
+
+
+def test_backward_deterministic(ssm):
+    b, t, h, p, n, g, L = 2, 300, 8, 64, 128, 2, 128
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 5, dev, h0="randn", dh_final=True)
+    _, _, _, g1 = _run(ssm, pr, L)
+    _, _, _, g2 = _run(ssm, pr, L)
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert torch.equal(g1[k], g2[k]), k
+
+
+def test_full_prefill_workload_one_group(ssm):
+    w = inputs.WORKLOADS["prefill_b4_t4096"]
+    pr = inputs.make_workload_problem(w, dev)
+    _, _, _, gr = _run(ssm, pr, w.chunk)
+    torch.cuda.synchronize()
+    hpg = w.nheads // w.ngroups
+    gg = 5
+    hs = slice(gg * hpg, (gg + 1) * hpg)
+    print(f"oracle backward: all batches, group {gg} ({hpg} heads)", flush=True)
+    ref = oracle.bwd(pr["x"][:, :, hs], pr["B"][:, :, gg:gg + 1], pr["C"][:, :, gg:gg + 1],
+                     pr["dt"][:, :, hs], pr["A"][hs], pr["D"][hs], pr["dy"][:, :, hs])
+    assert_close("dx", gr["dx"][:, :, hs], ref["dx"], 2e-2)
+    assert_close("dB", gr["dB"][:, :, gg:gg + 1], ref["dB"], 2e-2)
+    assert_close("dC", gr["dC"][:, :, gg:gg + 1], ref["dC"], 2e-2)
+    assert_close("ddt", gr["ddt"][:, :, hs], ref["ddt"], 2e-2)
+    assert_close("dA", gr["dA"][hs], ref["dA"], 2e-2)
+    assert_close("dD", gr["dD"][hs], ref["dD"], 2e-2)
+    assert_close("dh0", gr["dh0"][:, hs], ref["dh0"], 2e-2)
+
+
+def test_long_context_workload(ssm):
+    w = inputs.WORKLOADS["long_b1_t131072"]
+    pr = inputs.make_workload_problem(w, dev)
+    y, hf, cs, gr = _run(ssm, pr, w.chunk)
+    torch.cuda.synchronize()
+    assert cs.shape[2] == w.seqlen // w.chunk == 512
+    hpg = w.nheads // w.ngroups
+    # per head, whole sequence (dx, ddt, dA, dD, dh0 of a head depend on that head only)
+    for h in (0, 131):
+        gg = h // hpg
+        print(f"oracle long head {h}", flush=True)
+        sub = dict(x=pr["x"][:, :, h:h + 1], B=pr["B"][:, :, gg:gg + 1],
+                   C=pr["C"][:, :, gg:gg + 1], dt=pr["dt"][:, :, h:h + 1], A=pr["A"][h:h + 1],
+                   D=pr["D"][h:h + 1])
+        rf = oracle.fwd(**sub, chunk=w.chunk, want_chunk_states=True)
+        assert_close("y", y[:, :, h:h + 1], rf["y"], 2e-2)
+        assert_close("chunk_states", cs[:, h:h + 1], rf["chunk_states"], 2e-2)
+        rb = oracle.bwd(**sub, dy=pr["dy"][:, :, h:h + 1])
+        for k, got in (("dx", gr["dx"][:, :, h:h + 1]), ("ddt", gr["ddt"][:, :, h:h + 1]),
+                       ("dA", gr["dA"][h:h + 1]), ("dD", gr["dD"][h:h + 1]),
+                       ("dh0", gr["dh0"][:, h:h + 1])):
+            assert_close(k, got, rb[k], 2e-2)
+    # all heads of one group over the last 1024 tokens (a suffix: its gradients
+    # need no later tokens); the window starts from the saved chunk state
+    gg, win = 6, 1024
+    hs = slice(gg * hpg, (gg + 1) * hpg)
+    t0 = w.seqlen - win
+    print(f"oracle long group {gg} suffix window", flush=True)
+    rb = oracle.bwd(pr["x"][:, t0:, hs], pr["B"][:, t0:, gg:gg + 1], pr["C"][:, t0:, gg:gg + 1],
+                    pr["dt"][:, t0:, hs], pr["A"][hs], pr["D"][hs], pr["dy"][:, t0:, hs],
+                    h0=cs[:, hs, t0 // w.chunk])
+    assert_close("dB window", gr["dB"][:, t0:, gg:gg + 1], rb["dB"], 2e-2)
+    assert_close("dC window", gr["dC"][:, t0:, gg:gg + 1], rb["dC"], 2e-2)
+    assert_close("dx window", gr["dx"][:, t0:, hs], rb["dx"], 2e-2)
+    assert_close("ddt window", gr["ddt"][:, t0:, hs], rb["ddt"], 2e-2)
