@@ -1,0 +1,122 @@
+"""Full-size decode and checkpoint/replay workloads on the GPU.
+
+Decode: 64 sequences x 48 layers of [256, 64, 128] fp32 states (24 GiB), one
+token per sequence per layer, 100 steps, in place.  Sampled (sequence, layer)
+pairs are checked against the fp64 oracle stepped over the same 100 tokens:
+states at 1e-5 (fp32 recurrence on identical inputs), the bf16 y of every step
+at 2e-2.
+
+Checkpoint/replay: batch 16, T = 16384, checkpoint j = live state after 1024*j
+tokens (j = 0 is the initial state), stored as fp32 and as SR16.  Checked:
+  - SR16 bits of every checkpoint equal the oracle's SR16 of the same fp32
+    values (bit-exact, all 33.5 M elements of each of the 16 checkpoints);
+  - exact replay of 1024 tokens from fp32 checkpoint j equals checkpoint j+1
+    bit for bit ("Nemotron 3 Ultra: replaying a rounded state", section
+    "Recovering the state by replay");
+  - live states at the checkpoints match the fp64 oracle on sampled heads;
+  - SR16 replay of the last 1..1024 tokens in lockstep with the live state:
+    drift_max never exceeds the checkpoint's rounding error (retention <= 1,
+    section "The Mamba state update") beyond fp32 noise, and drift_max after
+    1024 tokens equals the directly measured max |replayed - live|.
+"""
+import numpy as np
+import pytest
+import torch
+
+from backward_mamba_ssd_amd import inputs
+from oracle import oracle
+from tests.parity import assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+dev = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    from backward_mamba_ssd_amd import ssm as m
+    return m
+
+
+def test_decode_workload(ssm):
+    w = inputs.WORKLOADS["decode_s64_l48"]
+    layers, steps = w.extra["layers"], w.extra["steps"]
+    pr = inputs.make_decode_problem(w.batch, layers, steps, w.nheads, w.headdim, w.dstate,
+                                    w.ngroups, w.seed, dev)
+    pairs = [(0, 0), (63, 47), (17, 5), (40, 23)]
+    ref_state = {pl: to_np(pr["state"][pl[1], pl[0]:pl[0] + 1]).copy() for pl in pairs}
+    y = torch.empty((layers, w.batch, w.nheads, w.headdim), dtype=torch.bfloat16, device=dev)
+    worst = 0.0
+    for s in range(steps):
+        for l in range(layers):
+            ssm.ssm_decode_step(pr["state"][l], pr["x"][s, l], pr["B"][s, l], pr["C"][s, l],
+                                pr["dt"][s, l], pr["A"][l], pr["D"][l], y=y[l])
+        if s % 10 == 0 or s == steps - 1:
+            torch.cuda.synchronize()
+        for (q, l) in pairs:
+            ry = oracle.decode_step(ref_state[(q, l)], pr["x"][s, l, q:q + 1],
+                                    pr["B"][s, l, q:q + 1], pr["C"][s, l, q:q + 1],
+                                    pr["dt"][s, l, q:q + 1], pr["A"][l], pr["D"][l])
+            gy = to_np(y[l, q:q + 1])
+            err = float(np.max(np.abs(gy - ry)) / np.max(np.abs(ry)))
+            worst = max(worst, err)
+            assert err <= 2e-2, (s, q, l, err)
+    print(f"  worst y scaled error over {steps} steps: {worst:.3e}")
+    torch.cuda.synchronize()
+    for (q, l) in pairs:
+        assert_close(f"state seq {q} layer {l}", pr["state"][l, q:q + 1], ref_state[(q, l)], 1e-5)
+
+
+def test_checkpoint_replay_workload(ssm):
+    w = inputs.WORKLOADS["ckpt_replay_b16_t16384"]
+    L = w.chunk  # checkpoint interval 1024
+    pr = inputs.make_workload_problem(w, dev, with_dy=False)
+    nck = w.seqlen // L
+    ck = [torch.zeros((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)]
+    for j in range(nck):
+        ck.append(ssm.ssm_replay(ck[-1], pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                                 j * L, L)["state"])
+    torch.cuda.synchronize()
+    seed = 20261202
+    # SR16 bits: GPU vs oracle on the same fp32 values
+    bits = []
+    for j in range(nck):
+        bj = ssm.ssm_checkpoint_sr16(ck[j], seed, j)
+        torch.cuda.synchronize()
+        want = oracle.sr16(ck[j].cpu().numpy(), seed, j, 0)
+        got = bj.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), (j, int(np.sum(got != want)))
+        bits.append(bj)
+    print(f"  SR16 bit-exact on {nck} checkpoints x {ck[0].numel()} elements")
+    # exact replay from fp32 checkpoints reproduces the next checkpoint bit for bit
+    for j in range(nck):
+        again = ssm.ssm_replay(ck[j], pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                               j * L, L)["state"]
+        assert torch.equal(again, ck[j + 1]), j
+    # live states against the fp64 oracle on sampled (batch, head) pairs
+    hpg = w.nheads // w.ngroups
+    for (bb, hh) in ((0, 0), (15, 255), (7, 100)):
+        gg = hh // hpg
+        ref = oracle.fwd(pr["x"][bb:bb + 1, :, hh:hh + 1], pr["B"][bb:bb + 1, :, gg:gg + 1],
+                         pr["C"][bb:bb + 1, :, gg:gg + 1], pr["dt"][bb:bb + 1, :, hh:hh + 1],
+                         pr["A"][hh:hh + 1], pr["D"][hh:hh + 1], chunk=L, want_chunk_states=True)
+        for j in (4, 11):
+            assert_close(f"live ckpt {j} b{bb} h{hh}", ck[j][bb:bb + 1, hh:hh + 1],
+                         ref["chunk_states"][:, :, j], 1e-5)
+        assert_close(f"live final b{bb} h{hh}", ck[nck][bb:bb + 1, hh:hh + 1], ref["h_final"], 1e-5)
+    # SR16 replay with the live copy in lockstep
+    eps = float(torch.finfo(torch.float32).eps)
+    for j in (0, 1, 8, nck - 1):
+        out = ssm.ssm_replay(bits[j], pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                             j * L, L, live=ck[j])
+        torch.cuda.synchronize()
+        d0 = float((bits[j].view(torch.float16).float() - ck[j]).abs().max())
+        dmax = out["drift_max"].cpu().numpy()
+        dmean = out["drift_mean"].cpu().numpy()
+        scale = max(float(ck[j].abs().max()), float(ck[j + 1].abs().max()))
+        noise = 8 * L * eps * scale
+        direct = float((out["state"] - ck[j + 1]).abs().max())
+        print(f"  ckpt {j}: |delta0| {d0:.3e}, drift_max r=1 {dmax[0]:.3e} r=1024 {dmax[-1]:.3e}, "
+              f"drift_mean r=1024 {dmean[-1]:.3e}")
+        assert dmax[-1] == direct
+        assert np.all(dmax <= d0 + noise)
+        assert np.all(dmean <= dmax)
