@@ -16,12 +16,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// float32 -> bf16, round to nearest even (NaN stays NaN).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// float32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+// Two floats -> two bf16 packed in one dword (low half = a), one instruction.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
 // Scalar load/store of a storage dtype as float.

@@ -76,8 +76,8 @@ __global__ void __launch_bounds__(256) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
             G[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    const int yt0 = 2 * (tid >> 3), yp0 = (tid & 7) * 8;   // dy: 2 tokens x 8 channels
-    const int ct0 = 4 * (tid >> 4), cn0 = (tid & 15) * 8;  // C: 4 tokens x 8 coords
+    const int yt0 = map64_tok(tid), yp0 = map64_col(tid);    // dy: 2 tokens x 8 channels
+    const int ct0 = map128_tok(tid), cn0 = map128_col(tid);  // C: 4 tokens x 8 coords
     u16x8 yr[2], cr[4];
     float dtr = 0.f;
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -119,9 +119,8 @@ __global__ void __launch_bounds__(256) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
             const float e0 = __expf(lam[yt0]), e1 = __expf(lam[yt0 + 1]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = f32_to_bf16(bf16_to_f32(yr[0][e]) * e0);
-                const uint32_t hi = f32_to_bf16(bf16_to_f32(yr[1][e]) * e1);
-                *reinterpret_cast<uint32_t *>(&sm.EdYT[(yp0 + e) * kS64 + yt0]) = lo | (hi << 16);
+                *reinterpret_cast<uint32_t *>(&sm.EdYT[(yp0 + e) * kS64 + yt0]) =
+                    pack2_bf16(bf16_to_f32(yr[0][e]) * e0, bf16_to_f32(yr[1][e]) * e1);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -208,8 +207,8 @@ __global__ void __launch_bounds__(256) ssd_bwd_block_kernel(SsdBwdArgs a) {
     bf16_t *U = sm.U;
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
-    const int rt0 = 2 * (tid >> 3), rp0 = (tid & 7) * 8;   // [tok][p] rows: 2 tokens x 8 channels
-    const int nt0 = 4 * (tid >> 4), nn0 = (tid & 15) * 8;  // [tok][n] rows: 4 tokens x 8 coords
+    const int rt0 = map64_tok(tid), rp0 = map64_col(tid);    // [tok][p] rows: 2 tokens x 8 channels
+    const int nt0 = map128_tok(tid), nn0 = map128_col(tid);  // [tok][n] rows: 4 tokens x 8 coords
 
     auto load_rows64 = [&](const bf16_t *src, int64_t t0, int h, u16x8 *r) {
 #pragma unroll
@@ -306,12 +305,10 @@ __global__ void __launch_bounds__(256) ssd_bwd_block_kernel(SsdBwdArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) coef[i] = __expf(lam_end - sm.lam[nt0 + i]) * sm.dt[nt0 + i];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    u16x4 v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(bf16_to_f32(br[i][e]) * coef[i]);
-                    *reinterpret_cast<u16x4 *>(&BsT[(nn0 + e) * kS64 + nt0]) = v;
-                }
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<u16x4 *>(&BsT[(nn0 + e) * kS64 + nt0]) =
+                        pack4(bf16_to_f32(br[0][e]) * coef[0], bf16_to_f32(br[1][e]) * coef[1],
+                              bf16_to_f32(br[2][e]) * coef[2], bf16_to_f32(br[3][e]) * coef[3]);
             }
             __syncthreads();
             const float el = __expf(lam_end);
@@ -344,9 +341,8 @@ __global__ void __launch_bounds__(256) ssd_bwd_block_kernel(SsdBwdArgs a) {
                 const float e0 = __expf(sm.lam[rt0]), e1 = __expf(sm.lam[rt0 + 1]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t lo = f32_to_bf16(bf16_to_f32(yr[0][e]) * e0);
-                    const uint32_t hi = f32_to_bf16(bf16_to_f32(yr[1][e]) * e1);
-                    *reinterpret_cast<uint32_t *>(&EdYT[(rp0 + e) * kS64 + rt0]) = lo | (hi << 16);
+                    *reinterpret_cast<uint32_t *>(&EdYT[(rp0 + e) * kS64 + rt0]) =
+                        pack2_bf16(bf16_to_f32(yr[0][e]) * e0, bf16_to_f32(yr[1][e]) * e1);
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {

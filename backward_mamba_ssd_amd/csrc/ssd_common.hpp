@@ -42,12 +42,20 @@ __device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
 }
 
 __device__ __forceinline__ u16x4 pack4(float a, float b, float c, float d) {
-    u16x4 v;
-    v[0] = f32_to_bf16(a);
-    v[1] = f32_to_bf16(b);
-    v[2] = f32_to_bf16(c);
-    v[3] = f32_to_bf16(d);
-    return v;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = {pack2_bf16(a, b), pack2_bf16(c, d)};
+    return __builtin_bit_cast(u16x4, w);
 }
+
+// Staging thread maps (256 threads).  Transposed LDS writes are the bank-hot
+// accesses; these maps spread one wave's lanes over all 64 banks.
+//  [tok][p] source rows -> [p][tok] tile: thread covers 2 tokens x 8 channels,
+//  lanes of a wave vary the token pair (32 pairs) and 2 channel blocks.
+__device__ __forceinline__ int map64_tok(int tid) { return 2 * (tid & 31); }
+__device__ __forceinline__ int map64_col(int tid) { return 8 * ((tid >> 5) & 1) + 16 * (tid >> 6); }
+//  [tok][n] source rows -> [n][tok] tile: thread covers 4 tokens x 8 coords,
+//  lanes vary the token quad (16 quads) and 4 coordinate blocks.
+__device__ __forceinline__ int map128_tok(int tid) { return 4 * (tid & 15); }
+__device__ __forceinline__ int map128_col(int tid) { return 8 * ((tid >> 4) & 3) + 32 * (tid >> 6); }
 
 }  // namespace ssm

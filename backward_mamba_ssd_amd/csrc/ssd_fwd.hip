@@ -78,8 +78,8 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
     }
 
     // cooperative load mapping
-    const int xt0 = 2 * (tid >> 3), xp0 = (tid & 7) * 8;   // x: 2 tokens x 8 channels
-    const int bt0 = 4 * (tid >> 4), bn0 = (tid & 15) * 8;  // B, C: 4 tokens x 8 coords
+    const int xt0 = map64_tok(tid), xp0 = map64_col(tid);    // x: 2 tokens x 8 channels
+    const int bt0 = map128_tok(tid), bn0 = map128_col(tid);  // B, C: 4 tokens x 8 coords
     u16x8 xr[2], br[4], cr[4];
     float dtr = 0.f;
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -128,12 +128,10 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) coef[i] = __expf(lam_end - lam[bt0 + i]) * dts[bt0 + i];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                u16x4 v;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(bf16_to_f32(br[i][e]) * coef[i]);
-                *reinterpret_cast<u16x4 *>(&sm.BsT[(bn0 + e) * kS64 + bt0]) = v;
-            }
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<u16x4 *>(&sm.BsT[(bn0 + e) * kS64 + bt0]) =
+                    pack4(bf16_to_f32(br[0][e]) * coef[0], bf16_to_f32(br[1][e]) * coef[1],
+                          bf16_to_f32(br[2][e]) * coef[2], bf16_to_f32(br[3][e]) * coef[3]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const uint32_t pr = static_cast<uint32_t>(xr[0][e]) | (static_cast<uint32_t>(xr[1][e]) << 16);
@@ -157,7 +155,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
             const int i = 16 * wave + lr;
             const float lam_i = lam[i];
             for (int jt = 0; jt < 4; ++jt) {
-                u16x4 out = {0, 0, 0, 0};
+                float gv[4] = {0.f, 0.f, 0.f, 0.f};
                 if (jt <= wave) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -167,11 +165,10 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int j = 16 * jt + lq + v;
-                        const float gm = (j <= i) ? acc[v] * __expf(lam_i - lam[j]) * dts[j] : 0.f;
-                        out[v] = f32_to_bf16(gm);
+                        gv[v] = (j <= i) ? acc[v] * __expf(lam_i - lam[j]) * dts[j] : 0.f;
                     }
                 }
-                *reinterpret_cast<u16x4 *>(&sm.Gm[i * kS64 + 16 * jt + lq]) = out;
+                *reinterpret_cast<u16x4 *>(&sm.Gm[i * kS64 + 16 * jt + lq]) = pack4(gv[0], gv[1], gv[2], gv[3]);
             }
         }
         __syncthreads();
@@ -180,10 +177,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
-            u16x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = f32_to_bf16(H[q][e]);
-            *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = v;
+            *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(H[q][0], H[q][1], H[q][2], H[q][3]);
         }
         __syncthreads();
         // (5) outputs: Y^T rows p in [16w, 16w+16), 16 tokens at a time
@@ -206,10 +200,9 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
                 if (t < T) {
                     const int64_t off = ((b * T + t) * a.H + h) * kP + 16 * wave + lq;
                     const u16x4 xv = *reinterpret_cast<const u16x4 *>(x + off);
-                    u16x4 yv;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) yv[v] = f32_to_bf16(fmaf(Dh, bf16_to_f32(xv[v]), acc[v]));
-                    *reinterpret_cast<u16x4 *>(y + off) = yv;
+                    *reinterpret_cast<u16x4 *>(y + off) =
+                        pack4(fmaf(Dh, bf16_to_f32(xv[0]), acc[0]), fmaf(Dh, bf16_to_f32(xv[1]), acc[1]),
+                              fmaf(Dh, bf16_to_f32(xv[2]), acc[2]), fmaf(Dh, bf16_to_f32(xv[3]), acc[3]));
                 }
             }
         }
