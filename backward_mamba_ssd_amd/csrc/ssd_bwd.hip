@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(256) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
                 *reinterpret_cast<float4 *>(dst + p * kN + n) = make_float4(G[q][0], G[q][1], G[q][2], G[q][3]);
             }
         }
-        if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(dtr * Ah, lane);
+        if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(dtr * Ah);
         __syncthreads();
         const float *lam = sm.lam[buf];
         const float lam_end = lam[kLs - 1];
@@ -157,31 +157,35 @@ __global__ void __launch_bounds__(256) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
 // ===========================================================================
 // 2. per (batch, group, chunk, block): everything else
 // ===========================================================================
-// phase-aliased region U (bf16 element offsets)
-constexpr int kT64 = kLs * kS64;   // a [64][72] tile
-constexpr int kT128 = kN * kS64;   // a [128][72] tile
-// block phase
-constexpr int oX = 0, odY = kT64, odYT = 2 * kT64, oQT = 3 * kT64, oHT = 4 * kT64;
-constexpr int odHT = oHT + kT128, odH = odHT + kT128, kUsize = odH + kP * kS128;
-// recompute phase
-constexpr int oR1 = 0, oR2 = kT64;
-// final phase
-constexpr int oK = 0, oKT = kT64, oBT = 2 * kT64, oCT = 2 * kT64 + kT128;
-static_assert(oCT + kT128 <= kUsize, "final phase fits");
+// All LDS tiles keep the natural global row layout ([tok][p] or [tok][n]);
+// operands that contract over a tile's row index are read with frag_tr.
+//
+// Per head the block-entry state and block-exit gradient are single products
+// over the chunk's other blocks, with chunk-local cumulative Lc:
+//   H_k^T  = exp(Lc[s]) H_c^T + sum_{tok < 64k} B_tok (x) [exp(Lc[s]-Lc[tok]) dt_tok x_tok]
+//   dH^T   = exp(Lc[end]-Lc[e]) dH_{c+1}^T + sum_{tok > e} C_tok (x) [exp(Lc[tok]-Lc[e]) dy_tok]
+// (s = last token before block k, e = last token of block k; every exponent <= 0).
+constexpr int kT64 = kLs * kS64;    // a [64][72] tile
+constexpr int kT128 = kLs * kS128;  // a [64][136] tile
+constexpr int kMaxBlk = 4;          // blocks per chunk (chunk <= 256)
+
+constexpr int kBlkThreads = 512;  // 8 waves: w = 4*wh + wq
 
 struct BlkSmem {
-    bf16_t B[kLs * kS128];  // block rows [j][n]
-    bf16_t C[kLs * kS128];  // block rows [i][n]
-    bf16_t U[kUsize];
-    float lam[kLs], dt[kLs];
-    float row[kLs];
-    float col[4][kLs], off[4][kLs], fin[4][kLs], dd[4][kLs];
-    float dot[4], dd_sum[4];
+    bf16_t B[kT128];                    // block k rows of B [j][n]
+    bf16_t C[kT128];                    // block k rows of C [i][n]
+    bf16_t chainBC[(kMaxBlk - 1) * kT128];  // B rows of earlier blocks / C rows of later blocks
+    bf16_t R[2 * kT128];                // per head: scaled x / dy rows of the other blocks,
+                                        // then H and dH in bf16 ([p][n])
+    bf16_t X[kT64], dY[kT64], QT[kT64]; // block k rows of x, dy; Q^T [j][i]
+    float lam[2][kMaxBlk * kLs], dt[2][kMaxBlk * kLs];  // chunk-local, by head parity
+    float row[2][kLs], col[4][kLs], dd[4][kLs], off[8][kLs], fin[8][kLs];
+    float dot[8], dd_sum[8];
 };
+static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the state tiles");
 
-__global__ void __launch_bounds__(256) ssd_bwd_block_kernel(SsdBwdArgs a) {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    BlkSmem &sm = *reinterpret_cast<BlkSmem *>(smem_raw);
+__global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a) {
+    __shared__ BlkSmem sm;
     const int nb = static_cast<int>(a.L / kLs);
     int id = xcd_remap(blockIdx.x, gridDim.x);
     const int k = id % nb;
@@ -196,422 +200,396 @@ __global__ void __launch_bounds__(256) ssd_bwd_block_kernel(SsdBwdArgs a) {
     const int64_t cend = (cstart + a.L < T) ? cstart + a.L : T;
     const int nbc = static_cast<int>((cend - cstart + kLs - 1) / kLs);
     const int hpg = a.H / a.G;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int wq = wave & 3, wh = wave >> 2;
+    // Lane-derived indices are re-formed at the top of every head iteration from a
+    // value the compiler cannot see through, so the LDS addresses built from them are
+    // computed next to their uses instead of occupying registers across the loop.
+    int tid, lane, lr, lk, lq, pr_tok, pr_col;
+    auto refresh_lane = [&]() {
+        tid = static_cast<int>(threadIdx.x);
+        asm volatile("" : "+v"(tid));
+        lane = tid & 63;
+        lr = lane & 15;
+        lk = (lane >> 4) * 8;
+        lq = (lane >> 4) * 4;
+        pr_tok = tid >> 3;
+        pr_col = (tid & 7) * 8;
+    };
+    refresh_lane();
     constexpr int PN = kP * kN;
     const bf16_t *x = static_cast<const bf16_t *>(a.x);
     const bf16_t *dy = static_cast<const bf16_t *>(a.dy);
     const bf16_t *Bm = static_cast<const bf16_t *>(a.B);
     const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
     bf16_t *dx = static_cast<bf16_t *>(a.dx);
-    bf16_t *U = sm.U;
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    // row staging: [tok][p] tiles: one 16-byte chunk per thread; [tok][n] tiles: two
+    const int nr_tok = tid >> 4, nr_col = (tid & 15) * 8;
 
-    const int rt0 = map64_tok(tid), rp0 = map64_col(tid);    // [tok][p] rows: 2 tokens x 8 channels
-    const int nt0 = map128_tok(tid), nn0 = map128_col(tid);  // [tok][n] rows: 4 tokens x 8 coords
-
-    auto load_rows64 = [&](const bf16_t *src, int64_t t0, int h, u16x8 *r) {
+    auto load_rows_n = [&](const bf16_t *src, int64_t t0, bf16_t *dst) {
+        u16x8 r[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int64_t t = t0 + rt0 + i;
-            r[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(src + ((b * T + t) * a.H + h) * kP + rp0) : z8;
+            const int64_t t = t0 + nr_tok + 32 * i;
+            r[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(src + ((b * T + t) * a.G + g) * kN + nr_col) : z8;
         }
-    };
-    auto load_rows128 = [&](const bf16_t *src, int64_t t0, u16x8 *r) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t t = t0 + nt0 + i;
-            r[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(src + ((b * T + t) * a.G + g) * kN + nn0) : z8;
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<u16x8 *>(&dst[(nr_tok + 32 * i) * kS128 + nr_col]) = r[i];
+    };
+    // head-independent tiles: block k B and C rows, B rows of earlier blocks, C rows of later ones
+    load_rows_n(Bm, tk, sm.B);
+    load_rows_n(Cm, tk, sm.C);
+    for (int kb = 0; kb < nbc; ++kb) {
+        if (kb == k) continue;
+        const int slot = kb < k ? kb : kb - 1;
+        load_rows_n(kb < k ? Bm : Cm, cstart + static_cast<int64_t>(kb) * kLs, sm.chainBC + slot * kT128);
+    }
+
+    // per-head inputs held in registers one head ahead
+    u16x8 xr[kMaxBlk];  // x rows of blocks <= k, dy rows of blocks > k
+    u16x8 yk;           // dy rows of block k
+    float dtr[4];
+    // Per-head global accesses: a wave-uniform base pointer plus a 32-bit lane offset
+    // (token strides within a chunk stay far below 2^31 elements).
+    const int tok_stride = a.H * kP;                       // elements between tokens of x, dy, dx
+    const int nvalid = static_cast<int>(cend - cstart);    // valid tokens of this chunk
+    auto prefetch = [&](int h) {
+        const int64_t hb = ((static_cast<int64_t>(b) * T + cstart) * a.H + h) * kP;
+        const bf16_t *xh = x + hb, *yh = dy + hb;
+        const uint32_t row_off = static_cast<uint32_t>(pr_tok * tok_stride + pr_col);
+#pragma unroll
+        for (int kb = 0; kb < kMaxBlk; ++kb) {
+            const bf16_t *src = (kb <= k ? xh : yh) + static_cast<uint32_t>(kb * kLs * tok_stride);
+            xr[kb] = (kb < nbc && kb * kLs + pr_tok < nvalid) ? *reinterpret_cast<const u16x8 *>(src + row_off) : z8;
+        }
+        yk = (k * kLs + pr_tok < nvalid) ? *reinterpret_cast<const u16x8 *>(yh + static_cast<uint32_t>(k * kLs * tok_stride) + row_off) : z8;
+        if (wave == 0) {
+            const float *dth = a.dt + (static_cast<int64_t>(b) * T + cstart) * a.H + h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * lane + e;
+                dtr[e] = (t < nvalid) ? dth[static_cast<uint32_t>(t * a.H)] : 0.f;
+            }
         }
     };
-    auto load_dt = [&](int64_t t0, int h) -> float {
-        const int64_t t = t0 + lane;
-        return (t < T) ? a.dt[(b * T + t) * a.H + h] : 0.f;
+    // chunk-local cumulative log-retention of head h (wave 0; lane = 4 tokens)
+    auto scan = [&](int h, int par) {
+        const float Ah = a.A[h];
+        const float v0 = dtr[0] * Ah, v1 = v0 + dtr[1] * Ah, v2 = v1 + dtr[2] * Ah, v3 = v2 + dtr[3] * Ah;
+        const float off = wave_prefix_sum(v3) - v3;
+        sm.lam[par][4 * lane + 0] = off + v0;
+        sm.lam[par][4 * lane + 1] = off + v1;
+        sm.lam[par][4 * lane + 2] = off + v2;
+        sm.lam[par][4 * lane + 3] = off + v3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dt[par][4 * lane + e] = dtr[e];
+    };
+    // states in accumulators, [n][p]: n-tile = wave, p-tiles 0..3
+    f32x4 Hs[4], dHs[4];
+    auto load_states = [&](int h) {
+        const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+        const float *hc = a.chunk_states + (bh * a.nchunks + c) * PN;
+        const float *dc = a.dstates + (bh * a.nchunks + c) * PN;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = 16 * wave + lq, p = 16 * q + lr;
+            const float4 u = *reinterpret_cast<const float4 *>(hc + p * kN + n);
+            const float4 v = *reinterpret_cast<const float4 *>(dc + p * kN + n);
+            Hs[q] = f32x4{u.x, u.y, u.z, u.w};
+            dHs[q] = f32x4{v.x, v.y, v.z, v.w};
+        }
     };
 
-    // block rows of B and C, and the group's Gram tile G[i][j] (wave w: i-tile w)
-    {
-        u16x8 br[4], cr[4];
-        load_rows128(Bm, tk, br);
-        load_rows128(Cm, tk, cr);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u16x8 *>(&sm.B[(nt0 + i) * kS128 + nn0]) = br[i];
-            *reinterpret_cast<u16x8 *>(&sm.C[(nt0 + i) * kS128 + nn0]) = cr[i];
-        }
-    }
+    const int h0 = g * hpg;
+    prefetch(h0);
+    load_states(h0);
+    if (wave == 0) scan(h0, 0);
     __syncthreads();
-    f32x4 Gt[4];
+    // Gram tiles of block k, [i][j]: i-tile wq, j-tiles 2wh, 2wh+1
+    f32x4 Gt[2];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        Gt[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (jt <= wave) {
+    for (int q = 0; q < 2; ++q) {
+        const int jt = 2 * wh + q;
+        Gt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (jt <= wq) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                Gt[jt] = mma16(&sm.C[(16 * wave + lr) * kS128 + 32 * kk + lk],
-                               &sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk], Gt[jt]);
+                Gt[q] = mma16(&sm.C[(16 * wq + lr) * kS128 + 32 * kk + lk],
+                              &sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk], Gt[q]);
         }
     }
-    f32x4 Ks[4];                 // sum over heads of K, [i][j] like Gt
-    f32x4 dCa[8], dBa[8];        // [n][tok]: tile q: nt = 2w + q/4, tt = q%4
+    f32x4 Ks[2], dCa[4], dBa[4];  // Ks like Gt; dCa/dBa [n][tok]: n-tile = wave, tok-tiles 0..3
 #pragma unroll
-    for (int q = 0; q < 4; ++q) Ks[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 2; ++q) Ks[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
         dCa[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         dBa[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const int kS = 64 * k - 1;              // chunk-local index of the token before block k
+    const int kE = 64 * k + kLs - 1;        // last token of block k
+    const int kEnd = 64 * nbc - 1;          // last (padded) token of the chunk
+    const int base = 64 * k;
 
     for (int hh = 0; hh < hpg; ++hh) {
-        const int h = g * hpg + hh;
+        refresh_lane();
+        const int h = h0 + hh, par = hh & 1;
         const int64_t bh = static_cast<int64_t>(b) * a.H + h;
         const float Ah = a.A[h], Dh = a.D[h];
-        // entering state and exit gradient of block k, [p][n]: p = 16w + lq + v, n = 16nt + lr
-        f32x4 Hs[8], dHs[8];
-        {
-            const float *hc = a.chunk_states + (bh * a.nchunks + c) * PN;
-            const float *dc = a.dstates + (bh * a.nchunks + c) * PN;
+        const float *lam = sm.lam[par], *dts = sm.dt[par];
+        const float lam_blk0 = kS >= 0 ? lam[kS] : 0.f;  // block-local Lam_i = lam[base+i] - lam_blk0
+        const float lam_e = lam[kE];
+        // ---- S1: stage this head's rows (scaled for the state products) ----
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int o = (16 * wave + lq + v) * kN + 16 * nt + lr;
-                    Hs[nt][v] = hc[o];
-                    dHs[nt][v] = dc[o];
-                }
+        for (int kb = 0; kb < kMaxBlk; ++kb) {
+            if (kb >= nbc) break;
+            const int tl = 64 * kb + pr_tok;  // chunk-local token
+            if (kb == k) {
+                *reinterpret_cast<u16x8 *>(&sm.X[pr_tok * kS64 + pr_col]) = xr[kb];
+                *reinterpret_cast<u16x8 *>(&sm.dY[pr_tok * kS64 + pr_col]) = yk;
+                continue;
             }
-        }
-        // forward over the earlier blocks of the chunk: H <- exp(Lam_63) H + X^T Bs
-        for (int kb = 0; kb < k; ++kb) {
-            const int64_t t0 = cstart + static_cast<int64_t>(kb) * kLs;
-            u16x8 xr[2], br[4];
-            load_rows64(x, t0, h, xr);
-            load_rows128(Bm, t0, br);
-            if (wave == 0) {
-                const float d = load_dt(t0, h);
-                sm.lam[lane] = wave_prefix_sum(d * Ah, lane);
-                sm.dt[lane] = d;
-            }
-            __syncthreads();
-            const float lam_end = sm.lam[kLs - 1];
-            {
-                bf16_t *XT = U + oR1, *BsT = U + oR2;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t pr = static_cast<uint32_t>(xr[0][e]) | (static_cast<uint32_t>(xr[1][e]) << 16);
-                    *reinterpret_cast<uint32_t *>(&XT[(rp0 + e) * kS64 + rt0]) = pr;
-                }
-                float coef[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) coef[i] = __expf(lam_end - sm.lam[nt0 + i]) * sm.dt[nt0 + i];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *reinterpret_cast<u16x4 *>(&BsT[(nn0 + e) * kS64 + nt0]) =
-                        pack4(bf16_to_f32(br[0][e]) * coef[0], bf16_to_f32(br[1][e]) * coef[1],
-                              bf16_to_f32(br[2][e]) * coef[2], bf16_to_f32(br[3][e]) * coef[3]);
-            }
-            __syncthreads();
-            const float el = __expf(lam_end);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                f32x4 acc = Hs[nt];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] *= el;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    acc = mma16(&U[oR1 + (16 * wave + lr) * kS64 + 32 * kk + lk],
-                                &U[oR2 + (16 * nt + lr) * kS64 + 32 * kk + lk], acc);
-                Hs[nt] = acc;
-            }
-        }
-        // reverse over the later blocks: dH <- exp(Lam_63) dH + (E dY)^T C
-        for (int kb = nbc - 1; kb > k; --kb) {
-            const int64_t t0 = cstart + static_cast<int64_t>(kb) * kLs;
-            u16x8 yr[2], cr[4];
-            load_rows64(dy, t0, h, yr);
-            load_rows128(Cm, t0, cr);
-            if (wave == 0) {
-                const float d = load_dt(t0, h);
-                sm.lam[lane] = wave_prefix_sum(d * Ah, lane);
-            }
-            __syncthreads();
-            const float lam_end = sm.lam[kLs - 1];
-            {
-                bf16_t *EdYT = U + oR1, *CT = U + oR2;
-                const float e0 = __expf(sm.lam[rt0]), e1 = __expf(sm.lam[rt0 + 1]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    *reinterpret_cast<uint32_t *>(&EdYT[(rp0 + e) * kS64 + rt0]) =
-                        pack2_bf16(bf16_to_f32(yr[0][e]) * e0, bf16_to_f32(yr[1][e]) * e1);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const u16x4 v = {cr[0][e], cr[1][e], cr[2][e], cr[3][e]};
-                    *reinterpret_cast<u16x4 *>(&CT[(nn0 + e) * kS64 + nt0]) = v;
-                }
-            }
-            __syncthreads();
-            const float el = __expf(lam_end);
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                f32x4 acc = dHs[nt];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] *= el;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    acc = mma16(&U[oR1 + (16 * wave + lr) * kS64 + 32 * kk + lk],
-                                &U[oR2 + (16 * nt + lr) * kS64 + 32 * kk + lk], acc);
-                dHs[nt] = acc;
-            }
-        }
-
-        // ---- block k ----
-        {
-            u16x8 xr[2], yr[2];
-            load_rows64(x, tk, h, xr);
-            load_rows64(dy, tk, h, yr);
-            if (wave == 0) {
-                const float d = load_dt(tk, h);
-                sm.lam[lane] = wave_prefix_sum(d * Ah, lane);
-                sm.dt[lane] = d;
-            }
-            __syncthreads();
-            bf16_t *X = U + oX, *dY = U + odY, *dYT = U + odYT;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                *reinterpret_cast<u16x8 *>(&X[(rt0 + i) * kS64 + rp0]) = xr[i];
-                *reinterpret_cast<u16x8 *>(&dY[(rt0 + i) * kS64 + rp0]) = yr[i];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t pr = static_cast<uint32_t>(yr[0][e]) | (static_cast<uint32_t>(yr[1][e]) << 16);
-                *reinterpret_cast<uint32_t *>(&dYT[(rp0 + e) * kS64 + rt0]) = pr;
-            }
-            float dotp = 0.f;
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const int p0 = 16 * wave + lq, n = 16 * nt + lr;
-                *reinterpret_cast<u16x4 *>(&U[oHT + n * kS64 + p0]) = pack4(Hs[nt][0], Hs[nt][1], Hs[nt][2], Hs[nt][3]);
-                *reinterpret_cast<u16x4 *>(&U[odHT + n * kS64 + p0]) = pack4(dHs[nt][0], dHs[nt][1], dHs[nt][2], dHs[nt][3]);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    U[odH + (p0 + v) * kS128 + n] = f32_to_bf16(dHs[nt][v]);
-                    dotp = fmaf(Hs[nt][v], dHs[nt][v], dotp);
-                }
-            }
-            dotp = wave_sum(dotp);
-            if (lane == 0) sm.dot[wave] = dotp;
+            const float cf = kb < k ? __expf(lam_blk0 - lam[tl]) * dts[tl] : __expf(lam[tl] - lam_e);
+            const int slot = kb < k ? kb : kb - 1;
+            const u16x8 v = xr[kb];
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * cf, bf16_to_f32(v[1]) * cf),
+                             pack2_bf16(bf16_to_f32(v[2]) * cf, bf16_to_f32(v[3]) * cf),
+                             pack2_bf16(bf16_to_f32(v[4]) * cf, bf16_to_f32(v[5]) * cf),
+                             pack2_bf16(bf16_to_f32(v[6]) * cf, bf16_to_f32(v[7]) * cf)};
+            *reinterpret_cast<u32x4 *>(&sm.R[slot * kT64 + pr_tok * kS64 + pr_col]) = w;
         }
         __syncthreads();
-        const float *lam = sm.lam, *dts = sm.dt;
-        const float lam_end = lam[kLs - 1];
-        // Phase I: dW = dY X^T, K, R = K G, Q = G M   (wave w: rows i in [16w, 16w+16))
+        if (hh + 1 < hpg) prefetch(h + 1);  // registers are free once staged
+        // ---- S2: state products over the other blocks; Phase I of block k ----
         {
-            const bf16_t *X = U + oX, *dY = U + odY;
-            bf16_t *QT = U + oQT;
-            float lam_i[4], rowacc[4] = {0.f, 0.f, 0.f, 0.f};
+            const float es = __expf(lam_blk0);
+            const float ee = __expf(lam[kEnd] - lam_e);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) lam_i[v] = lam[16 * wave + lq + v];
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                const int j = 16 * jt + lr;
-                f32x4 dW = {0.f, 0.f, 0.f, 0.f};
-                if (jt <= wave) {
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
-                        dW = mma16(&dY[(16 * wave + lr) * kS64 + 32 * kk + lk],
-                                   &X[(16 * jt + lr) * kS64 + 32 * kk + lk], dW);
-                }
-                const float lam_j = lam[j], dt_j = dts[j];
-                float q[4], colacc = 0.f;
+            for (int q = 0; q < 4; ++q) {
+                const int n0 = 16 * wave, p0 = 16 * q;
+                f32x4 hacc = Hs[q], gacc = dHs[q];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int i = 16 * wave + lq + v;
+                    hacc[v] *= es;
+                    gacc[v] *= ee;
+                }
+                for (int kb = 0; kb < nbc; ++kb) {
+                    if (kb == k) continue;
+                    const int slot = kb < k ? kb : kb - 1;
+                    const bf16_t *bc = sm.chainBC + slot * kT128;
+                    const bf16_t *xs = sm.R + slot * kT64;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
+                        const bf16x8 fb = frag_tr(xs, kS64, p0, 32 * kk, lane);
+                        if (kb < k) hacc = mfma(fa, fb, hacc);
+                        else gacc = mfma(fa, fb, gacc);
+                    }
+                }
+                Hs[q] = hacc;
+                dHs[q] = gacc;
+            }
+        }
+        // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile wq, j-tiles 2wh, 2wh+1)
+        {
+            float lam_i[4], rowacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) lam_i[v] = lam[base + 16 * wq + lq + v];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int jt = 2 * wh + q, j = 16 * jt + lr;
+                f32x4 dW = {0.f, 0.f, 0.f, 0.f};
+                if (jt <= wq) {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+                        dW = mma16(&sm.dY[(16 * wq + lr) * kS64 + 32 * kk + lk],
+                                   &sm.X[(16 * jt + lr) * kS64 + 32 * kk + lk], dW);
+                }
+                const float lam_j = lam[base + j], dt_j = dts[base + j];
+                float qv[4], colacc = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = 16 * wq + lq + v;
                     const float m = (j <= i) ? __expf(lam_i[v] - lam_j) : 0.f;
                     const float kv = dW[v] * m * dt_j;
-                    Ks[jt][v] += kv;
-                    const float r = kv * Gt[jt][v];
+                    Ks[q][v] += kv;
+                    const float r = kv * Gt[q][v];
                     rowacc[v] += r;
                     colacc += r;
-                    q[v] = Gt[jt][v] * m;
+                    qv[v] = Gt[q][v] * m;
                 }
-                *reinterpret_cast<u16x4 *>(&QT[j * kS64 + 16 * wave + lq]) = pack4(q[0], q[1], q[2], q[3]);
-                colacc += __shfl_xor(colacc, 16, 64);
-                colacc += __shfl_xor(colacc, 32, 64);
-                if (lane < 16) sm.col[wave][j] = colacc;
+                *reinterpret_cast<u16x4 *>(&sm.QT[j * kS64 + 16 * wq + lq]) = pack4(qv[0], qv[1], qv[2], qv[3]);
+                colacc = rows4_sum(colacc);
+                if (lane < 16) sm.col[wq][j] = colacc;
             }
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                float r = rowacc[v];
-                r += __shfl_xor(r, 1, 64);
-                r += __shfl_xor(r, 2, 64);
-                r += __shfl_xor(r, 4, 64);
-                r += __shfl_xor(r, 8, 64);
-                if (lr == 0) sm.row[16 * wave + lq + v] = r;
+                const float r = row16_sum(rowacc[v]);
+                if (lr == 0) sm.row[wh][16 * wq + lq + v] = r;
             }
         }
         __syncthreads();
-        // Phase II: dXpre^T = dY^T Q + w (dH B^T)   (wave w: p in [16w, 16w+16))
+        // ---- S3: block-entry state and exit gradient in bf16, [p][n] ----
+        bf16_t *Hb = sm.R, *dHb = sm.R + kT128;
         {
-            const bf16_t *X = U + oX, *dY = U + odY, *dYT = U + odYT, *QT = U + oQT, *dH = U + odH;
+            float dotp = 0.f;
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                const int j = 16 * jt + lr;
+            for (int q = 0; q < 4; ++q) {
+                const int n = 16 * wave + lq, p = 16 * q + lr;
+                *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(Hs[q][0], Hs[q][1], Hs[q][2], Hs[q][3]);
+                *reinterpret_cast<u16x4 *>(&dHb[p * kS128 + n]) = pack4(dHs[q][0], dHs[q][1], dHs[q][2], dHs[q][3]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dotp = fmaf(Hs[q][v], dHs[q][v], dotp);
+            }
+            dotp = wave_total(dotp);
+            if (lane == 0) sm.dot[wave] = dotp;
+        }
+        if (hh + 1 < hpg) {
+            load_states(h + 1);
+            // the other parity slot is free: this head reads only lam[par], dt[par], and
+            // the barrier below publishes the next head's values before its first use
+            if (wave == 0) scan(h + 1, par ^ 1);
+        }
+        __syncthreads();
+        // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tiles 2wh, 2wh+1) ----
+        {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int jt = 2 * wh + q, j = 16 * jt + lr;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     if (32 * (kk + 1) <= 16 * jt) continue;  // Q[i][j] = 0 for i < j
-                    acc = mma16(&dYT[(16 * wave + lr) * kS64 + 32 * kk + lk],
-                                &QT[(16 * jt + lr) * kS64 + 32 * kk + lk], acc);
+                    acc = mfma(frag_tr(sm.dY, kS64, 16 * wq, 32 * kk, lane),
+                               frag_row(&sm.QT[(16 * jt + lr) * kS64 + 32 * kk + lk]), acc);
                 }
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    acc4 = mma16(&dH[(16 * wave + lr) * kS128 + 32 * kk + lk],
+                    acc4 = mma16(&dHb[(16 * wq + lr) * kS128 + 32 * kk + lk],
                                  &sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk], acc4);
-                const float wj = __expf(lam_end - lam[j]), dt_j = dts[j];
-                const u16x4 x4 = *reinterpret_cast<const u16x4 *>(&X[j * kS64 + 16 * wave + lq]);
-                const u16x4 y4 = *reinterpret_cast<const u16x4 *>(&dY[j * kS64 + 16 * wave + lq]);
-                float ddp = 0.f;
-                f32x4 dxv;
+                const float wj = __expf(lam_e - lam[base + j]), dt_j = dts[base + j];
+                const u16x4 x4 = *reinterpret_cast<const u16x4 *>(&sm.X[j * kS64 + 16 * wq + lq]);
+                const u16x4 y4 = *reinterpret_cast<const u16x4 *>(&sm.dY[j * kS64 + 16 * wq + lq]);
+                float ddp = 0.f, dxv[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const float pre = fmaf(wj, acc4[v], acc[v]);
                     ddp = fmaf(bf16_to_f32(x4[v]), pre, ddp);
                     dxv[v] = fmaf(Dh, bf16_to_f32(y4[v]), dt_j * pre);
                 }
-                if (tk + j < T) {
-                    *reinterpret_cast<u16x4 *>(dx + ((b * T + tk + j) * a.H + h) * kP + 16 * wave + lq) =
+                if (k * kLs + j < nvalid)
+                    *reinterpret_cast<u16x4 *>(dx + ((b * T + tk) * a.H + h) * kP + static_cast<uint32_t>(j * tok_stride + 16 * wq + lq)) =
                         pack4(dxv[0], dxv[1], dxv[2], dxv[3]);
-                }
-                ddp += __shfl_xor(ddp, 16, 64);
-                ddp += __shfl_xor(ddp, 32, 64);
-                if (lane < 16) sm.dd[wave][j] = ddp;
+                ddp = rows4_sum(ddp);
+                if (lane < 16) sm.dd[wq][j] = ddp;
             }
         }
-        // Phase III / IV: per-head dC, dB contributions   (wave w: n in [32w, 32w+32))
+        // Phase III / IV: per-head dC, dB contributions (n-tile = wave, tok-tiles 0..3)
         {
-            const bf16_t *X = U + oX, *dY = U + odY, *HT = U + oHT, *dHT = U + odHT;
-            float offacc[4] = {0.f, 0.f, 0.f, 0.f}, finacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int nt = 2 * wave + q / 4, tt = q % 4;
+            for (int tt = 0; tt < 4; ++tt) {
                 const int i = 16 * tt + lr;
                 f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    ac = mma16(&HT[(16 * nt + lr) * kS64 + 32 * kk + lk],
-                               &dY[(16 * tt + lr) * kS64 + 32 * kk + lk], ac);
-                    ab = mma16(&dHT[(16 * nt + lr) * kS64 + 32 * kk + lk],
-                               &X[(16 * tt + lr) * kS64 + 32 * kk + lk], ab);
+                    ac = mfma(frag_tr(Hb, kS128, 16 * wave, 32 * kk, lane),
+                              frag_row(&sm.dY[(16 * tt + lr) * kS64 + 32 * kk + lk]), ac);
+                    ab = mfma(frag_tr(dHb, kS128, 16 * wave, 32 * kk, lane),
+                              frag_row(&sm.X[(16 * tt + lr) * kS64 + 32 * kk + lk]), ab);
                 }
-                const float ei = __expf(lam[i]);
-                const float wdt = __expf(lam_end - lam[i]) * dts[i];
-                const u16x4 c4 = *reinterpret_cast<const u16x4 *>(&sm.C[i * kS128 + 16 * nt + lq]);
-                const u16x4 b4 = *reinterpret_cast<const u16x4 *>(&sm.B[i * kS128 + 16 * nt + lq]);
+                const float ei = __expf(lam[base + i] - lam_blk0);
+                const float wdt = __expf(lam_e - lam[base + i]) * dts[base + i];
+                const u16x4 c4 = *reinterpret_cast<const u16x4 *>(&sm.C[i * kS128 + 16 * wave + lq]);
+                const u16x4 b4 = *reinterpret_cast<const u16x4 *>(&sm.B[i * kS128 + 16 * wave + lq]);
+                float o = 0.f, f = 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     ac[v] *= ei;
                     ab[v] *= wdt;
-                    offacc[tt] = fmaf(bf16_to_f32(c4[v]), ac[v], offacc[tt]);
-                    finacc[tt] = fmaf(bf16_to_f32(b4[v]), ab[v], finacc[tt]);
-                    dCa[q][v] += ac[v];
-                    dBa[q][v] += ab[v];
+                    o = fmaf(bf16_to_f32(c4[v]), ac[v], o);
+                    f = fmaf(bf16_to_f32(b4[v]), ab[v], f);
+                    dCa[tt][v] += ac[v];
+                    dBa[tt][v] += ab[v];
                 }
-            }
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                float o = offacc[tt], f = finacc[tt];
-                o += __shfl_xor(o, 16, 64);
-                o += __shfl_xor(o, 32, 64);
-                f += __shfl_xor(f, 16, 64);
-                f += __shfl_xor(f, 32, 64);
+                o = rows4_sum(o);
+                f = rows4_sum(f);
                 if (lane < 16) {
-                    sm.off[wave][16 * tt + lr] = o;
-                    sm.fin[wave][16 * tt + lr] = f;
+                    sm.off[wave][i] = o;
+                    sm.fin[wave][i] = f;
                 }
             }
-            // dD share: 16 products of dy . x per thread
             float dsum = 0.f;
-            const int jr = tid >> 2, pc = (tid & 3) * 16;
+            const int jr = tid >> 3, pc = (tid & 7) * 8;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                dsum = fmaf(bf16_to_f32(dY[jr * kS64 + pc + e]), bf16_to_f32(X[jr * kS64 + pc + e]), dsum);
-            dsum = wave_sum(dsum);
+            for (int e = 0; e < 8; ++e)
+                dsum = fmaf(bf16_to_f32(sm.dY[jr * kS64 + pc + e]), bf16_to_f32(sm.X[jr * kS64 + pc + e]), dsum);
+            dsum = wave_total(dsum);
             if (lane == 0) sm.dd_sum[wave] = dsum;
         }
         __syncthreads();
-        // combine per token (wave 0, lane = token of the block), suffix sum, ddt
+        // ---- S5: combine per token (wave 0, lane = token of the block) ----
         if (wave == 0) {
             const int j = lane;
-            float dl = sm.row[j];
+            float dl = sm.row[0][j] + sm.row[1][j];
             float ddd = 0.f, fs = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                dl += sm.off[w][j] - sm.col[w][j] - sm.fin[w][j];
-                fs += sm.fin[w][j];
+                dl -= sm.col[w][j];
                 ddd += sm.dd[w][j];
             }
-            const float fin_total = wave_sum(fs);
-            if (j == kLs - 1) {
-                const float dotv = (sm.dot[0] + sm.dot[1]) + (sm.dot[2] + sm.dot[3]);
-                dl += fin_total + __expf(lam_end) * dotv;
-            }
-            // da_j = sum_{i >= j} dLam_i
-            float da = dl;
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float t = __shfl_down(da, o, 64);
-                if (lane + o < 64) da += t;
+            for (int w = 0; w < 8; ++w) {
+                dl += sm.off[w][j] - sm.fin[w][j];
+                fs += sm.fin[w][j];
             }
-            if (tk + j < T) a.ddt[(b * T + tk + j) * a.H + h] = fmaf(Ah, da, ddd);
-            const float pa = wave_sum(dts[j] * da);
+            const float fin_total = wave_total(fs);
+            if (j == kLs - 1) {
+                float dotv = 0.f;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) dotv += sm.dot[w];
+                dl += fin_total + __expf(lam_e - lam_blk0) * dotv;
+            }
+            const float da = wave_suffix_sum(dl);  // da_j = sum_{i >= j} dLam_i within the block
+            if (k * kLs + j < nvalid) a.ddt[(b * T + tk) * a.H + h + static_cast<uint32_t>(j * a.H)] = fmaf(Ah, da, ddd);
+            const float pa = wave_total(dts[base + j] * da);
             if (lane == 0) {
+                float ds = 0.f;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) ds += sm.dd_sum[w];
                 const int64_t pi = (bh * a.nchunks + c) * nb + k;
                 a.pA[pi] = static_cast<double>(pa);
-                a.pD[pi] = static_cast<double>((sm.dd_sum[0] + sm.dd_sum[1]) + (sm.dd_sum[2] + sm.dd_sum[3]));
+                a.pD[pi] = static_cast<double>(ds);
             }
         }
     }
 
-    // sum_h K applied once: dC += K B (contract over j), dB += K^T C (contract over i)
+    // sum_h K applied once: dC^T[n][i] += sum_j B[j][n] K[i][j]; dB^T[n][j] += sum_i C[i][n] K[i][j]
+    refresh_lane();
     __syncthreads();
-    {
-        bf16_t *Kr = U + oK, *KT = U + oKT, *BT = U + oBT, *CT = U + oCT;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            const int j = 16 * jt + lr, i0 = 16 * wave + lq;
-            *reinterpret_cast<u16x4 *>(&KT[j * kS64 + i0]) = pack4(Ks[jt][0], Ks[jt][1], Ks[jt][2], Ks[jt][3]);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) Kr[(i0 + v) * kS64 + j] = f32_to_bf16(Ks[jt][v]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const u16x4 vb = {sm.B[(nt0 + 0) * kS128 + nn0 + e], sm.B[(nt0 + 1) * kS128 + nn0 + e],
-                              sm.B[(nt0 + 2) * kS128 + nn0 + e], sm.B[(nt0 + 3) * kS128 + nn0 + e]};
-            const u16x4 vc = {sm.C[(nt0 + 0) * kS128 + nn0 + e], sm.C[(nt0 + 1) * kS128 + nn0 + e],
-                              sm.C[(nt0 + 2) * kS128 + nn0 + e], sm.C[(nt0 + 3) * kS128 + nn0 + e]};
-            *reinterpret_cast<u16x4 *>(&BT[(nn0 + e) * kS64 + nt0]) = vb;
-            *reinterpret_cast<u16x4 *>(&CT[(nn0 + e) * kS64 + nt0]) = vc;
-        }
+    for (int q = 0; q < 2; ++q) {
+        const int j = 16 * (2 * wh + q) + lr;
+        *reinterpret_cast<u16x4 *>(&sm.QT[j * kS64 + 16 * wq + lq]) = pack4(Ks[q][0], Ks[q][1], Ks[q][2], Ks[q][3]);
     }
     __syncthreads();
     {
-        const bf16_t *Kr = U + oK, *KT = U + oKT, *BT = U + oBT, *CT = U + oCT;
+        const bf16_t *KT = sm.QT;  // [j][i]
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int nt = 2 * wave + q / 4, tt = q % 4;
+        for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                dCa[q] = mma16(&BT[(16 * nt + lr) * kS64 + 32 * kk + lk],
-                               &Kr[(16 * tt + lr) * kS64 + 32 * kk + lk], dCa[q]);
-                dBa[q] = mma16(&CT[(16 * nt + lr) * kS64 + 32 * kk + lk],
-                               &KT[(16 * tt + lr) * kS64 + 32 * kk + lk], dBa[q]);
+                dCa[tt] = mfma(frag_tr(sm.B, kS128, 16 * wave, 32 * kk, lane),
+                               frag_tr(KT, kS64, 16 * tt, 32 * kk, lane), dCa[tt]);
+                dBa[tt] = mfma(frag_tr(sm.C, kS128, 16 * wave, 32 * kk, lane),
+                               frag_row(&KT[(16 * tt + lr) * kS64 + 32 * kk + lk]), dBa[tt]);
             }
             const int t = 16 * tt + lr;
             if (tk + t < T) {
-                const int64_t o = ((b * T + tk + t) * a.G + g) * kN + 16 * nt + lq;
-                *reinterpret_cast<float4 *>(a.dC + o) = make_float4(dCa[q][0], dCa[q][1], dCa[q][2], dCa[q][3]);
-                *reinterpret_cast<float4 *>(a.dB + o) = make_float4(dBa[q][0], dBa[q][1], dBa[q][2], dBa[q][3]);
+                const int64_t o = ((b * T + tk + t) * a.G + g) * kN + 16 * wave + lq;
+                *reinterpret_cast<float4 *>(a.dC + o) = make_float4(dCa[tt][0], dCa[tt][1], dCa[tt][2], dCa[tt][3]);
+                *reinterpret_cast<float4 *>(a.dB + o) = make_float4(dBa[tt][0], dBa[tt][1], dBa[tt][2], dBa[tt][3]);
             }
         }
     }
@@ -648,17 +626,9 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s) {
     ssd_bwd_dstate_kernel<<<static_cast<unsigned>(a.Bsz * a.H), 256, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t smem = sizeof(BlkSmem);
-    static bool configured = false;
-    if (!configured) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ssd_bwd_block_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
     const int64_t nwg = a.Bsz * a.G * a.nchunks * (a.L / kLs);
     if (a.ev_begin != nullptr && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
-    ssd_bwd_block_kernel<<<static_cast<unsigned>(nwg), 256, smem, s>>>(a);
+    ssd_bwd_block_kernel<<<static_cast<unsigned>(nwg), kBlkThreads, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_end != nullptr && (e = hipEventRecord(a.ev_end, s)) != hipSuccess) return e;

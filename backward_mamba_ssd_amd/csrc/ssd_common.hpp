@@ -23,6 +23,32 @@ __device__ __forceinline__ f32x4 mma16(const bf16_t *a, const bf16_t *b, f32x4 a
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
 }
 
+// Fragment of a row-major [16 x K] operand tile: 8 consecutive K of row l%16.
+__device__ __forceinline__ bf16x8 frag_row(const bf16_t *rowk) {
+    return *reinterpret_cast<const bf16x8 *>(rowk);
+}
+
+// Fragment of the operand A[r][k] = T[k][r] read from a row-major [K][R] LDS
+// tile T (row stride ld elements) with gfx950's transposing LDS read: within a
+// 16-lane group, lane i receives element i%4 of the 8-byte chunks addressed by
+// lanes i/4, i/4+4, i/4+8, i/4+12.  Lane j of group g therefore addresses row
+// k0 + 8g + j/4, columns r0 + 4(j%4) .. +3, and lane i gets T[k0+8g+m][r0+i],
+// m = 0..3; a second read 4 rows further down supplies m = 4..7.
+__device__ __forceinline__ bf16x8 frag_tr(const bf16_t *T, int ld, int r0, int k0, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int g = lane >> 4, j = lane & 15;
+    const bf16_t *p = T + (k0 + 8 * g + (j >> 2)) * ld + r0 + 4 * (j & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 4 * ld));
+    const v4i16 both[2] = {lo, hi};
+    return *reinterpret_cast<const bf16x8 *>(both);
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
 // Dispatch places workgroup i on XCD i % 8; hand each XCD a contiguous range
 // of logical ids so that neighbouring ids (the heads of one group, the blocks
 // of one chunk) share that XCD's L2.
@@ -31,12 +57,68 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
     return (i & 7) * (n >> 3) + (i >> 3);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
+// Cross-lane sums without lane-address registers.  A 64-lane wave is four rows of
+// 16 lanes.  Within a row, DPP swaps neighbours (quad_perm 1,0,3,2 and 2,3,0,1), then
+// mirrors half-rows and rows; across rows, the gfx950 permlane swaps pair row r with
+// r^1 and the half-waves with each other.  Each helper returns the sum in every lane
+// it covers; the order of additions is fixed, so results are deterministic.
+#define SSM_DPP(v, ctrl) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), 0xf, 0xf, false))
+// sum over the 16 lanes of the row
+__device__ __forceinline__ float row16_sum(float v) {
+    v += SSM_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
+    v += SSM_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
+    v += SSM_DPP(v, 0x141);  // row_half_mirror
+    v += SSM_DPP(v, 0x140);  // row_mirror
+    return v;
+}
+// sum over lanes l, l^16, l^32, l^48.  A swap given the same value in both operands
+// returns rows (0,0,2,2)/(1,1,3,3) for the 16-lane form and halves (lo,lo)/(hi,hi)
+// for the 32-lane form, so the sum of its two results is the pair sum.  The results
+// are read with __uint_as_float: __builtin_bit_cast of a subscript of the returned
+// pair reads element 0 for both.
+__device__ __forceinline__ float swap_pair_sum16(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_pair_sum32(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float rows4_sum(float v) { return swap_pair_sum32(swap_pair_sum16(v)); }
+__device__ __forceinline__ float wave_total(float v) { return rows4_sum(row16_sum(v)); }
+#undef SSM_DPP
+
+// Lane index the compiler cannot treat as loop-invariant: shuffle addresses derived
+// from it are formed where they are used instead of being held in registers across
+// loops.
+__device__ __forceinline__ int lane_here() {
+    int l = static_cast<int>(__lane_id());
+    asm volatile("" : "+v"(l));
+    return l;
+}
+__device__ __forceinline__ float lane_read(float v, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+// inclusive prefix sum over the wave (lane 0 first)
+__device__ __forceinline__ float wave_prefix_sum(float v) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(v, off, 64);
-        if (lane >= off) v += o;
+        const int l = lane_here();
+        const float o = lane_read(v, l - off);
+        if (l >= off) v += o;
+    }
+    return v;
+}
+// inclusive suffix sum over the wave (lane 63 first)
+__device__ __forceinline__ float wave_suffix_sum(float v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int l = lane_here();
+        const float o = lane_read(v, l + off);
+        if (l + off < 64) v += o;
     }
     return v;
 }

@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         const int buf = static_cast<int>(s & 1);
         // (1) cumulative log-retention of the block (one wave, one token per lane)
         if (wave == 0) {
-            sm.lam[buf][lane] = wave_prefix_sum(dtr * Ah, lane);
+            sm.lam[buf][lane] = wave_prefix_sum(dtr * Ah);
             sm.dt[buf][lane] = dtr;
         }
         __syncthreads();
