@@ -363,33 +363,38 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         __syncthreads();
         if (hh + 1 < hpg) prefetch(h + 1);  // registers are free once staged
         // ---- S2: state products over the other blocks; Phase I of block k ----
+        // Each A fragment (16 state rows n of one block's B or C) is read once and used
+        // for all four p-tiles.
         {
             const float es = __expf(lam_blk0);
             const float ee = __expf(lam[kEnd] - lam_e);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n0 = 16 * wave, p0 = 16 * q;
-                f32x4 hacc = Hs[q], gacc = dHs[q];
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    hacc[v] *= es;
-                    gacc[v] *= ee;
+                    Hs[q][v] *= es;
+                    dHs[q][v] *= ee;
                 }
-                for (int kb = 0; kb < nbc; ++kb) {
-                    if (kb == k) continue;
-                    const int slot = kb < k ? kb : kb - 1;
-                    const bf16_t *bc = sm.chainBC + slot * kT128;
-                    const bf16_t *xs = sm.R + slot * kT64;
+            const int n0 = 16 * wave;
+            for (int kb = 0; kb < k; ++kb) {  // H_k = e H_c + sum over earlier blocks
+                const bf16_t *bc = sm.chainBC + kb * kT128;
+                const bf16_t *xs = sm.R + kb * kT64;
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
-                        const bf16x8 fb = frag_tr(xs, kS64, p0, 32 * kk, lane);
-                        if (kb < k) hacc = mfma(fa, fb, hacc);
-                        else gacc = mfma(fa, fb, gacc);
-                    }
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) Hs[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), Hs[q]);
                 }
-                Hs[q] = hacc;
-                dHs[q] = gacc;
+            }
+            for (int kb = k + 1; kb < nbc; ++kb) {  // dH_{k+1} = e dH_c + sum over later blocks
+                const bf16_t *bc = sm.chainBC + (kb - 1) * kT128;
+                const bf16_t *xs = sm.R + (kb - 1) * kT64;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) dHs[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), dHs[q]);
+                }
             }
         }
         // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile wq, j-tiles 2wh, 2wh+1)
@@ -455,27 +460,37 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         __syncthreads();
         // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tiles 2wh, 2wh+1) ----
         {
+            f32x4 acc[2], acc4[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int jt = 2 * wh + q, j = 16 * jt + lr;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc4 = {0.f, 0.f, 0.f, 0.f};
+                acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc4[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    if (32 * (kk + 1) <= 16 * jt) continue;  // Q[i][j] = 0 for i < j
-                    acc = mfma(frag_tr(sm.dY, kS64, 16 * wq, 32 * kk, lane),
-                               frag_row(&sm.QT[(16 * jt + lr) * kS64 + 32 * kk + lk]), acc);
-                }
+            for (int kk = 0; kk < 2; ++kk) {
+                if (32 * (kk + 1) <= 32 * wh) continue;  // Q[i][j] = 0 for i < j (both j-tiles)
+                const bf16x8 fa = frag_tr(sm.dY, kS64, 16 * wq, 32 * kk, lane);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    acc4 = mma16(&dHb[(16 * wq + lr) * kS128 + 32 * kk + lk],
-                                 &sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk], acc4);
+                for (int q = 0; q < 2; ++q)
+                    acc[q] = mfma(fa, frag_row(&sm.QT[(16 * (2 * wh + q) + lr) * kS64 + 32 * kk + lk]), acc[q]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 fa = frag_row(&dHb[(16 * wq + lr) * kS128 + 32 * kk + lk]);
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    acc4[q] = mfma(fa, frag_row(&sm.B[(16 * (2 * wh + q) + lr) * kS128 + 32 * kk + lk]), acc4[q]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int j = 16 * (2 * wh + q) + lr;
                 const float wj = __expf(lam_e - lam[base + j]), dt_j = dts[base + j];
                 const u16x4 x4 = *reinterpret_cast<const u16x4 *>(&sm.X[j * kS64 + 16 * wq + lq]);
                 const u16x4 y4 = *reinterpret_cast<const u16x4 *>(&sm.dY[j * kS64 + 16 * wq + lq]);
                 float ddp = 0.f, dxv[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float pre = fmaf(wj, acc4[v], acc[v]);
+                    const float pre = fmaf(wj, acc4[q][v], acc[q][v]);
                     ddp = fmaf(bf16_to_f32(x4[v]), pre, ddp);
                     dxv[v] = fmaf(Dh, bf16_to_f32(y4[v]), dt_j * pre);
                 }
@@ -486,18 +501,23 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 if (lane < 16) sm.dd[wq][j] = ddp;
             }
         }
-        // Phase III / IV: per-head dC, dB contributions (n-tile = wave, tok-tiles 0..3)
+        // Phase III / IV: per-head dC, dB contributions (n-tile = wave, tok-tiles 0..3);
+        // the state fragments are read once for the four token tiles.
         {
+            bf16x8 fH[2], fdH[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                fH[kk] = frag_tr(Hb, kS128, 16 * wave, 32 * kk, lane);
+                fdH[kk] = frag_tr(dHb, kS128, 16 * wave, 32 * kk, lane);
+            }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const int i = 16 * tt + lr;
                 f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    ac = mfma(frag_tr(Hb, kS128, 16 * wave, 32 * kk, lane),
-                              frag_row(&sm.dY[(16 * tt + lr) * kS64 + 32 * kk + lk]), ac);
-                    ab = mfma(frag_tr(dHb, kS128, 16 * wave, 32 * kk, lane),
-                              frag_row(&sm.X[(16 * tt + lr) * kS64 + 32 * kk + lk]), ab);
+                    ac = mfma(fH[kk], frag_row(&sm.dY[(16 * tt + lr) * kS64 + 32 * kk + lk]), ac);
+                    ab = mfma(fdH[kk], frag_row(&sm.X[(16 * tt + lr) * kS64 + 32 * kk + lk]), ab);
                 }
                 const float ei = __expf(lam[base + i] - lam_blk0);
                 const float wdt = __expf(lam_e - lam[base + i]) * dts[base + i];
@@ -520,11 +540,12 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     sm.fin[wave][i] = f;
                 }
             }
+            // dD partial: dy . x over the block (one 8-element row segment per thread)
+            const u16x8 y8 = *reinterpret_cast<const u16x8 *>(&sm.dY[pr_tok * kS64 + pr_col]);
+            const u16x8 x8 = *reinterpret_cast<const u16x8 *>(&sm.X[pr_tok * kS64 + pr_col]);
             float dsum = 0.f;
-            const int jr = tid >> 3, pc = (tid & 7) * 8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                dsum = fmaf(bf16_to_f32(sm.dY[jr * kS64 + pc + e]), bf16_to_f32(sm.X[jr * kS64 + pc + e]), dsum);
+            for (int e = 0; e < 8; ++e) dsum = fmaf(bf16_to_f32(y8[e]), bf16_to_f32(x8[e]), dsum);
             dsum = wave_total(dsum);
             if (lane == 0) sm.dd_sum[wave] = dsum;
         }
