@@ -53,6 +53,44 @@ def bwd_block_bytes_per_token(w):
     return (3 * 2 * H * P + 2 * 4 * H * P * N / L + 2 * 2 * G * N + 2 * 4 * G * N + 2 * 4 * H)
 
 
+KERNEL_SOURCES = {
+    "ssd_fwd_kernel": ("ssd_fwd.hip", "ssd_common.hpp", "common.hpp", "launch.hpp"),
+    "ssd_bwd_block_kernel": ("ssd_bwd.hip", "ssd_common.hpp", "common.hpp", "launch.hpp"),
+}
+
+
+def kernel_source_sha256(kernel):
+    """sha256 over the HIP sources a kernel is built from (in a fixed order)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "backward_mamba_ssd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary
+    profiles/<kernel>_<workload>_hbm_counters.md (FETCH_SIZE and WRITE_SIZE,
+    each scaled by what the counter reads for a copy of known size), or None
+    when there is no summary or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_sha256(kernel):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def fwd_mfma_flops_per_token(w):
     """MFMA flops the forward kernel issues per token (64-token blocks, per head):
     Gram 10 causal 16x16 tiles x K=128, outputs 16 tiles x K=128 plus 6 steps of
@@ -227,7 +265,8 @@ def main():
     ms, nbytes = kernels[dom]
     achieved = nbytes / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dom, w.name),
                 "kernel": dom, "mean_ms": round(ms, 4), "bytes_per_launch": int(nbytes)}
     res = {
         "metric": "SSM fwd+bwd tokens/s at 256h x 64 x 128",
