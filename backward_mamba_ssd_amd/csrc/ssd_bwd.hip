@@ -250,27 +250,27 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     u16x8 xr[kMaxBlk];  // x rows of blocks <= k, dy rows of blocks > k
     u16x8 yk;           // dy rows of block k
     float dtr[4];
-    // Per-head global accesses: a wave-uniform base pointer plus a 32-bit lane offset
-    // (token strides within a chunk stay far below 2^31 elements).
-    const int tok_stride = a.H * kP;                       // elements between tokens of x, dy, dx
-    const int nvalid = static_cast<int>(cend - cstart);    // valid tokens of this chunk
+    // Per-head rows of x, dy, dx and dt, ddt through buffer descriptors over this
+    // chunk: offsets past the chunk's valid tokens read zero / drop the write.
+    const int nvalid = static_cast<int>(cend - cstart);   // valid tokens of this chunk
+    const uint32_t tokb = static_cast<uint32_t>(a.H) * kP * 2;  // bytes between tokens of x, dy, dx
+    const int64_t row0 = (static_cast<int64_t>(b) * T + cstart) * a.H;  // first (token, head) of the chunk
+    const rsrc_t rx = make_rsrc(x + row0 * kP, nvalid * tokb);
+    const rsrc_t ry = make_rsrc(dy + row0 * kP, nvalid * tokb);
+    const rsrc_t rdx = make_rsrc(dx + row0 * kP, nvalid * tokb);
+    const rsrc_t rdt = make_rsrc(a.dt + row0, nvalid * a.H * 4u);
+    const rsrc_t rddt = make_rsrc(a.ddt + row0, nvalid * a.H * 4u);
+    const uint32_t row_off = static_cast<uint32_t>(pr_tok) * tokb + pr_col * 2;  // this thread's row segment
     auto prefetch = [&](int h) {
-        const int64_t hb = ((static_cast<int64_t>(b) * T + cstart) * a.H + h) * kP;
-        const bf16_t *xh = x + hb, *yh = dy + hb;
-        const uint32_t row_off = static_cast<uint32_t>(pr_tok * tok_stride + pr_col);
+        const uint32_t o = row_off + static_cast<uint32_t>(h) * (kP * 2);
 #pragma unroll
-        for (int kb = 0; kb < kMaxBlk; ++kb) {
-            const bf16_t *src = (kb <= k ? xh : yh) + static_cast<uint32_t>(kb * kLs * tok_stride);
-            xr[kb] = (kb < nbc && kb * kLs + pr_tok < nvalid) ? *reinterpret_cast<const u16x8 *>(src + row_off) : z8;
-        }
-        yk = (k * kLs + pr_tok < nvalid) ? *reinterpret_cast<const u16x8 *>(yh + static_cast<uint32_t>(k * kLs * tok_stride) + row_off) : z8;
+        for (int kb = 0; kb < kMaxBlk; ++kb)  // blocks past the chunk read zero
+            xr[kb] = buf_ld_16b(kb <= k ? rx : ry, o + kb * kLs * tokb);
+        yk = buf_ld_16b(ry, o + k * kLs * tokb);
         if (wave == 0) {
-            const float *dth = a.dt + (static_cast<int64_t>(b) * T + cstart) * a.H + h;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 4 * lane + e;
-                dtr[e] = (t < nvalid) ? dth[static_cast<uint32_t>(t * a.H)] : 0.f;
-            }
+            for (int e = 0; e < 4; ++e)
+                dtr[e] = buf_ld_f32(rdt, (static_cast<uint32_t>(4 * lane + e) * a.H + h) * 4u);
         }
     };
     // chunk-local cumulative log-retention of head h (wave 0; lane = 4 tokens)
@@ -317,6 +317,18 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             for (int kk = 0; kk < 4; ++kk)
                 Gt[q] = mma16(&sm.C[(16 * wq + lr) * kS128 + 32 * kk + lk],
                               &sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk], Gt[q]);
+        }
+    }
+    // B and C of block k at this lane's (token, n) positions of the Phase III/IV tiles
+    float cC[4][4], cB[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const u16x4 c4 = *reinterpret_cast<const u16x4 *>(&sm.C[(16 * tt + lr) * kS128 + 16 * wave + lq]);
+        const u16x4 b4 = *reinterpret_cast<const u16x4 *>(&sm.B[(16 * tt + lr) * kS128 + 16 * wave + lq]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            cC[tt][v] = bf16_to_f32(c4[v]);
+            cB[tt][v] = bf16_to_f32(b4[v]);
         }
     }
     f32x4 Ks[2], dCa[4], dBa[4];  // Ks like Gt; dCa/dBa [n][tok]: n-tile = wave, tok-tiles 0..3
@@ -376,7 +388,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     dHs[q][v] *= ee;
                 }
             const int n0 = 16 * wave;
-            for (int kb = 0; kb < k; ++kb) {  // H_k = e H_c + sum over earlier blocks
+#pragma unroll
+            for (int kb = 0; kb < kMaxBlk - 1; ++kb) {  // H_k = e H_c + sum over earlier blocks
+                if (kb >= k) break;
                 const bf16_t *bc = sm.chainBC + kb * kT128;
                 const bf16_t *xs = sm.R + kb * kT64;
 #pragma unroll
@@ -386,9 +400,11 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     for (int q = 0; q < 4; ++q) Hs[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), Hs[q]);
                 }
             }
-            for (int kb = k + 1; kb < nbc; ++kb) {  // dH_{k+1} = e dH_c + sum over later blocks
-                const bf16_t *bc = sm.chainBC + (kb - 1) * kT128;
-                const bf16_t *xs = sm.R + (kb - 1) * kT64;
+#pragma unroll
+            for (int sl = 0; sl < kMaxBlk - 1; ++sl) {  // dH_{k+1} = e dH_c + sum over later blocks (slot sl = block sl+1)
+                if (sl < k || sl + 1 >= nbc) continue;
+                const bf16_t *bc = sm.chainBC + sl * kT128;
+                const bf16_t *xs = sm.R + sl * kT64;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
@@ -399,18 +415,22 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         }
         // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile wq, j-tiles 2wh, 2wh+1)
         {
-            float lam_i[4], rowacc[4] = {0.f, 0.f, 0.f, 0.f};
+            float lam_i[4], rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) lam_i[v] = lam[base + 16 * wq + lq + v];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int jt = 2 * wh + q, j = 16 * jt + lr;
+                // tiles above the diagonal are computed too: the mask below zeroes them
                 f32x4 dW = {0.f, 0.f, 0.f, 0.f};
-                if (jt <= wq) {
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
-                        dW = mma16(&sm.dY[(16 * wq + lr) * kS64 + 32 * kk + lk],
-                                   &sm.X[(16 * jt + lr) * kS64 + 32 * kk + lk], dW);
+                for (int kk = 0; kk < 2; ++kk)
+                    dW = mma16(&sm.dY[(16 * wq + lr) * kS64 + 32 * kk + lk],
+                               &sm.X[(16 * jt + lr) * kS64 + 32 * kk + lk], dW);
+                if (jt == wq) {  // diagonal tile: dW[i][i] = dy_i . x_i feeds dD
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (lq + v == lr) diag += dW[v];
                 }
                 const float lam_j = lam[base + j], dt_j = dts[base + j];
                 float qv[4], colacc = 0.f;
@@ -434,6 +454,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 const float r = row16_sum(rowacc[v]);
                 if (lr == 0) sm.row[wh][16 * wq + lq + v] = r;
             }
+            diag = wave_total(diag);
+            if (lane == 0) sm.dd_sum[wave] = diag;
         }
         __syncthreads();
         // ---- S3: block-entry state and exit gradient in bf16, [p][n] ----
@@ -468,7 +490,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                if (32 * (kk + 1) <= 32 * wh) continue;  // Q[i][j] = 0 for i < j (both j-tiles)
+                // Q[i][j] = 0 for i < j, so the kk block below the diagonal adds zeros
                 const bf16x8 fa = frag_tr(sm.dY, kS64, 16 * wq, 32 * kk, lane);
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
@@ -494,9 +516,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     ddp = fmaf(bf16_to_f32(x4[v]), pre, ddp);
                     dxv[v] = fmaf(Dh, bf16_to_f32(y4[v]), dt_j * pre);
                 }
-                if (k * kLs + j < nvalid)
-                    *reinterpret_cast<u16x4 *>(dx + ((b * T + tk) * a.H + h) * kP + static_cast<uint32_t>(j * tok_stride + 16 * wq + lq)) =
-                        pack4(dxv[0], dxv[1], dxv[2], dxv[3]);
+                buf_st_8b(rdx, static_cast<uint32_t>(k * kLs + j) * tokb + (h * kP + 16 * wq + lq) * 2,
+                          pack4(dxv[0], dxv[1], dxv[2], dxv[3]));
                 ddp = rows4_sum(ddp);
                 if (lane < 16) sm.dd[wq][j] = ddp;
             }
@@ -521,15 +542,13 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 }
                 const float ei = __expf(lam[base + i] - lam_blk0);
                 const float wdt = __expf(lam_e - lam[base + i]) * dts[base + i];
-                const u16x4 c4 = *reinterpret_cast<const u16x4 *>(&sm.C[i * kS128 + 16 * wave + lq]);
-                const u16x4 b4 = *reinterpret_cast<const u16x4 *>(&sm.B[i * kS128 + 16 * wave + lq]);
                 float o = 0.f, f = 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     ac[v] *= ei;
                     ab[v] *= wdt;
-                    o = fmaf(bf16_to_f32(c4[v]), ac[v], o);
-                    f = fmaf(bf16_to_f32(b4[v]), ab[v], f);
+                    o = fmaf(cC[tt][v], ac[v], o);
+                    f = fmaf(cB[tt][v], ab[v], f);
                     dCa[tt][v] += ac[v];
                     dBa[tt][v] += ab[v];
                 }
@@ -540,14 +559,6 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     sm.fin[wave][i] = f;
                 }
             }
-            // dD partial: dy . x over the block (one 8-element row segment per thread)
-            const u16x8 y8 = *reinterpret_cast<const u16x8 *>(&sm.dY[pr_tok * kS64 + pr_col]);
-            const u16x8 x8 = *reinterpret_cast<const u16x8 *>(&sm.X[pr_tok * kS64 + pr_col]);
-            float dsum = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dsum = fmaf(bf16_to_f32(y8[e]), bf16_to_f32(x8[e]), dsum);
-            dsum = wave_total(dsum);
-            if (lane == 0) sm.dd_sum[wave] = dsum;
         }
         __syncthreads();
         // ---- S5: combine per token (wave 0, lane = token of the block) ----
@@ -573,7 +584,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 dl += fin_total + __expf(lam_e - lam_blk0) * dotv;
             }
             const float da = wave_suffix_sum(dl);  // da_j = sum_{i >= j} dLam_i within the block
-            if (k * kLs + j < nvalid) a.ddt[(b * T + tk) * a.H + h + static_cast<uint32_t>(j * a.H)] = fmaf(Ah, da, ddd);
+            buf_st_f32(rddt, (static_cast<uint32_t>(k * kLs + j) * a.H + h) * 4u, fmaf(Ah, da, ddd));
             const float pa = wave_total(dts[base + j] * da);
             if (lane == 0) {
                 float ds = 0.f;

@@ -123,6 +123,28 @@ __device__ __forceinline__ float wave_suffix_sum(float v) {
     return v;
 }
 
+// Raw buffer access over one chunk's rows.  The hardware range-checks the per-lane
+// byte offset against `bytes`: reads at or past it return zero and writes there are
+// dropped, so ragged tails need no branches.  The scalar offset is always 0 (it is
+// not part of the check).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u16x8 buf_ld_16b(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_ld_f32(rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st_8b(rsrc_t r, uint32_t off, u16x4 v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st_f32(rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
 __device__ __forceinline__ u16x4 pack4(float a, float b, float c, float d) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 w = {pack2_bf16(a, b), pack2_bf16(c, d)};
