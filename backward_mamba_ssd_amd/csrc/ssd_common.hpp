@@ -91,36 +91,39 @@ __device__ __forceinline__ float rows4_sum(float v) { return swap_pair_sum32(swa
 __device__ __forceinline__ float wave_total(float v) { return rows4_sum(row16_sum(v)); }
 #undef SSM_DPP
 
-// Lane index the compiler cannot treat as loop-invariant: shuffle addresses derived
-// from it are formed where they are used instead of being held in registers across
-// loops.
-__device__ __forceinline__ int lane_here() {
-    int l = static_cast<int>(__lane_id());
-    asm volatile("" : "+v"(l));
-    return l;
-}
-__device__ __forceinline__ float lane_read(float v, int src) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
-}
-// inclusive prefix sum over the wave (lane 0 first)
+// Inclusive prefix sum over the wave (lane 0 first) with DPP: row_shr 1, 2, 4, 8
+// scan each row of 16 (lanes shifted in from outside the row add zero), then
+// row_bcast15 adds row r's total into row r+1 (rows 1, 3) and row_bcast31 adds the
+// first half's total into rows 2, 3.
+#define SSM_DPP0(v, ctrl, rmask) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), (rmask), 0xf, true))
 __device__ __forceinline__ float wave_prefix_sum(float v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int l = lane_here();
-        const float o = lane_read(v, l - off);
-        if (l >= off) v += o;
-    }
+    v += SSM_DPP0(v, 0x111, 0xf);  // row_shr:1
+    v += SSM_DPP0(v, 0x112, 0xf);  // row_shr:2
+    v += SSM_DPP0(v, 0x114, 0xf);  // row_shr:4
+    v += SSM_DPP0(v, 0x118, 0xf);  // row_shr:8
+    v += SSM_DPP0(v, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+    v += SSM_DPP0(v, 0x143, 0xc);  // row_bcast:31 into rows 2 and 3
     return v;
 }
-// inclusive suffix sum over the wave (lane 63 first)
+#undef SSM_DPP0
+// inclusive suffix sum over the wave (lane 63 first): the prefix sum of the
+// lane-reversed values, reversed back (row_mirror within rows, then the two
+// permlane swaps exchange rows r and 3-r).
+__device__ __forceinline__ float lane_reverse(float v) {
+    v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false));
+    uint32_t u = __float_as_uint(v);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // (lo,lo) / (hi,hi)
+    // lane l < 32 takes the upper half, lane l >= 32 the lower half
+    const bool lo = (__lane_id() < 32);
+    u = lo ? r32[1] : r32[0];
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows (0,0,2,2) / (1,1,3,3)
+    const bool even = ((__lane_id() >> 4) & 1) == 0;
+    u = even ? r16[1] : r16[0];
+    return __uint_as_float(u);
+}
 __device__ __forceinline__ float wave_suffix_sum(float v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int l = lane_here();
-        const float o = lane_read(v, l + off);
-        if (l + off < 64) v += o;
-    }
-    return v;
+    return lane_reverse(wave_prefix_sum(lane_reverse(v)));
 }
 
 // Raw buffer access over one chunk's rows.  The hardware range-checks the per-lane
