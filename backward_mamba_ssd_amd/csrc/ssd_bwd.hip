@@ -267,6 +267,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         for (int kb = 0; kb < kMaxBlk; ++kb)  // blocks past the chunk read zero
             xr[kb] = buf_ld_16b(kb <= k ? rx : ry, o + kb * kLs * tokb);
         yk = buf_ld_16b(ry, o + k * kLs * tokb);
+    };
+    // dt of head h, four tokens per lane (wave 0 only; consumed by the scan)
+    auto prefetch_dt = [&](int h) {
         if (wave == 0) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -303,6 +306,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 
     const int h0 = g * hpg;
     prefetch(h0);
+    prefetch_dt(h0);
     load_states(h0);
     if (wave == 0) scan(h0, 0);
     __syncthreads();
@@ -352,6 +356,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const float *lam = sm.lam[par], *dts = sm.dt[par];
         const float lam_blk0 = kS >= 0 ? lam[kS] : 0.f;  // block-local Lam_i = lam[base+i] - lam_blk0
         const float lam_e = lam[kE];
+        if (hh + 1 < hpg) prefetch_dt(h + 1);  // used by the next head's scan in S3
         // ---- S1: stage this head's rows (scaled for the state products) ----
 #pragma unroll
         for (int kb = 0; kb < kMaxBlk; ++kb) {

@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 
 
 def log(*a):
@@ -51,6 +52,44 @@ def bwd_block_bytes_per_token(w):
     read (2 B), dB and dC written (4 B), dt read and ddt written (4 B)."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     return (3 * 2 * H * P + 2 * 4 * H * P * N / L + 2 * 2 * G * N + 2 * 4 * G * N + 2 * 4 * H)
+
+
+def fwd_flops_per_token(w):
+    """The method's MFMA-mapped flops of the chunked forward per token (causal halves
+    counted once): group Gram L*N/hpg, intra-chunk output L*P, chunk state 2PN,
+    off-diagonal output 2PN, per head."""
+    H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    return H * (L * N / (H // G) + L * P + 3 * 2 * P * N)
+
+
+def bwd_flops_per_token(w):
+    """The method's flops of the backward per token: off-diagonal + reverse state pass
+    4PN, intra-chunk 2LP + 3LN/hpg, chunk-state gradients 4PN, per head."""
+    H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    return H * (4 * P * N + 2 * L * P + 3 * L * N / (H // G) + 4 * P * N)
+
+
+def bwd_call_bytes_per_token(w):
+    """Algorithmic HBM bytes per token of the whole backward call of this design: the
+    reverse state pass (dy and C read, chunk-exit state gradients written once per
+    chunk) plus the per-block kernel (bwd_block_bytes_per_token)."""
+    H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    return 2 * H * P + 2 * G * N + 4 * H * P * N / L + bwd_block_bytes_per_token(w)
+
+
+def path_entry(flops, nbytes, ms, flop_peak_tflops=None):
+    """flops, bytes, rates and the fraction of both roofs for one timed path."""
+    sec = ms * 1e-3
+    gbps = nbytes / sec / 1e9
+    e = {"ms": round(ms, 4), "bytes": int(nbytes), "GBps": round(gbps, 1),
+         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    if flops:
+        tf = flops / sec / 1e12
+        peak = flop_peak_tflops or BF16_PEAK_TFLOPS
+        e.update({"flops": float(flops), "TFLOPs": round(tf, 2), "flop_peak_TFLOPs": peak,
+                  "flop_frac": round(tf / peak, 4)})
+        e["bound"] = "hbm" if e["hbm_frac"] >= e["flop_frac"] else "flop"
+    return e
 
 
 KERNEL_SOURCES = {
@@ -100,7 +139,7 @@ def fwd_mfma_flops_per_token(w):
     return 2 * per_block_macs / 64 * w.nheads
 
 
-def cpu_baseline(w, budget_s=20.0):
+def cpu_baseline(w, budget_s=30.0):
     """fp64 oracle (sequential recurrence + reverse sweep) on a bounded sample:
     4 batches x 4 groups (128 heads) x a token window, grown until the run takes
     a few seconds; reported as equivalent full-width tokens/s (tokens x heads
@@ -137,8 +176,144 @@ def cpu_baseline(w, budget_s=20.0):
     }
 
 
+def time_fwd_bwd(w, dev, steps, warmup):
+    """Time `steps` fwd+bwd steps of workload w (inputs resident before timing).
+    Returns per-step event means/medians and the wall-clock over the timed steps."""
+    import statistics
+
+    import torch
+
+    from backward_mamba_ssd_amd import inputs, ssm
+
+    pr = inputs.make_workload_problem(w, dev)
+    dims = ssm.dims_of(pr["x"], pr["B"], w.chunk)
+    b, t, h, p = pr["x"].shape
+    g, n = pr["B"].shape[2], pr["B"].shape[3]
+    nc = (t + w.chunk - 1) // w.chunk
+    f32 = dict(dtype=torch.float32, device=dev)
+    y = torch.empty_like(pr["x"])
+    cs = torch.empty((b, h, nc, p, n), **f32)
+    grads = {"dx": torch.empty_like(pr["x"]), "dB": torch.empty((b, t, g, n), **f32),
+             "dC": torch.empty((b, t, g, n), **f32), "ddt": torch.empty((b, t, h), **f32),
+             "dA": torch.empty((h,), **f32), "dD": torch.empty((h,), **f32), "dh0": None}
+    ws = torch.empty(ssm.ssm_workspace_bytes(dims, ssm.SSM_BF16, ssm.SSM_WS_BWD),
+                     dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], chunk=w.chunk,
+                            h_final=None, chunk_states=cs, y=y)
+        if ev is not None:
+            ev[1].record()
+            ssm.ssm_profile_next_bwd_block(ev[2], ev[3])
+        ssm.ssm_bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], cs, pr["dy"],
+                    chunk=w.chunk, out=grads, workspace=ws)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+
+    def stat(i, j):
+        v = [e[i].elapsed_time(e[j]) for e in evs]
+        return sum(v) / len(v), statistics.median(v)
+
+    r = {"tokens": b * t, "wall_s": el,
+         "fwd": stat(0, 1), "blk": stat(2, 3), "bwd": stat(1, 4), "step": stat(0, 4)}
+    del pr, y, cs, grads, ws
+    torch.cuda.empty_cache()
+    return r
+
+
+def measured_peaks(dev):
+    """Achievable rates on this GPU: a 1 GiB device-to-device copy (read + write bytes)
+    and an 8192^3 bf16 matrix product (torch / hipBLASLt)."""
+    import torch
+
+    out = {}
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_GBps"] = round(2 * src.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    n = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    bm = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16).contiguous()
+    for _ in range(2):
+        torch.mm(a, bm)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.mm(a, bm)
+    e1.record()
+    torch.cuda.synchronize()
+    out["bf16_gemm_TFLOPs"] = round(2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    del a, bm
+    torch.cuda.empty_cache()
+    return out
+
+
+def replay_sweep(dev):
+    """Replay r tokens from SR16 checkpoints at the checkpoint workload's shape
+    (16 sequences x 256 heads x [64,128]): bytes, GB/s and fp32-VALU fraction."""
+    import torch
+
+    from backward_mamba_ssd_amd import inputs, ssm
+
+    w = inputs.WORKLOADS["ckpt_replay_b16_t16384"]
+    rmax = 1024
+    pr = inputs.make_problem(w.batch, rmax, w.nheads, w.headdim, w.dstate, w.ngroups, "bf16",
+                             w.seed, dev, with_dy=False)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 99)
+    live = torch.randn((w.batch, w.nheads, w.headdim, w.dstate), generator=g, device=dev)
+    bits = ssm.ssm_checkpoint_sr16(live, 5, 0)
+    out_state = torch.empty_like(live)
+    heads = w.batch * w.nheads
+    PN = w.headdim * w.dstate
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in (1, 4, 16, 64, 256, 1024):
+        ssm.ssm_replay(bits, pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], 0, r,
+                       state_out=out_state)
+        torch.cuda.synchronize()
+        reps = 20 if r <= 64 else 5
+        e0.record()
+        for _ in range(reps):
+            ssm.ssm_replay(bits, pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], 0, r,
+                           state_out=out_state)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = heads * (PN * (2 + 4) + r * (2 * w.headdim + 4 + 2 * 2 * w.dstate * w.ngroups
+                                                  / w.nheads))
+        flops = heads * 3 * PN * r
+        res[f"r{r}"] = path_entry(flops, nbytes, ms, FP32_VALU_PEAK_TFLOPS)
+    del pr, live, bits, out_state
+    torch.cuda.empty_cache()
+    return res
+
+
 def secondary(dev):
-    """Decode (full 64 x 48 x 100 workload) and SR16 rates."""
+    """Decode (full 64 x 48 x 100 workload), SR16 and replay rates."""
     import torch
 
     from backward_mamba_ssd_amd import inputs, ssm
@@ -166,11 +341,11 @@ def secondary(dev):
     PN = w.headdim * w.dstate
     per_call = (w.batch * w.nheads * (8 * PN + 2 * 2 * w.headdim + 4)
                 + w.batch * w.ngroups * 2 * 2 * w.dstate)
-    gbps = steps * layers * per_call / (ms * 1e-3) / 1e9
-    out["decode_state_update_GBps"] = round(gbps, 1)
-    out["decode_hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
-    out["decode_ms_per_step_48_layers"] = round(ms / steps, 4)
-    out["decode_tokens_per_s"] = round(w.batch * steps / (ms * 1e-3), 1)
+    dec = path_entry(steps * layers * w.batch * w.nheads * 5 * PN, steps * layers * per_call, ms,
+                     FP32_VALU_PEAK_TFLOPS)
+    dec["ms_per_step_48_layers"] = round(ms / steps, 4)
+    dec["tokens_per_s"] = round(w.batch * steps / (ms * 1e-3), 1)
+    out["decode"] = dec
     st = pr["state"][0]
     del pr
     bits = torch.empty(st.shape, dtype=torch.int16, device=dev)
@@ -181,8 +356,20 @@ def secondary(dev):
         ssm.ssm_checkpoint_sr16(st, 1, k, out=bits)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 20
-    out["sr16_GBps"] = round(st.numel() * 6 / (ms * 1e-3) / 1e9, 1)
+    out["sr16"] = path_entry(0, st.numel() * 6, e0.elapsed_time(e1) / 20)
+    del st, bits
+    torch.cuda.empty_cache()
+    log("replay sweep ...")
+    out["replay_sr16_b16"] = replay_sweep(dev)
+    wl = inputs.WORKLOADS["long_b1_t131072"]
+    log(f"long context: {wl.name}")
+    r = time_fwd_bwd(wl, dev, steps=3, warmup=1)
+    fb = fwd_flops_per_token(wl) + bwd_flops_per_token(wl)
+    by = fwd_bytes_per_token(wl) + bwd_call_bytes_per_token(wl)
+    lc = path_entry(fb * r["tokens"], by * r["tokens"], r["step"][1])
+    lc["tokens_per_s"] = round(r["tokens"] * 3 / r["wall_s"], 1)
+    lc["workload"] = wl.name
+    out["long_context_fwd_bwd"] = lc
     return out
 
 
@@ -205,54 +392,17 @@ def main():
 
     import torch
 
-    from backward_mamba_ssd_amd import inputs, ssm
+    from backward_mamba_ssd_amd import inputs
 
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
     log(f"workload {w.name}: batch {w.batch} T {w.seqlen} heads {w.nheads} P {w.headdim} "
         f"N {w.dstate} groups {w.ngroups} chunk {w.chunk}")
-    pr = inputs.make_workload_problem(w, dev)
-    dims = ssm.dims_of(pr["x"], pr["B"], w.chunk)
-    assert ssm.ssm_uses_mfma_path(dims, ssm.SSM_BF16)
-    b, t, h, p = pr["x"].shape
-    g, n = pr["B"].shape[2], pr["B"].shape[3]
-    nc = (t + w.chunk - 1) // w.chunk
-    f32 = dict(dtype=torch.float32, device=dev)
-    y = torch.empty_like(pr["x"])
-    cs = torch.empty((b, h, nc, p, n), **f32)
-    grads = {"dx": torch.empty_like(pr["x"]), "dB": torch.empty((b, t, g, n), **f32),
-             "dC": torch.empty((b, t, g, n), **f32), "ddt": torch.empty((b, t, h), **f32),
-             "dA": torch.empty((h,), **f32), "dD": torch.empty((h,), **f32), "dh0": None}
-    ws = torch.empty(ssm.ssm_workspace_bytes(dims, ssm.SSM_BF16, ssm.SSM_WS_BWD),
-                     dtype=torch.uint8, device=dev)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], chunk=w.chunk,
-                            h_final=None, chunk_states=cs, y=y)
-        if ev is not None:
-            ev[1].record()
-            ssm.ssm_profile_next_bwd_block(ev[2], ev[3])
-        ssm.ssm_bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], cs, pr["dy"],
-                    chunk=w.chunk, out=grads, workspace=ws)
-        if ev is not None:
-            ev[4].record()
-
-    for _ in range(args.warmup):
-        step()
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        step(evs[k])
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
-    blk_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
-    bwd_ms = sum(e[1].elapsed_time(e[4]) for e in evs) / K
-    tokens = b * t
+    r = time_fwd_bwd(w, dev, K, args.warmup)
+    tokens = r["tokens"]
+    el = r["wall_s"]
+    fwd_ms, blk_ms, bwd_ms = r["fwd"][0], r["blk"][0], r["bwd"][0]
     value = tokens * K / el
     log(f"step {el / K * 1e3:.3f} ms: forward kernel {fwd_ms:.3f} ms, backward call {bwd_ms:.3f} ms "
         f"(per-block kernel {blk_ms:.3f} ms)")
@@ -268,6 +418,13 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(dom, w.name),
                 "kernel": dom, "mean_ms": round(ms, 4), "bytes_per_launch": int(nbytes)}
+    ff, bf = fwd_flops_per_token(w) * tokens, bwd_flops_per_token(w) * tokens
+    fb, bb = fwd_bytes_per_token(w) * tokens, bwd_call_bytes_per_token(w) * tokens
+    paths = {
+        "fwd_chunked": path_entry(ff, fb, r["fwd"][1]),
+        "bwd_call": path_entry(bf, bb, r["bwd"][1]),
+        "fwd_bwd_step": path_entry(ff + bf, fb + bb, r["step"][1]),
+    }
     res = {
         "metric": "SSM fwd+bwd tokens/s at 256h x 64 x 128",
         "value": round(value, 1),
@@ -281,17 +438,24 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; x,B,C,dy bf16; dt,A,D fp32)",
-        "config": {"workload": w.name, "batch": b, "seqlen": t, "nheads": h, "headdim": p,
-                   "dstate": n, "ngroups": g, "chunk": w.chunk},
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk": w.chunk},
         "roofline": roofline,
         "kernels_ms": {"ssd_fwd_kernel": round(fwd_ms, 4), "ssm_bwd_call": round(bwd_ms, 4),
                        "ssd_bwd_block_kernel": round(blk_ms, 4)},
+        "kernels_median_ms": {"ssd_fwd_kernel": round(r["fwd"][1], 4),
+                              "ssm_bwd_call": round(r["bwd"][1], 4),
+                              "ssd_bwd_block_kernel": round(r["blk"][1], 4)},
+        "paths": paths,
         "fwd_mfma_frac": round(fwd_mfma_flops_per_token(w) * tokens / (fwd_ms * 1e-3)
                                / (BF16_PEAK_TFLOPS * 1e12), 4),
     }
-    del pr, y, cs, grads, ws
-    torch.cuda.empty_cache()
     if not args.no_secondary:
+        pk = measured_peaks(dev)
+        res["measured_peaks"] = pk
+        roofline["measured_peak"] = pk["copy_GBps"]
+        roofline["frac_of_measured"] = round(achieved / pk["copy_GBps"], 4)
         res["secondary"] = secondary(dev)
         torch.cuda.empty_cache()
     if args.copy_calibration:
