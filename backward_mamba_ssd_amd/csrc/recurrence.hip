@@ -16,6 +16,8 @@
 // Thread mapping (both kernels): a state row of N floats is covered by
 // LPR = N/4 lanes holding 4 consecutive coordinates each (16-byte accesses);
 // a 256-thread workgroup covers 256/LPR rows per pass and one (batch, head).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -43,12 +45,11 @@ __device__ __forceinline__ void row_update(float4 &s, float a, float xp, const f
     s.w = fmaf(a, s.w, __fmul_rn(xp, bdt.w));
 }
 
-// Sum over the LPR lanes of one row (fixed xor tree).
+// Sum over the LPR lanes of one row (DPP within 16-lane rows, permlane swaps
+// across them; the same fixed order in decode and replay).
 template <int LPR>
 __device__ __forceinline__ float row_reduce(float acc) {
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-    return acc;
+    return lane_group_reduce<LPR, false>(acc);
 }
 
 __device__ __forceinline__ float retention(float dtv, float Ah) { return expf(__fmul_rn(dtv, Ah)); }
@@ -79,6 +80,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < MAXR; ++i) {
         const int p = r0 + i * RPW;
+        s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (p < a.P) s[i] = *reinterpret_cast<const float4 *>(st + static_cast<int64_t>(p) * N + n0);
     }
     const float dtv = a.dt[bh];
@@ -89,11 +91,12 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const float4 c = IO<T>::ld4(Cm, bgN);
 #pragma unroll
     for (int i = 0; i < MAXR; ++i) {
+        if (i * RPW >= a.P) break;  // uniform: no row of this pass exists
         const int p = r0 + i * RPW;
+        const float xp = (p < a.P) ? IO<T>::ld(x, static_cast<int64_t>(bh) * a.P + p) : 0.f;
+        float acc = row_step(s[i], av, xp, bdt, c);
+        acc = row_reduce<LPR>(acc);  // whole rows are active or inactive together
         if (p < a.P) {
-            const float xp = IO<T>::ld(x, static_cast<int64_t>(bh) * a.P + p);
-            float acc = row_step(s[i], av, xp, bdt, c);
-            acc = row_reduce<LPR>(acc);
             *reinterpret_cast<float4 *>(st + static_cast<int64_t>(p) * N + n0) = s[i];
             if ((tid % LPR) == 0)
                 IO<T>::st(static_cast<T *>(a.y), static_cast<int64_t>(bh) * a.P + p,
@@ -103,12 +106,31 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Token-serial scan / replay: state in registers across r tokens.
+// Token-serial scan / replay: state in registers across r tokens.  The per-token
+// inputs are staged in LDS TT tokens at a time (the retention factor, B*dt and C
+// as floats, x permuted so a thread's MAXR rows are contiguous), and the next
+// tile is loaded into registers while the current one is consumed.
 // ---------------------------------------------------------------------------
+template <int N>
+struct ScanTile {
+    static constexpr int LPR = N / 4;                       // lanes per state row
+    static constexpr int RPW = 256 / LPR;                   // rows per pass
+    static constexpr int TT = (2 * LPR < 16) ? 2 * LPR : 16;  // tokens per tile
+    static constexpr int NJ = (TT * LPR + 255) / 256;       // (token, 4 coords) items per thread
+    static constexpr int XW = 8 * RPW;                      // staged x width (MAXR = 8 passes)
+    static constexpr int XJ = TT * XW / 256;                // x elements per thread
+};
+
 template <int N, int MAXR, typename T, typename CK, bool LIVE>
 __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
-    constexpr int LPR = N / 4;
-    constexpr int RPW = 256 / LPR;
+    using TL = ScanTile<N>;
+    constexpr int LPR = TL::LPR, RPW = TL::RPW, TT = TL::TT, NJ = TL::NJ, XW = TL::XW, XJ = TL::XJ;
+    static_assert(MAXR == 8, "tile layout assumes 8 row passes");
+    __shared__ float s_av[TT];
+    __shared__ __align__(16) float s_bdt[TT * N];
+    __shared__ __align__(16) float s_c[TT * N];
+    __shared__ __align__(16) float s_x[TT * XW];
+
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x;
@@ -119,6 +141,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     const T *Bm = static_cast<const T *>(a.B);
     const T *Cm = static_cast<const T *>(a.C);
     T *y = static_cast<T *>(a.y);
+    const bool want_y = (y != nullptr);
 
     float4 s[MAXR];
     float4 l[LIVE ? MAXR : 1];
@@ -147,48 +170,112 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     const int wave = tid / 64, lane = tid % 64;
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
 
-    for (int64_t k = 0; k < a.r; ++k) {
-        const int64_t t = a.t0 + k;
-        if (a.chunk_states != nullptr && (k % a.L) == 0) {
-            float *cs = a.chunk_states + (bh * a.nchunks + k / a.L) * PN;
+    // next tile in registers: (token, 4 coords) items of B, C with their dt; x elements
+    using Raw4 = typename std::conditional<sizeof(T) == 2, u16x4, float4>::type;
+    Raw4 rb[NJ], rc[NJ];
+    float rdt[NJ], rx[XJ];
+    auto raw4 = [](const T *p, int64_t i) { return *reinterpret_cast<const Raw4 *>(p + i); };
+    auto wide4 = [](const Raw4 &v) -> float4 {
+        if constexpr (sizeof(T) == 2)
+            return make_float4(bf16_to_f32(v[0]), bf16_to_f32(v[1]), bf16_to_f32(v[2]), bf16_to_f32(v[3]));
+        else
+            return v;
+    };
+    auto prefetch = [&](int64_t k0) {
 #pragma unroll
-            for (int i = 0; i < MAXR; ++i) {
-                const int p = r0 + i * RPW;
-                if (p < a.P) *reinterpret_cast<float4 *>(cs + static_cast<int64_t>(p) * N + n0) = s[i];
+        for (int j = 0; j < NJ; ++j) {
+            const int q = tid + 256 * j, tt = q / LPR, nn = (q % LPR) * 4;
+            rb[j] = rc[j] = Raw4{};
+            rdt[j] = 0.f;
+            if (q < TT * LPR && k0 + tt < a.r) {
+                const int64_t bt = static_cast<int64_t>(b) * a.T + a.t0 + k0 + tt;
+                const int64_t bgN = (bt * a.G + g) * N + nn;
+                rb[j] = raw4(Bm, bgN);
+                rc[j] = raw4(Cm, bgN);
+                rdt[j] = a.dt[bt * a.H + h];
             }
         }
-        const int64_t bt = static_cast<int64_t>(b) * a.T + t;
-        const float dtv = a.dt[bt * a.H + h];
-        const float av = retention(dtv, Ah);
-        const int64_t bgN = (bt * a.G + g) * N + n0;
-        const float4 bdt = scale4(IO<T>::ld4(Bm, bgN), dtv);
-        const float4 c = IO<T>::ld4(Cm, bgN);
-        const int64_t xrow = (bt * a.H + h) * a.P;
-        float dmax = 0.f, dsum = 0.f;
 #pragma unroll
-        for (int i = 0; i < MAXR; ++i) {
-            const int p = r0 + i * RPW;
-            if (p < a.P) {
-                const float xp = IO<T>::ld(x, xrow + p);
-                float acc = row_step(s[i], av, xp, bdt, c);
-                acc = row_reduce<LPR>(acc);
-                if (y != nullptr && (tid % LPR) == 0) IO<T>::st(y, xrow + p, fmaf(Dh, xp, acc));
-                if constexpr (LIVE) {
-                    row_update(l[i], av, xp, bdt);
+        for (int j = 0; j < XJ; ++j) {
+            const int e = tid + 256 * j, tt = e / XW, p = e % XW;
+            rx[j] = 0.f;
+            if (p < a.P && k0 + tt < a.r) {
+                const int64_t bt = static_cast<int64_t>(b) * a.T + a.t0 + k0 + tt;
+                rx[j] = IO<T>::ld(x, (bt * a.H + h) * a.P + p);
+            }
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int q = tid + 256 * j, tt = q / LPR, nn = (q % LPR) * 4;
+            if (q < TT * LPR) {
+                *reinterpret_cast<float4 *>(&s_bdt[tt * N + nn]) = scale4(wide4(rb[j]), rdt[j]);
+                *reinterpret_cast<float4 *>(&s_c[tt * N + nn]) = wide4(rc[j]);
+                if (nn == 0) s_av[tt] = retention(rdt[j], Ah);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) {
+            const int e = tid + 256 * j, tt = e / XW, p = e % XW;
+            s_x[tt * XW + (p % RPW) * MAXR + p / RPW] = rx[j];  // row p = r0 + i*RPW -> r0*MAXR + i
+        }
+    };
+
+    if (a.r > 0) prefetch(0);
+    for (int64_t k0 = 0; k0 < a.r; k0 += TT) {
+        __syncthreads();  // the previous tile has been consumed
+        stage();
+        __syncthreads();
+        if (k0 + TT < a.r) prefetch(k0 + TT);
+        const int nt = (a.r - k0 < TT) ? static_cast<int>(a.r - k0) : TT;
+        for (int tt = 0; tt < nt; ++tt) {
+            const int64_t k = k0 + tt;
+            if (a.chunk_states != nullptr && (k % a.L) == 0) {
+                float *cs = a.chunk_states + (bh * a.nchunks + k / a.L) * PN;
+#pragma unroll
+                for (int i = 0; i < MAXR; ++i) {
+                    const int p = r0 + i * RPW;
+                    if (p < a.P) *reinterpret_cast<float4 *>(cs + static_cast<int64_t>(p) * N + n0) = s[i];
+                }
+            }
+            const float av = s_av[tt];
+            const float4 bdt = *reinterpret_cast<const float4 *>(&s_bdt[tt * N + n0]);
+            const float4 xa = *reinterpret_cast<const float4 *>(&s_x[tt * XW + r0 * MAXR]);
+            const float4 xb = *reinterpret_cast<const float4 *>(&s_x[tt * XW + r0 * MAXR + 4]);
+            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            float dmax = 0.f, dsum = 0.f;
+            if (want_y) {
+                const float4 c = *reinterpret_cast<const float4 *>(&s_c[tt * N + n0]);
+                const int64_t xrow = ((static_cast<int64_t>(b) * a.T + a.t0 + k) * a.H + h) * a.P;
+#pragma unroll
+                for (int i = 0; i < MAXR; ++i) {
+                    if (i * RPW >= a.P) break;  // uniform
+                    const int p = r0 + i * RPW;
+                    float acc = row_step(s[i], av, xv[i], bdt, c);
+                    acc = row_reduce<LPR>(acc);
+                    if (p < a.P && (tid % LPR) == 0) IO<T>::st(y, xrow + p, fmaf(Dh, xv[i], acc));
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < MAXR; ++i) row_update(s[i], av, xv[i], bdt);
+            }
+            if constexpr (LIVE) {
+#pragma unroll
+                for (int i = 0; i < MAXR; ++i) {
+                    row_update(l[i], av, xv[i], bdt);  // rows past P stay zero in both copies
                     const float d0 = fabsf(s[i].x - l[i].x), d1 = fabsf(s[i].y - l[i].y);
                     const float d2 = fabsf(s[i].z - l[i].z), d3 = fabsf(s[i].w - l[i].w);
                     dmax = fmaxf(dmax, fmaxf(fmaxf(d0, d1), fmaxf(d2, d3)));
                     dsum += (d0 + d1) + (d2 + d3);
                 }
-            }
-        }
-        if constexpr (LIVE) {
-            dmax = wave_max(dmax);
-            dsum = wave_sum(dsum);
-            if (lane == 0) {
-                const int64_t w = static_cast<int64_t>(bh) * 4 + wave;
-                a.part_max[k * nwaves + w] = dmax;
-                a.part_sum[k * nwaves + w] = dsum;
+                dmax = lane_group_reduce<64, true>(dmax);
+                dsum = lane_group_reduce<64, false>(dsum);
+                if (lane == 0) {
+                    const int64_t w = static_cast<int64_t>(bh) * 4 + wave;
+                    a.part_max[k * nwaves + w] = dmax;
+                    a.part_sum[k * nwaves + w] = dsum;
+                }
             }
         }
     }

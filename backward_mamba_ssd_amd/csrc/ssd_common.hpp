@@ -57,75 +57,6 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
     return (i & 7) * (n >> 3) + (i >> 3);
 }
 
-// Cross-lane sums without lane-address registers.  A 64-lane wave is four rows of
-// 16 lanes.  Within a row, DPP swaps neighbours (quad_perm 1,0,3,2 and 2,3,0,1), then
-// mirrors half-rows and rows; across rows, the gfx950 permlane swaps pair row r with
-// r^1 and the half-waves with each other.  Each helper returns the sum in every lane
-// it covers; the order of additions is fixed, so results are deterministic.
-#define SSM_DPP(v, ctrl) \
-    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), 0xf, 0xf, false))
-// sum over the 16 lanes of the row
-__device__ __forceinline__ float row16_sum(float v) {
-    v += SSM_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
-    v += SSM_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
-    v += SSM_DPP(v, 0x141);  // row_half_mirror
-    v += SSM_DPP(v, 0x140);  // row_mirror
-    return v;
-}
-// sum over lanes l, l^16, l^32, l^48.  A swap given the same value in both operands
-// returns rows (0,0,2,2)/(1,1,3,3) for the 16-lane form and halves (lo,lo)/(hi,hi)
-// for the 32-lane form, so the sum of its two results is the pair sum.  The results
-// are read with __uint_as_float: __builtin_bit_cast of a subscript of the returned
-// pair reads element 0 for both.
-__device__ __forceinline__ float swap_pair_sum16(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float swap_pair_sum32(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float rows4_sum(float v) { return swap_pair_sum32(swap_pair_sum16(v)); }
-__device__ __forceinline__ float wave_total(float v) { return rows4_sum(row16_sum(v)); }
-#undef SSM_DPP
-
-// Inclusive prefix sum over the wave (lane 0 first) with DPP: row_shr 1, 2, 4, 8
-// scan each row of 16 (lanes shifted in from outside the row add zero), then
-// row_bcast15 adds row r's total into row r+1 (rows 1, 3) and row_bcast31 adds the
-// first half's total into rows 2, 3.
-#define SSM_DPP0(v, ctrl, rmask) \
-    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), (rmask), 0xf, true))
-__device__ __forceinline__ float wave_prefix_sum(float v) {
-    v += SSM_DPP0(v, 0x111, 0xf);  // row_shr:1
-    v += SSM_DPP0(v, 0x112, 0xf);  // row_shr:2
-    v += SSM_DPP0(v, 0x114, 0xf);  // row_shr:4
-    v += SSM_DPP0(v, 0x118, 0xf);  // row_shr:8
-    v += SSM_DPP0(v, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
-    v += SSM_DPP0(v, 0x143, 0xc);  // row_bcast:31 into rows 2 and 3
-    return v;
-}
-#undef SSM_DPP0
-// inclusive suffix sum over the wave (lane 63 first): the prefix sum of the
-// lane-reversed values, reversed back (row_mirror within rows, then the two
-// permlane swaps exchange rows r and 3-r).
-__device__ __forceinline__ float lane_reverse(float v) {
-    v = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false));
-    uint32_t u = __float_as_uint(v);
-    const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // (lo,lo) / (hi,hi)
-    // lane l < 32 takes the upper half, lane l >= 32 the lower half
-    const bool lo = (__lane_id() < 32);
-    u = lo ? r32[1] : r32[0];
-    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows (0,0,2,2) / (1,1,3,3)
-    const bool even = ((__lane_id() >> 4) & 1) == 0;
-    u = even ? r16[1] : r16[0];
-    return __uint_as_float(u);
-}
-__device__ __forceinline__ float wave_suffix_sum(float v) {
-    return lane_reverse(wave_prefix_sum(lane_reverse(v)));
-}
-
 // Raw buffer access over one chunk's rows.  The hardware range-checks the per-lane
 // byte offset against `bytes`: reads at or past it return zero and writes there are
 // dropped, so ragged tails need no branches.  The scalar offset is always 0 (it is
