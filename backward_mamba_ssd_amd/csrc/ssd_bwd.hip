@@ -179,8 +179,10 @@ struct BlkSmem {
                                         // then H and dH in bf16 ([p][n])
     bf16_t X[kT64], dY[kT64], QT[kT64]; // block k rows of x, dy; Q^T [j][i]
     float lam[2][kMaxBlk * kLs], dt[2][kMaxBlk * kLs];  // chunk-local, by head parity
-    float row[2][kLs], col[4][kLs], dd[4][kLs], off[8][kLs], fin[8][kLs];
-    float dot[8], dd_sum[8];
+    // row, col, dd_sum are written before the S2 barrier and read by the combine of the
+    // previous head during S2, so they are double-buffered by head parity
+    float row[2][2][kLs], col[2][4][kLs], dd[4][kLs], off[8][kLs], fin[8][kLs];
+    float dot[8], dd_sum[2][8];
 };
 static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the state tiles");
 
@@ -348,6 +350,47 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const int kEnd = 64 * nbc - 1;          // last (padded) token of the chunk
     const int base = 64 * k;
 
+    // Per-token combine of head hc (wave 0, lane = token of the block): the dLam terms,
+    // da = reverse cumulative sum within the block, ddt, and the dA/dD partials.  Runs
+    // for head h-1 during head h's S2 (the arrays it reads are rewritten only after
+    // that phase's barrier, or are double-buffered by head parity).
+    auto combine = [&](int hc, int pc) {
+        const int j = lane;
+        const float *lamc = sm.lam[pc], *dtc = sm.dt[pc];
+        const float lb0 = kS >= 0 ? lamc[kS] : 0.f;
+        const float le = lamc[kE];
+        float dl = sm.row[pc][0][j] + sm.row[pc][1][j];
+        float ddd = 0.f, fs = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            dl -= sm.col[pc][w][j];
+            ddd += sm.dd[w][j];
+        }
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            dl += sm.off[w][j] - sm.fin[w][j];
+            fs += sm.fin[w][j];
+        }
+        const float fin_total = wave_total(fs);
+        if (j == kLs - 1) {
+            float dotv = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) dotv += sm.dot[w];
+            dl += fin_total + __expf(le - lb0) * dotv;
+        }
+        const float da = wave_suffix_sum(dl);  // da_j = sum_{i >= j} dLam_i within the block
+        buf_st_f32(rddt, (static_cast<uint32_t>(k * kLs + j) * a.H + hc) * 4u, fmaf(a.A[hc], da, ddd));
+        const float pa = wave_total(dtc[base + j] * da);
+        if (lane == 0) {
+            float ds = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) ds += sm.dd_sum[pc][w];
+            const int64_t pi = ((static_cast<int64_t>(b) * a.H + hc) * a.nchunks + c) * nb + k;
+            a.pA[pi] = static_cast<double>(pa);
+            a.pD[pi] = static_cast<double>(ds);
+        }
+    };
+
     for (int hh = 0; hh < hpg; ++hh) {
         refresh_lane();
         const int h = h0 + hh, par = hh & 1;
@@ -380,6 +423,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         __syncthreads();
         if (hh + 1 < hpg) prefetch(h + 1);  // registers are free once staged
         // ---- S2: state products over the other blocks; Phase I of block k ----
+        if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
         // Each A fragment (16 state rows n of one block's B or C) is read once and used
         // for all four p-tiles.
         {
@@ -452,15 +496,15 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 }
                 *reinterpret_cast<u16x4 *>(&sm.QT[j * kS64 + 16 * wq + lq]) = pack4(qv[0], qv[1], qv[2], qv[3]);
                 colacc = rows4_sum(colacc);
-                if (lane < 16) sm.col[wq][j] = colacc;
+                if (lane < 16) sm.col[par][wq][j] = colacc;
             }
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const float r = row16_sum(rowacc[v]);
-                if (lr == 0) sm.row[wh][16 * wq + lq + v] = r;
+                if (lr == 0) sm.row[par][wh][16 * wq + lq + v] = r;
             }
             diag = wave_total(diag);
-            if (lane == 0) sm.dd_sum[wave] = diag;
+            if (lane == 0) sm.dd_sum[par][wave] = diag;
         }
         __syncthreads();
         // ---- S3: block-entry state and exit gradient in bf16, [p][n] ----
@@ -547,18 +591,18 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 }
                 const float ei = __expf(lam[base + i] - lam_blk0);
                 const float wdt = __expf(lam_e - lam[base + i]) * dts[base + i];
+                // the token's scale (ei, wdt) is fused into the accumulate and applied to
+                // the dot products once after their reduction
                 float o = 0.f, f = 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    ac[v] *= ei;
-                    ab[v] *= wdt;
                     o = fmaf(cC[tt][v], ac[v], o);
                     f = fmaf(cB[tt][v], ab[v], f);
-                    dCa[tt][v] += ac[v];
-                    dBa[tt][v] += ab[v];
+                    dCa[tt][v] = fmaf(ac[v], ei, dCa[tt][v]);
+                    dBa[tt][v] = fmaf(ab[v], wdt, dBa[tt][v]);
                 }
-                o = rows4_sum(o);
-                f = rows4_sum(f);
+                o = rows4_sum(o) * ei;
+                f = rows4_sum(f) * wdt;
                 if (lane < 16) {
                     sm.off[wave][i] = o;
                     sm.fin[wave][i] = f;
@@ -566,41 +610,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             }
         }
         __syncthreads();
-        // ---- S5: combine per token (wave 0, lane = token of the block) ----
-        if (wave == 0) {
-            const int j = lane;
-            float dl = sm.row[0][j] + sm.row[1][j];
-            float ddd = 0.f, fs = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                dl -= sm.col[w][j];
-                ddd += sm.dd[w][j];
-            }
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                dl += sm.off[w][j] - sm.fin[w][j];
-                fs += sm.fin[w][j];
-            }
-            const float fin_total = wave_total(fs);
-            if (j == kLs - 1) {
-                float dotv = 0.f;
-#pragma unroll
-                for (int w = 0; w < 8; ++w) dotv += sm.dot[w];
-                dl += fin_total + __expf(lam_e - lam_blk0) * dotv;
-            }
-            const float da = wave_suffix_sum(dl);  // da_j = sum_{i >= j} dLam_i within the block
-            buf_st_f32(rddt, (static_cast<uint32_t>(k * kLs + j) * a.H + h) * 4u, fmaf(Ah, da, ddd));
-            const float pa = wave_total(dts[base + j] * da);
-            if (lane == 0) {
-                float ds = 0.f;
-#pragma unroll
-                for (int w = 0; w < 8; ++w) ds += sm.dd_sum[w];
-                const int64_t pi = (bh * a.nchunks + c) * nb + k;
-                a.pA[pi] = static_cast<double>(pa);
-                a.pD[pi] = static_cast<double>(ds);
-            }
-        }
     }
+    // the last head's combine (its partials were published by the final S4 barrier)
+    if (wave == 0) combine(h0 + hpg - 1, (hpg - 1) & 1);
 
     // sum_h K applied once: dC^T[n][i] += sum_j B[j][n] K[i][j]; dB^T[n][j] += sum_i C[i][n] K[i][j]
     refresh_lane();
