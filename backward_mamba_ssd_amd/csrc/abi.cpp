@@ -77,7 +77,7 @@ bool mfma_fwd_path(const ssm_dims *d, ssm_dtype t) {
 
 bool mfma_bwd_path(const ssm_dims *d, ssm_dtype t) {
 #ifdef SSM_WITH_MFMA_BWD
-    return mfma_shape(d, t) && d->chunk <= 256;
+    return mfma_shape(d, t) && d->chunk <= 256 && d->nheads / d->ngroups <= 64;
 #else
     (void)d;
     (void)t;

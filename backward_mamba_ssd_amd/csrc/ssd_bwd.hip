@@ -219,6 +219,19 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         pr_col = (tid & 7) * 8;
     };
     refresh_lane();
+    // A and D of the group's heads, lane l holding head h0 + l; a head's value is read
+    // with readlane (a scalar, no memory wait).  Loads through the kernel's pointers would
+    // be vector loads whose waits also drain every row and state load in flight.
+    const int h0 = g * hpg;
+    const float A_lane = (lane < hpg) ? a.A[h0 + lane] : 0.f;
+    const float D_lane = (lane < hpg) ? a.D[h0 + lane] : 0.f;
+    // (the host sends groups of at most 64 heads here)
+    auto head_A = [&](int hh) -> float {
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(A_lane), hh));
+    };
+    auto head_D = [&](int hh) -> float {
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(D_lane), hh));
+    };
     constexpr int PN = kP * kN;
     const bf16_t *x = static_cast<const bf16_t *>(a.x);
     const bf16_t *dy = static_cast<const bf16_t *>(a.dy);
@@ -280,7 +293,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     };
     // chunk-local cumulative log-retention of head h (wave 0; lane = 4 tokens)
     auto scan = [&](int h, int par) {
-        const float Ah = a.A[h];
+        const float Ah = head_A(h - h0);
         const float v0 = dtr[0] * Ah, v1 = v0 + dtr[1] * Ah, v2 = v1 + dtr[2] * Ah, v3 = v2 + dtr[3] * Ah;
         const float off = wave_prefix_sum(v3) - v3;
         sm.lam[par][4 * lane + 0] = off + v0;
@@ -291,6 +304,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         for (int e = 0; e < 4; ++e) sm.dt[par][4 * lane + e] = dtr[e];
     };
     // states in accumulators, [n][p]: n-tile = wave, p-tiles 0..3
+    // raw chunk-boundary state and chunk-exit gradient of the next head, loaded a full
+    // head ahead of their use in S3
     f32x4 Hs[4], dHs[4];
     auto load_states = [&](int h) {
         const int64_t bh = static_cast<int64_t>(b) * a.H + h;
@@ -306,7 +321,6 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         }
     };
 
-    const int h0 = g * hpg;
     prefetch(h0);
     prefetch_dt(h0);
     load_states(h0);
@@ -379,7 +393,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             dl += fin_total + __expf(le - lb0) * dotv;
         }
         const float da = wave_suffix_sum(dl);  // da_j = sum_{i >= j} dLam_i within the block
-        buf_st_f32(rddt, (static_cast<uint32_t>(k * kLs + j) * a.H + hc) * 4u, fmaf(a.A[hc], da, ddd));
+        buf_st_f32(rddt, (static_cast<uint32_t>(k * kLs + j) * a.H + hc) * 4u, fmaf(head_A(hc - h0), da, ddd));
         const float pa = wave_total(dtc[base + j] * da);
         if (lane == 0) {
             float ds = 0.f;
@@ -395,7 +409,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         refresh_lane();
         const int h = h0 + hh, par = hh & 1;
         const int64_t bh = static_cast<int64_t>(b) * a.H + h;
-        const float Ah = a.A[h], Dh = a.D[h];
+        const float Ah = head_A(hh), Dh = head_D(hh);
         const float *lam = sm.lam[par], *dts = sm.dt[par];
         const float lam_blk0 = kS >= 0 ? lam[kS] : 0.f;  // block-local Lam_i = lam[base+i] - lam_blk0
         const float lam_e = lam[kE];
@@ -426,16 +440,11 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
         // Each A fragment (16 state rows n of one block's B or C) is read once and used
         // for all four p-tiles.
+        // The sums start from zero; the decayed chunk-boundary terms are added in S3.
+        f32x4 aH[4], adH[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) aH[q] = adH[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
-            const float es = __expf(lam_blk0);
-            const float ee = __expf(lam[kEnd] - lam_e);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    Hs[q][v] *= es;
-                    dHs[q][v] *= ee;
-                }
             const int n0 = 16 * wave;
 #pragma unroll
             for (int kb = 0; kb < kMaxBlk - 1; ++kb) {  // H_k = e H_c + sum over earlier blocks
@@ -446,7 +455,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 for (int kk = 0; kk < 2; ++kk) {
                     const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) Hs[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), Hs[q]);
+                    for (int q = 0; q < 4; ++q) aH[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), aH[q]);
                 }
             }
 #pragma unroll
@@ -458,7 +467,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 for (int kk = 0; kk < 2; ++kk) {
                     const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) dHs[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), dHs[q]);
+                    for (int q = 0; q < 4; ++q) adH[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), adH[q]);
                 }
             }
         }
@@ -510,14 +519,21 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         // ---- S3: block-entry state and exit gradient in bf16, [p][n] ----
         bf16_t *Hb = sm.R, *dHb = sm.R + kT128;
         {
+            const float es = __expf(lam_blk0);           // chunk start -> block k start
+            const float ee = __expf(lam[kEnd] - lam_e);  // block k end -> chunk end
             float dotp = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int n = 16 * wave + lq, p = 16 * q + lr;
-                *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(Hs[q][0], Hs[q][1], Hs[q][2], Hs[q][3]);
-                *reinterpret_cast<u16x4 *>(&dHb[p * kS128 + n]) = pack4(dHs[q][0], dHs[q][1], dHs[q][2], dHs[q][3]);
+                f32x4 hv, gv;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) dotp = fmaf(Hs[q][v], dHs[q][v], dotp);
+                for (int v = 0; v < 4; ++v) {
+                    hv[v] = fmaf(es, Hs[q][v], aH[q][v]);
+                    gv[v] = fmaf(ee, dHs[q][v], adH[q][v]);
+                    dotp = fmaf(hv[v], gv[v], dotp);
+                }
+                *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(hv[0], hv[1], hv[2], hv[3]);
+                *reinterpret_cast<u16x4 *>(&dHb[p * kS128 + n]) = pack4(gv[0], gv[1], gv[2], gv[3]);
             }
             dotp = wave_total(dotp);
             if (lane == 0) sm.dot[wave] = dotp;
