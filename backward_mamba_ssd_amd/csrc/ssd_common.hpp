@@ -68,6 +68,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ u16x8 buf_ld_16b(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ u16x4 buf_ld_8b(rsrc_t r, uint32_t off) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(u16x4, __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0)));
+}
 __device__ __forceinline__ float buf_ld_f32(rsrc_t r, uint32_t off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }

@@ -15,7 +15,8 @@
 //   H'   = exp(Lam_63) H + sum_j [exp(Lam_63 - Lam_j) dt_j] x_j B_j^T
 // Every exponent is <= 0, so no factor exceeds 1.  The three products
 //   G^T = B C^T (Gram of the group's B and C, causal half, masked and decayed),
-//   Y^T = H C^T (scaled by exp(Lam)) + X^T Gm^T,
+//   Y^T = H C^T (scaled by exp(Lam)) + X^T Gm^T, with D added to the diagonal of
+//         Gm so the same product carries the skip term D x,
 //   H'^T = exp(Lam_63) H^T + Bs^T X   (Bs = B scaled per token)
 // run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the state lives in
 // the accumulators of the workgroup for the whole sequence (the inter-block
@@ -82,24 +83,30 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
     const int bt0 = map128_tok(tid), bn0 = map128_col(tid);  // B, C: 4 tokens x 8 coords
     u16x8 xr[2], br[4], cr[4];
     float dtr = 0.f;
-    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    // Per-block buffer descriptors: offsets at or past the block's valid tokens read
+    // zero (loads) or are dropped (stores); byte offsets stay 32-bit at any T.
+    const uint32_t tokx = static_cast<uint32_t>(a.H) * kP * 2;   // bytes between tokens of x, y
+    const uint32_t tokbc = static_cast<uint32_t>(a.G) * kN * 2;  // ... of B, C
+    auto nvalid_of = [&](int64_t t0) { return static_cast<uint32_t>(T - t0 < kLs ? T - t0 : kLs); };
+    auto rows_x = [&](const bf16_t *base, int64_t t0) {
+        return make_rsrc(base + ((b * T + t0) * a.H + h) * kP, nvalid_of(t0) * tokx);
+    };
+    auto rows_bc = [&](const bf16_t *base, int64_t t0) {
+        return make_rsrc(base + ((b * T + t0) * a.G + g) * kN, nvalid_of(t0) * tokbc);
+    };
 
     auto prefetch = [&](int64_t t0) {
+        const rsrc_t rx = rows_x(x, t0), rb = rows_bc(Bm, t0), rc = rows_bc(Cm, t0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t t = t0 + xt0 + i;
-            xr[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(x + ((b * T + t) * a.H + h) * kP + xp0) : z8;
-        }
+        for (int i = 0; i < 2; ++i) xr[i] = buf_ld_16b(rx, (xt0 + i) * tokx + xp0 * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t t = t0 + bt0 + i;
-            const int64_t off = ((b * T + t) * a.G + g) * kN + bn0;
-            br[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(Bm + off) : z8;
-            cr[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(Cm + off) : z8;
+            br[i] = buf_ld_16b(rb, (bt0 + i) * tokbc + bn0 * 2);
+            cr[i] = buf_ld_16b(rc, (bt0 + i) * tokbc + bn0 * 2);
         }
         if (tid < kLs) {
-            const int64_t t = t0 + tid;
-            dtr = (t < T) ? a.dt[(b * T + t) * a.H + h] : 0.f;
+            const rsrc_t rd = make_rsrc(a.dt + (b * T + t0) * a.H + h, nvalid_of(t0) * a.H * 4u);
+            dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
         }
     };
 
@@ -166,6 +173,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
                     for (int v = 0; v < 4; ++v) {
                         const int j = 16 * jt + lq + v;
                         gv[v] = (j <= i) ? acc[v] * __expf(lam_i - lam[j]) * dts[j] : 0.f;
+                        if (j == i) gv[v] += Dh;  // skip term: Y = (Gm + D I) X
                     }
                 }
                 *reinterpret_cast<u16x4 *>(&sm.Gm[i * kS64 + 16 * jt + lq]) = pack4(gv[0], gv[1], gv[2], gv[3]);
@@ -182,6 +190,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         __syncthreads();
         // (5) outputs: Y^T rows p in [16w, 16w+16), 16 tokens at a time
         {
+            const rsrc_t ry = rows_x(y, t0);
             const int prow = 16 * wave + lr;
             for (int tt = 0; tt < 4; ++tt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -196,14 +205,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
                 for (int kk = 0; kk <= tt / 2; ++kk)
                     acc = mma16(&sm.XT[prow * kS64 + 32 * kk + lk],
                                 &sm.Gm[(16 * tt + lr) * kS64 + 32 * kk + lk], acc);
-                const int64_t t = t0 + tok;
-                if (t < T) {
-                    const int64_t off = ((b * T + t) * a.H + h) * kP + 16 * wave + lq;
-                    const u16x4 xv = *reinterpret_cast<const u16x4 *>(x + off);
-                    *reinterpret_cast<u16x4 *>(y + off) =
-                        pack4(fmaf(Dh, bf16_to_f32(xv[0]), acc[0]), fmaf(Dh, bf16_to_f32(xv[1]), acc[1]),
-                              fmaf(Dh, bf16_to_f32(xv[2]), acc[2]), fmaf(Dh, bf16_to_f32(xv[3]), acc[3]));
-                }
+                buf_st_8b(ry, tok * tokx + (16 * wave + lq) * 2, pack4(acc[0], acc[1], acc[2], acc[3]));
             }
         }
         // (6) state update H^T = exp(Lam_63) H^T + Bs^T X
