@@ -663,20 +663,33 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 // ===========================================================================
 // 3. dA, dD: fixed-order fp64 sums over batch, chunks and blocks
 // ===========================================================================
-__global__ void ssd_bwd_params_kernel(SsdBwdArgs a) {
-    const int h = blockIdx.x * blockDim.x + threadIdx.x;
-    if (h >= a.H) return;
+// One 64-lane workgroup per head: lane l sums partials l, l+64, ... of the head's
+// (batch, block) list in order, then lane 0 adds the 64 lane sums in lane order
+// (a fixed order, so dA and dD do not depend on scheduling).
+__global__ void __launch_bounds__(64) ssd_bwd_params_kernel(SsdBwdArgs a) {
+    __shared__ double red[2][64];
+    const int h = blockIdx.x, lane = threadIdx.x;
     const int64_t per = a.nchunks * (a.L / kLs);
+    const int64_t total = a.Bsz * per;
     double sa = 0.0, sd = 0.0;
-    for (int64_t b = 0; b < a.Bsz; ++b) {
-        const int64_t base = (b * a.H + h) * per;
-        for (int64_t i = 0; i < per; ++i) {
-            sa += a.pA[base + i];
-            sd += a.pD[base + i];
-        }
+    for (int64_t i = lane; i < total; i += 64) {
+        const int64_t bidx = i / per, k = i % per;
+        const int64_t o = (bidx * a.H + h) * per + k;
+        sa += a.pA[o];
+        sd += a.pD[o];
     }
-    a.dA[h] = static_cast<float>(sa);
-    a.dD[h] = static_cast<float>(sd);
+    red[0][lane] = sa;
+    red[1][lane] = sd;
+    __syncthreads();
+    if (lane == 0) {
+        double ta = 0.0, td = 0.0;
+        for (int l = 0; l < 64; ++l) {
+            ta += red[0][l];
+            td += red[1][l];
+        }
+        a.dA[h] = static_cast<float>(ta);
+        a.dD[h] = static_cast<float>(td);
+    }
 }
 
 }  // namespace
@@ -697,7 +710,7 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.ev_end != nullptr && (e = hipEventRecord(a.ev_end, s)) != hipSuccess) return e;
-    ssd_bwd_params_kernel<<<static_cast<unsigned>((a.H + 255) / 256), 256, 0, s>>>(a);
+    ssd_bwd_params_kernel<<<static_cast<unsigned>(a.H), 64, 0, s>>>(a);
     return hipGetLastError();
 }
 
