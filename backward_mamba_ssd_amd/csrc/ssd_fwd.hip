@@ -157,18 +157,22 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         if (s + 1 < nblk) prefetch(t0 + kLs);
         __syncthreads();
 
-        // (3) masked, decayed Gram rows of this wave: i in [16w, 16w+16)
+        // (3) masked, decayed Gram rows of this wave: i in [16w, 16w+16); the wave's C
+        //     fragments are read once for the four j-tiles
         {
             const int i = 16 * wave + lr;
             const float lam_i = lam[i];
+            bf16x8 fc[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) fc[kk] = frag_row(&sm.C[i * kS128 + 32 * kk + lk]);
+#pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
                 float gv[4] = {0.f, 0.f, 0.f, 0.f};
                 if (jt <= wave) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        acc = mma16(&sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk],
-                                    &sm.C[i * kS128 + 32 * kk + lk], acc);
+                        acc = mfma(frag_row(&sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk]), fc[kk], acc);
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int j = 16 * jt + lq + v;
@@ -188,23 +192,29 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
             *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(H[q][0], H[q][1], H[q][2], H[q][3]);
         }
         __syncthreads();
-        // (5) outputs: Y^T rows p in [16w, 16w+16), 16 tokens at a time
+        // (5) outputs: Y^T rows p in [16w, 16w+16), 16 tokens at a time; the wave's
+        //     H and X^T fragments are read once for the four token tiles
         {
             const rsrc_t ry = rows_x(y, t0);
             const int prow = 16 * wave + lr;
+            bf16x8 fh[4], fx[2];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) fh[kk] = frag_row(&Hb[prow * kS128 + 32 * kk + lk]);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) fx[kk] = frag_row(&sm.XT[prow * kS64 + 32 * kk + lk]);
+#pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    acc = mma16(&Hb[prow * kS128 + 32 * kk + lk],
-                                &sm.C[(16 * tt + lr) * kS128 + 32 * kk + lk], acc);
+                    acc = mfma(fh[kk], frag_row(&sm.C[(16 * tt + lr) * kS128 + 32 * kk + lk]), acc);
                 const int tok = 16 * tt + lr;
                 const float el = __expf(lam[tok]);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[v] *= el;
+#pragma unroll
                 for (int kk = 0; kk <= tt / 2; ++kk)
-                    acc = mma16(&sm.XT[prow * kS64 + 32 * kk + lk],
-                                &sm.Gm[(16 * tt + lr) * kS64 + 32 * kk + lk], acc);
+                    acc = mfma(fx[kk], frag_row(&sm.Gm[(16 * tt + lr) * kS64 + 32 * kk + lk]), acc);
                 buf_st_8b(ry, tok * tokx + (16 * wave + lq) * 2, pack4(acc[0], acc[1], acc[2], acc[3]));
             }
         }
