@@ -52,7 +52,7 @@ struct DstSmem {
     float lam[2][kLs];
 };
 
-__global__ void __launch_bounds__(256) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
     __shared__ DstSmem sm;
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
@@ -80,21 +80,19 @@ __global__ void __launch_bounds__(256) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
     const int ct0 = map128_tok(tid), cn0 = map128_col(tid);  // C: 4 tokens x 8 coords
     u16x8 yr[2], cr[4];
     float dtr = 0.f;
-    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    // per-block buffer descriptors: rows at or past the end of the sequence read zero
+    const uint32_t toky = static_cast<uint32_t>(a.H) * kP * 2, tokc = static_cast<uint32_t>(a.G) * kN * 2;
     auto prefetch = [&](int64_t t0) {
+        const uint32_t nv = static_cast<uint32_t>(T - t0 < kLs ? T - t0 : kLs);
+        const rsrc_t ry = make_rsrc(dy + ((b * T + t0) * a.H + h) * kP, nv * toky);
+        const rsrc_t rc = make_rsrc(Cm + ((b * T + t0) * a.G + g) * kN, nv * tokc);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t t = t0 + yt0 + i;
-            yr[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(dy + ((b * T + t) * a.H + h) * kP + yp0) : z8;
-        }
+        for (int i = 0; i < 2; ++i) yr[i] = buf_ld_16b(ry, (yt0 + i) * toky + yp0 * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t t = t0 + ct0 + i;
-            cr[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(Cm + ((b * T + t) * a.G + g) * kN + cn0) : z8;
-        }
+        for (int i = 0; i < 4; ++i) cr[i] = buf_ld_16b(rc, (ct0 + i) * tokc + cn0 * 2);
         if (tid < kLs) {
-            const int64_t t = t0 + tid;
-            dtr = (t < T) ? a.dt[(b * T + t) * a.H + h] : 0.f;
+            const rsrc_t rd = make_rsrc(a.dt + (b * T + t0) * a.H + h, nv * a.H * 4u);
+            dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
         }
     };
     const int64_t nblk = (T + kLs - 1) / kLs;
