@@ -52,7 +52,7 @@ struct DstSmem {
     float lam[2][kLs];
 };
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
     __shared__ DstSmem sm;
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
@@ -78,26 +78,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
     }
     const int yt0 = map64_tok(tid), yp0 = map64_col(tid);    // dy: 2 tokens x 8 channels
     const int ct0 = map128_tok(tid), cn0 = map128_col(tid);  // C: 4 tokens x 8 coords
-    u16x8 yr[2], cr[4];
-    float dtr = 0.f;
+    // A block's rows in registers, loaded two blocks ahead: the loop is unrolled by two
+    // so the two register sets alternate without copies (a copy of a loaded register
+    // would wait for the load).
+    struct Rows {
+        u16x8 yr[2], cr[4];
+        float dtr;
+    };
     // per-block buffer descriptors: rows at or past the end of the sequence read zero
     const uint32_t toky = static_cast<uint32_t>(a.H) * kP * 2, tokc = static_cast<uint32_t>(a.G) * kN * 2;
-    auto prefetch = [&](int64_t t0) {
+    auto prefetch = [&](Rows &R, int64_t t0) {
         const uint32_t nv = static_cast<uint32_t>(T - t0 < kLs ? T - t0 : kLs);
         const rsrc_t ry = make_rsrc(dy + ((b * T + t0) * a.H + h) * kP, nv * toky);
         const rsrc_t rc = make_rsrc(Cm + ((b * T + t0) * a.G + g) * kN, nv * tokc);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) yr[i] = buf_ld_16b(ry, (yt0 + i) * toky + yp0 * 2);
+        for (int i = 0; i < 2; ++i) R.yr[i] = buf_ld_16b(ry, (yt0 + i) * toky + yp0 * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cr[i] = buf_ld_16b(rc, (ct0 + i) * tokc + cn0 * 2);
+        for (int i = 0; i < 4; ++i) R.cr[i] = buf_ld_16b(rc, (ct0 + i) * tokc + cn0 * 2);
+        R.dtr = 0.f;
         if (tid < kLs) {
             const rsrc_t rd = make_rsrc(a.dt + (b * T + t0) * a.H + h, nv * a.H * 4u);
-            dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
+            R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
         }
     };
     const int64_t nblk = (T + kLs - 1) / kLs;
-    prefetch((nblk - 1) * kLs);
-    for (int64_t s = nblk - 1; s >= 0; --s) {
+    // one block of the reverse walk; R is refilled with block s - 2 once staged
+    auto step = [&](int64_t s, Rows &R) {
         const int64_t t0 = s * kLs;
         const int buf = static_cast<int>(s & 1);
         if (s == nblk - 1 || ((t0 + kLs) % a.L) == 0) {
@@ -109,7 +115,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
                 *reinterpret_cast<float4 *>(dst + p * kN + n) = make_float4(G[q][0], G[q][1], G[q][2], G[q][3]);
             }
         }
-        if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(dtr * Ah);
+        if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(R.dtr * Ah);
         __syncthreads();
         const float *lam = sm.lam[buf];
         const float lam_end = lam[kLs - 1];
@@ -118,15 +124,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 *reinterpret_cast<uint32_t *>(&sm.EdYT[(yp0 + e) * kS64 + yt0]) =
-                    pack2_bf16(bf16_to_f32(yr[0][e]) * e0, bf16_to_f32(yr[1][e]) * e1);
+                    pack2_bf16(bf16_to_f32(R.yr[0][e]) * e0, bf16_to_f32(R.yr[1][e]) * e1);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const u16x4 v = {cr[0][e], cr[1][e], cr[2][e], cr[3][e]};
+                const u16x4 v = {R.cr[0][e], R.cr[1][e], R.cr[2][e], R.cr[3][e]};
                 *reinterpret_cast<u16x4 *>(&sm.CT[(cn0 + e) * kS64 + ct0]) = v;
             }
         }
-        if (s > 0) prefetch(t0 - kLs);
+        if (s >= 2) prefetch(R, t0 - 2 * kLs);
         __syncthreads();
         const float el = __expf(lam_end);
 #pragma unroll
@@ -141,6 +147,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
                             &sm.EdYT[(16 * pt + lr) * kS64 + 32 * kk + lk], acc);
             G[q] = acc;
         }
+    };
+    Rows RA, RB;
+    prefetch(RA, (nblk - 1) * kLs);
+    if (nblk >= 2) prefetch(RB, (nblk - 2) * kLs);
+    for (int64_t s = nblk - 1; s >= 0; s -= 2) {
+        step(s, RA);
+        if (s >= 1) step(s - 1, RB);
     }
     if (a.dh0 != nullptr) {
 #pragma unroll
