@@ -182,14 +182,14 @@ constexpr int kMaxBlk = 4;          // blocks per chunk (chunk <= 256)
 
 constexpr int kBlkThreads = 512;  // 8 waves: w = 4*wh + wq
 
-struct BlkSmem {
+struct __align__(16) BlkSmem {
     bf16_t B[kT128];                    // block k rows of B [j][n]
     bf16_t C[kT128];                    // block k rows of C [i][n]
     bf16_t chainBC[(kMaxBlk - 1) * kT128];  // B rows of earlier blocks / C rows of later blocks
     bf16_t R[2 * kT128];                // per head: scaled x / dy rows of the other blocks,
                                         // then H and dH in bf16 ([p][n])
     bf16_t X[kT64], dY[kT64], QT[kT64]; // block k rows of x, dy; Q^T [j][i]
-    float lam[2][kMaxBlk * kLs], dt[2][kMaxBlk * kLs];  // chunk-local, by head parity
+    float2 ld[2][kMaxBlk * kLs];  // chunk-local (Lam, dt) per token, by head parity
     // row, col, dd_sum are written before the S2 barrier and read by the combine of the
     // previous head during S2, so they are double-buffered by head parity
     float row[2][2][kLs], col[2][4][kLs], dd[4][kLs], off[8][kLs], fin[8][kLs];
@@ -307,14 +307,13 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const float Ah = head_A(h - h0);
         const float v0 = dtr[0] * Ah, v1 = v0 + dtr[1] * Ah, v2 = v1 + dtr[2] * Ah, v3 = v2 + dtr[3] * Ah;
         const float off = wave_prefix_sum(v3) - v3;
-        sm.lam[par][4 * lane + 0] = off + v0;
-        sm.lam[par][4 * lane + 1] = off + v1;
-        sm.lam[par][4 * lane + 2] = off + v2;
-        sm.lam[par][4 * lane + 3] = off + v3;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.dt[par][4 * lane + e] = dtr[e];
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        f32x4v* dstp = reinterpret_cast<f32x4v *>(&sm.ld[par][4 * lane]);
+        dstp[0] = f32x4v{off + v0, dtr[0], off + v1, dtr[1]};
+        dstp[1] = f32x4v{off + v2, dtr[2], off + v3, dtr[3]};
     };
-    // states in accumulators, [n][p]: n-tile = wave, p-tiles 0..3
+    // states in accumulators, [n][p], 2 x 2 tiles per wave: q -> n-tile 2wq + q/2,
+    // p-tile 2wh + q%2
     // raw chunk-boundary state and chunk-exit gradient of the next head, loaded a full
     // head ahead of their use in S3
     f32x4 Hs[4], dHs[4];
@@ -324,7 +323,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const float *dc = a.dstates + (bh * a.nchunks + c) * PN;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int n = 16 * wave + lq, p = 16 * q + lr;
+            const int n = 16 * (2 * wq + (q >> 1)) + lq, p = 16 * (2 * wh + (q & 1)) + lr;
             const float4 u = *reinterpret_cast<const float4 *>(hc + p * kN + n);
             const float4 v = *reinterpret_cast<const float4 *>(dc + p * kN + n);
             Hs[q] = f32x4{u.x, u.y, u.z, u.w};
@@ -381,9 +380,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     // that phase's barrier, or are double-buffered by head parity).
     auto combine = [&](int hc, int pc) {
         const int j = lane;
-        const float *lamc = sm.lam[pc], *dtc = sm.dt[pc];
-        const float lb0 = kS >= 0 ? lamc[kS] : 0.f;
-        const float le = lamc[kE];
+        const float2 *ldc = sm.ld[pc];
+        const float lb0 = kS >= 0 ? ldc[kS].x : 0.f;
+        const float le = ldc[kE].x;
         float dl = sm.row[pc][0][j] + sm.row[pc][1][j];
         float ddd = 0.f, fs = 0.f;
 #pragma unroll
@@ -405,7 +404,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         }
         const float da = wave_suffix_sum(dl);  // da_j = sum_{i >= j} dLam_i within the block
         buf_st_f32(rddt, (static_cast<uint32_t>(k * kLs + j) * a.H + hc) * 4u, fmaf(head_A(hc - h0), da, ddd));
-        const float pa = wave_total(dtc[base + j] * da);
+        const float pa = wave_total(ldc[base + j].y * da);
         if (lane == 0) {
             float ds = 0.f;
 #pragma unroll
@@ -421,9 +420,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const int h = h0 + hh, par = hh & 1;
         const int64_t bh = static_cast<int64_t>(b) * a.H + h;
         const float Ah = head_A(hh), Dh = head_D(hh);
-        const float *lam = sm.lam[par], *dts = sm.dt[par];
-        const float lam_blk0 = kS >= 0 ? lam[kS] : 0.f;  // block-local Lam_i = lam[base+i] - lam_blk0
-        const float lam_e = lam[kE];
+        const float2 *ld = sm.ld[par];  // (Lam, dt) of this head's chunk
+        const float lam_blk0 = kS >= 0 ? ld[kS].x : 0.f;  // block-local Lam_i = Lam[base+i] - lam_blk0
+        const float lam_e = ld[kE].x;
         if (hh + 1 < hpg) prefetch_dt(h + 1);  // used by the next head's scan in S3
         // ---- S1: stage this head's rows (scaled for the state products) ----
 #pragma unroll
@@ -435,7 +434,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 *reinterpret_cast<u16x8 *>(&sm.dY[pr_tok * kS64 + pr_col]) = yk;
                 continue;
             }
-            const float cf = kb < k ? __expf(lam_blk0 - lam[tl]) * dts[tl] : __expf(lam[tl] - lam_e);
+            const float2 lt = ld[tl];
+            const float cf = kb < k ? __expf(lam_blk0 - lt.x) * lt.y : __expf(lt.x - lam_e);
             const int slot = kb < k ? kb : kb - 1;
             const u16x8 v = xr[kb];
             typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -455,38 +455,41 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         f32x4 aH[4], adH[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) aH[q] = adH[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // 2 x 2 register blocking: per 32-token step the wave reads two n fragments and
+        // two p fragments for four products.
         {
-            const int n0 = 16 * wave;
+            auto chain = [&](const bf16_t *bc, const bf16_t *xs, f32x4 *acc) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 fa[2], fb[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        fa[t] = frag_tr(bc, kS128, 16 * (2 * wq + t), 32 * kk, lane);
+                        fb[t] = frag_tr(xs, kS64, 16 * (2 * wh + t), 32 * kk, lane);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q] = mfma(fa[q >> 1], fb[q & 1], acc[q]);
+                }
+            };
 #pragma unroll
             for (int kb = 0; kb < kMaxBlk - 1; ++kb) {  // H_k = e H_c + sum over earlier blocks
                 if (kb >= k) break;
-                const bf16_t *bc = sm.chainBC + kb * kT128;
-                const bf16_t *xs = sm.R + kb * kT64;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) aH[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), aH[q]);
-                }
+                chain(sm.chainBC + kb * kT128, sm.R + kb * kT64, aH);
             }
 #pragma unroll
             for (int sl = 0; sl < kMaxBlk - 1; ++sl) {  // dH_{k+1} = e dH_c + sum over later blocks (slot sl = block sl+1)
                 if (sl < k || sl + 1 >= nbc) continue;
-                const bf16_t *bc = sm.chainBC + sl * kT128;
-                const bf16_t *xs = sm.R + sl * kT64;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 fa = frag_tr(bc, kS128, n0, 32 * kk, lane);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) adH[q] = mfma(fa, frag_tr(xs, kS64, 16 * q, 32 * kk, lane), adH[q]);
-                }
+                chain(sm.chainBC + sl * kT128, sm.R + sl * kT64, adH);
             }
         }
         // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile wq, j-tiles 2wh, 2wh+1)
         {
             float lam_i[4], rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
+            bf16x8 fY[2];  // dY rows of the wave's i-tile, shared by both j-tiles
 #pragma unroll
-            for (int v = 0; v < 4; ++v) lam_i[v] = lam[base + 16 * wq + lq + v];
+            for (int kk = 0; kk < 2; ++kk) fY[kk] = frag_row(&sm.dY[(16 * wq + lr) * kS64 + 32 * kk + lk]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) lam_i[v] = ld[base + 16 * wq + lq + v].x;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int jt = 2 * wh + q, j = 16 * jt + lr;
@@ -494,14 +497,14 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 f32x4 dW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    dW = mma16(&sm.dY[(16 * wq + lr) * kS64 + 32 * kk + lk],
-                               &sm.X[(16 * jt + lr) * kS64 + 32 * kk + lk], dW);
+                    dW = mfma(fY[kk], frag_row(&sm.X[(16 * jt + lr) * kS64 + 32 * kk + lk]), dW);
                 if (jt == wq) {  // diagonal tile: dW[i][i] = dy_i . x_i feeds dD
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         if (lq + v == lr) diag += dW[v];
                 }
-                const float lam_j = lam[base + j], dt_j = dts[base + j];
+                const float2 lj = ld[base + j];
+                const float lam_j = lj.x, dt_j = lj.y;
                 float qv[4], colacc = 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -531,11 +534,11 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         bf16_t *Hb = sm.R, *dHb = sm.R + kT128;
         {
             const float es = __expf(lam_blk0);           // chunk start -> block k start
-            const float ee = __expf(lam[kEnd] - lam_e);  // block k end -> chunk end
+            const float ee = __expf(ld[kEnd].x - lam_e);  // block k end -> chunk end
             float dotp = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = 16 * wave + lq, p = 16 * q + lr;
+                const int n = 16 * (2 * wq + (q >> 1)) + lq, p = 16 * (2 * wh + (q & 1)) + lr;
                 f32x4 hv, gv;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -582,7 +585,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int j = 16 * (2 * wh + q) + lr;
-                const float wj = __expf(lam_e - lam[base + j]), dt_j = dts[base + j];
+                const float2 lj = ld[base + j];
+                const float wj = __expf(lam_e - lj.x), dt_j = lj.y;
                 const u16x4 x4 = *reinterpret_cast<const u16x4 *>(&sm.X[j * kS64 + 16 * wq + lq]);
                 const u16x4 y4 = *reinterpret_cast<const u16x4 *>(&sm.dY[j * kS64 + 16 * wq + lq]);
                 float ddp = 0.f, dxv[4];
@@ -616,8 +620,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     ac = mfma(fH[kk], frag_row(&sm.dY[(16 * tt + lr) * kS64 + 32 * kk + lk]), ac);
                     ab = mfma(fdH[kk], frag_row(&sm.X[(16 * tt + lr) * kS64 + 32 * kk + lk]), ab);
                 }
-                const float ei = __expf(lam[base + i] - lam_blk0);
-                const float wdt = __expf(lam_e - lam[base + i]) * dts[base + i];
+                const float2 li = ld[base + i];
+                const float ei = __expf(li.x - lam_blk0);
+                const float wdt = __expf(lam_e - li.x) * li.y;
                 // the token's scale (ei, wdt) is fused into the accumulate and applied to
                 // the dot products once after their reduction
                 float o = 0.f, f = 0.f;
