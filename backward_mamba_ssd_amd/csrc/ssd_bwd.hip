@@ -192,7 +192,9 @@ struct __align__(16) BlkSmem {
     float2 ld[2][kMaxBlk * kLs];  // chunk-local (Lam, dt) per token, by head parity
     // row, col, dd_sum are written before the S2 barrier and read by the combine of the
     // previous head during S2, so they are double-buffered by head parity
-    float row[2][2][kLs], col[2][4][kLs], dd[4][kLs], off[8][kLs], fin[8][kLs];
+    // (token-major, so the combine reads each token's partials with a few wide loads)
+    float row[2][2][kLs], col[2][kLs][4], dd[kLs][4];  // row: [wh][token], 4 tokens per write
+    float2 offin[kLs][8];  // (dy.(H C), x.(dH B)) partials per token and n-tile wave
     float dot[8], dd_sum[2][8];
 };
 static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the state tiles");
@@ -383,17 +385,22 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const float2 *ldc = sm.ld[pc];
         const float lb0 = kS >= 0 ? ldc[kS].x : 0.f;
         const float le = ldc[kE].x;
-        float dl = sm.row[pc][0][j] + sm.row[pc][1][j];
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        const float2 rw = make_float2(sm.row[pc][0][j], sm.row[pc][1][j]);
+        const f32x4v cl = *reinterpret_cast<const f32x4v *>(sm.col[pc][j]);
+        const f32x4v dv = *reinterpret_cast<const f32x4v *>(sm.dd[j]);
+        float dl = rw.x + rw.y;
         float ddd = 0.f, fs = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            dl -= sm.col[pc][w][j];
-            ddd += sm.dd[w][j];
+            dl -= cl[w];
+            ddd += dv[w];
         }
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
-            dl += sm.off[w][j] - sm.fin[w][j];
-            fs += sm.fin[w][j];
+            const float2 of = sm.offin[j][w];
+            dl += of.x - of.y;
+            fs += of.y;
         }
         const float fin_total = wave_total(fs);
         if (j == kLs - 1) {
@@ -519,12 +526,14 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 }
                 *reinterpret_cast<u16x4 *>(&sm.QT[j * kS64 + 16 * wq + lq]) = pack4(qv[0], qv[1], qv[2], qv[3]);
                 colacc = rows4_sum(colacc);
-                if (lane < 16) sm.col[par][wq][j] = colacc;
+                if (lane < 16) sm.col[par][j][wq] = colacc;
             }
+            {
+                typedef float f32x4v __attribute__((ext_vector_type(4)));
+                f32x4v r;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float r = row16_sum(rowacc[v]);
-                if (lr == 0) sm.row[par][wh][16 * wq + lq + v] = r;
+                for (int v = 0; v < 4; ++v) r[v] = row16_sum(rowacc[v]);
+                if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][wh][16 * wq + lq]) = r;
             }
             diag = wave_total(diag);
             if (lane == 0) sm.dd_sum[par][wave] = diag;
@@ -599,7 +608,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 buf_st_8b(rdx, static_cast<uint32_t>(k * kLs + j) * tokb + (h * kP + 16 * wq + lq) * 2,
                           pack4(dxv[0], dxv[1], dxv[2], dxv[3]));
                 ddp = rows4_sum(ddp);
-                if (lane < 16) sm.dd[wq][j] = ddp;
+                if (lane < 16) sm.dd[j][wq] = ddp;
             }
         }
         // Phase III / IV: per-head dC, dB contributions (n-tile = wave, tok-tiles 0..3);
@@ -635,10 +644,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 }
                 o = rows4_sum(o) * ei;
                 f = rows4_sum(f) * wdt;
-                if (lane < 16) {
-                    sm.off[wave][i] = o;
-                    sm.fin[wave][i] = f;
-                }
+                if (lane < 16) sm.offin[i][wave] = make_float2(o, f);
             }
         }
         __syncthreads();
