@@ -36,14 +36,13 @@
 namespace ssm {
 namespace {
 
-struct FwdSmem {
+struct __align__(16) FwdSmem {
     bf16_t C[kLs * kS128];    // [tok][n]
     bf16_t B[kLs * kS128];    // [tok][n]; after the Gram product: H in bf16, [p][n]
     bf16_t BsT[kN * kS64];    // [n][tok] = B[tok][n] * exp(Lam_63 - Lam_tok) * dt_tok
     bf16_t XT[kP * kS64];     // [p][tok]
     bf16_t Gm[kLs * kS64];    // [i][j] = (C_i.B_j) exp(Lam_i - Lam_j) dt_j for j <= i, else 0
-    float lam[2][kLs];        // double-buffered by block parity
-    float dt[2][kLs];
+    float2 ld[2][kLs];        // (Lam, dt) per token, double-buffered by block parity
 };
 
 __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
@@ -117,13 +116,11 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         const int buf = static_cast<int>(s & 1);
         // (1) cumulative log-retention of the block (one wave, one token per lane)
         if (wave == 0) {
-            sm.lam[buf][lane] = wave_prefix_sum(dtr * Ah);
-            sm.dt[buf][lane] = dtr;
+            sm.ld[buf][lane] = make_float2(wave_prefix_sum(dtr * Ah), dtr);
         }
         __syncthreads();
-        const float *lam = sm.lam[buf];
-        const float *dts = sm.dt[buf];
-        const float lam_end = lam[kLs - 1];
+        const float2 *ld = sm.ld[buf];
+        const float lam_end = ld[kLs - 1].x;
         // (2) stage the block in LDS
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -132,8 +129,12 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         }
         {
             float coef[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) coef[i] = __expf(lam_end - lam[bt0 + i]) * dts[bt0 + i];
+            const float4 l01 = *reinterpret_cast<const float4 *>(&ld[bt0]);      // (Lam, dt) of 2 tokens
+            const float4 l23 = *reinterpret_cast<const float4 *>(&ld[bt0 + 2]);
+            coef[0] = __expf(lam_end - l01.x) * l01.y;
+            coef[1] = __expf(lam_end - l01.z) * l01.w;
+            coef[2] = __expf(lam_end - l23.x) * l23.y;
+            coef[3] = __expf(lam_end - l23.z) * l23.w;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 *reinterpret_cast<u16x4 *>(&sm.BsT[(bn0 + e) * kS64 + bt0]) =
@@ -161,7 +162,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         //     fragments are read once for the four j-tiles
         {
             const int i = 16 * wave + lr;
-            const float lam_i = lam[i];
+            const float lam_i = ld[i].x;
             bf16x8 fc[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) fc[kk] = frag_row(&sm.C[i * kS128 + 32 * kk + lk]);
@@ -173,10 +174,15 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
                         acc = mfma(frag_row(&sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk]), fc[kk], acc);
+                    const float4 l01 = *reinterpret_cast<const float4 *>(&ld[16 * jt + lq]);
+                    const float4 l23 = *reinterpret_cast<const float4 *>(&ld[16 * jt + lq + 2]);
+                    const float2 ljs[4] = {make_float2(l01.x, l01.y), make_float2(l01.z, l01.w),
+                                           make_float2(l23.x, l23.y), make_float2(l23.z, l23.w)};
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int j = 16 * jt + lq + v;
-                        gv[v] = (j <= i) ? acc[v] * __expf(lam_i - lam[j]) * dts[j] : 0.f;
+                        const float2 lj = ljs[v];
+                        gv[v] = (j <= i) ? acc[v] * __expf(lam_i - lj.x) * lj.y : 0.f;
                         if (j == i) gv[v] += Dh;  // skip term: Y = (Gm + D I) X
                     }
                 }
@@ -209,7 +215,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
                 for (int kk = 0; kk < 4; ++kk)
                     acc = mfma(fh[kk], frag_row(&sm.C[(16 * tt + lr) * kS128 + 32 * kk + lk]), acc);
                 const int tok = 16 * tt + lr;
-                const float el = __expf(lam[tok]);
+                const float el = __expf(ld[tok].x);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[v] *= el;
 #pragma unroll
