@@ -228,16 +228,19 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         {
             const float el = __expf(lam_end);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int nt = 2 * wave + q / 4, pt = q % 4;
-                f32x4 acc = H[q];
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] *= el;
+                for (int v = 0; v < 4; ++v) H[q][v] *= el;
+            // each of the wave's 2 Bs^T and 4 X^T fragments is read once per 32-token step
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    acc = mma16(&sm.BsT[(16 * nt + lr) * kS64 + 32 * kk + lk],
-                                &sm.XT[(16 * pt + lr) * kS64 + 32 * kk + lk], acc);
-                H[q] = acc;
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 fb[2], fx[4];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) fb[t] = frag_row(&sm.BsT[(16 * (2 * wave + t) + lr) * kS64 + 32 * kk + lk]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) fx[t] = frag_row(&sm.XT[(16 * t + lr) * kS64 + 32 * kk + lk]);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) H[q] = mfma(fb[q / 4], fx[q % 4], H[q]);
             }
         }
     }
