@@ -84,9 +84,12 @@ size_t ssm_workspace_bytes(const ssm_dims *d, ssm_dtype dtype, int which, int64_
 /* Static human-readable name of a status code. */
 const char *ssm_status_string(ssm_status s);
 
-/* 1 when the chunked MFMA kernels serve these dims and dtype (bf16 operands,
- * headdim 64, dstate 128, chunk a multiple of 64); otherwise the exact-fp32
- * sequential kernels run.  Purely informational. */
+/* 1 when the chunked MFMA kernels serve both the forward and the backward for
+ * these dims and dtype: bf16 operands, headdim 64, dstate 128, chunk a multiple
+ * of 64, and for the backward also chunk <= 256 and at most 64 heads per group.
+ * Otherwise the exact-fp32 sequential kernels run the part the MFMA kernels do
+ * not serve (the forward alone still takes the MFMA path whenever its own
+ * conditions hold).  Purely informational. */
 int ssm_uses_mfma_path(const ssm_dims *d, ssm_dtype dtype);
 
 /*

@@ -134,3 +134,11 @@ def test_workspace_and_path_predicates():
         ssm.ssm_workspace_bytes(dims(dstate=48), ssm.SSM_BF16, ssm.SSM_WS_FWD)
     assert not ssm.ssm_uses_mfma_path(dims(headdim=8, dstate=16), ssm.SSM_F32)
     assert not ssm.ssm_uses_mfma_path(d, ssm.SSM_F32)
+    assert ssm.ssm_uses_mfma_path(d, ssm.SSM_BF16)
+    # the MFMA backward needs chunk <= 256 and at most 64 heads per group
+    assert not ssm.ssm_uses_mfma_path(dims(batch=4, seqlen=4096, nheads=256, ngroups=8, chunk=512),
+                                      ssm.SSM_BF16)
+    assert not ssm.ssm_uses_mfma_path(dims(batch=1, seqlen=256, nheads=128, ngroups=1, chunk=256),
+                                      ssm.SSM_BF16)
+    assert not ssm.ssm_uses_mfma_path(dims(batch=1, seqlen=256, nheads=8, ngroups=1, chunk=96),
+                                      ssm.SSM_BF16)

@@ -50,6 +50,21 @@ def test_backward_matches_oracle(ssm, t, L, h0, dhf):
         assert_close(k, gr[k], ref[k], 2e-2)
 
 
+@pytest.mark.parametrize("t,h,g,L", [(600, 8, 2, 512), (200, 128, 1, 128)])
+def test_shapes_outside_the_mfma_backward(ssm, t, h, g, L):
+    # chunk 512 or 128 heads in one group: the MFMA forward saves the chunk states and
+    # the exact-fp32 sequential backward takes over; same entry points, same tolerance
+    b, p, n = 1, 64, 128
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 700 + h, dev, h0="randn", dh_final=True)
+    assert not ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
+    _, _, _, gr = _run(ssm, pr, L)
+    ref = oracle.bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], pr["dy"],
+                     h0=pr["h0"], dh_final=pr["dh_final"])
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert_close(k, gr[k], ref[k], 2e-2)
+
+
 def test_backward_deterministic(ssm):
     b, t, h, p, n, g, L = 2, 300, 8, 64, 128, 2, 128
     pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 5, dev, h0="randn", dh_final=True)
