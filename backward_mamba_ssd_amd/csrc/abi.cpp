@@ -312,6 +312,29 @@ ssm_status ssm_decode_step(const ssm_dims *d, ssm_dtype dtype, float *state, con
                : SSM_ERR_HIP;
 }
 
+ssm_status ssm_decode_step_sr16(const ssm_dims *d, ssm_dtype dtype, uint16_t *state16,
+                                const void *x, const void *B, const void *C, const float *dt,
+                                const float *A, const float *D, void *y, uint64_t seed,
+                                uint64_t step, ssm_stream stream) {
+    ssm_status st = check_dims(d, false);
+    if (st != SSM_OK) return st;
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (!serial_supported(d)) return SSM_ERR_UNSUPPORTED;
+    if (d->batch > 0 && (!state16 || !x || !B || !C || !dt || !y)) return SSM_ERR_NULL;
+    if (!A || !D) return SSM_ERR_NULL;
+    if (!aligned(state16, 8)) return SSM_ERR_ALIGN;  // four binary16 per lane
+    if (!check_align({}, {B, C}, {x, y}, {dt, A, D}, dtype, false)) return SSM_ERR_ALIGN;
+    if (d->batch == 0) return SSM_OK;
+    DecodeArgs a{};
+    a.Bsz = d->batch; a.H = static_cast<int>(d->nheads); a.P = static_cast<int>(d->headdim);
+    a.N = static_cast<int>(d->dstate); a.G = static_cast<int>(d->ngroups);
+    a.state16 = state16; a.seed = seed; a.key = step;
+    a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.D = D; a.y = y;
+    return launch_decode(a, dtype == SSM_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSM_OK
+               : SSM_ERR_HIP;
+}
+
 ssm_status ssm_checkpoint_sr16(const float *state, uint16_t *out, uint64_t n_elems,
                                uint64_t seed, uint64_t ckpt_index, uint64_t elem_offset,
                                ssm_stream stream) {

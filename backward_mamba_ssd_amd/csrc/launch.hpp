@@ -10,7 +10,9 @@ namespace ssm {
 struct DecodeArgs {
     int64_t Bsz;
     int H, P, N, G;
-    float *state;
+    float *state;         // float state, or nullptr when state16 is used
+    uint16_t *state16;    // binary16 state cache (stochastically rounded on store)
+    uint64_t seed, key;   // SR entropy key of this step (state16 only)
     const void *x, *B, *C;
     const float *dt, *A, *D;
     void *y;
@@ -79,7 +81,7 @@ struct SsdBwdArgs {
 
 hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);  // state or state16
 hipError_t launch_scan(const ScanArgs &a, bool bf16, bool ckpt_f16, hipStream_t s);
 hipError_t launch_drift_reduce(const float *pm, const float *ps, int64_t nwaves, int64_t r,
                                double inv_count, float *dmax, float *dmean, hipStream_t s);

@@ -20,6 +20,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "sr16.hpp"
 
 namespace ssm {
 
@@ -60,9 +61,13 @@ __device__ __forceinline__ float4 scale4(const float4 &v, float s) {
 
 // ---------------------------------------------------------------------------
 // Decode: one (batch, head) per workgroup, MAXR row passes unrolled so all
-// state loads are in flight before the arithmetic.
+// state loads are in flight before the arithmetic.  With SR16 the state lives in
+// binary16: it is widened exactly, updated in float32 with the same arithmetic,
+// and stored back stochastically rounded ("Nemotron 3 Ultra: replaying a rounded
+// state": the quantized model keeps its recurrent state cache in FP16 with
+// stochastic rounding), element e of the state using entropy (seed, key, e).
 // ---------------------------------------------------------------------------
-template <int N, int MAXR, typename T>
+template <int N, int MAXR, typename T, bool SR16>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     constexpr int LPR = N / 4;
     constexpr int RPW = 256 / LPR;
@@ -74,14 +79,26 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const T *x = static_cast<const T *>(a.x);
     const T *Bm = static_cast<const T *>(a.B);
     const T *Cm = static_cast<const T *>(a.C);
-    float *st = a.state + static_cast<int64_t>(bh) * a.P * N;
+    const int64_t row_base = static_cast<int64_t>(bh) * a.P;  // state row index of p = 0
+    float *st = SR16 ? nullptr : a.state + row_base * N;
+    uint16_t *st16 = SR16 ? a.state16 + row_base * N : nullptr;
 
     float4 s[MAXR];
 #pragma unroll
     for (int i = 0; i < MAXR; ++i) {
         const int p = r0 + i * RPW;
         s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (p < a.P) s[i] = *reinterpret_cast<const float4 *>(st + static_cast<int64_t>(p) * N + n0);
+        if (p < a.P) {
+            if constexpr (SR16) {
+                // binary16 -> float32 is exact; convert the whole vector (an element-wise
+                // bit_cast of a vector subscript is not reliable here)
+                const h16x4 hv = *reinterpret_cast<const h16x4 *>(st16 + static_cast<int64_t>(p) * N + n0);
+                const f32x4 fv = __builtin_convertvector(hv, f32x4);
+                s[i] = make_float4(fv[0], fv[1], fv[2], fv[3]);
+            } else {
+                s[i] = *reinterpret_cast<const float4 *>(st + static_cast<int64_t>(p) * N + n0);
+            }
+        }
     }
     const float dtv = a.dt[bh];
     const float av = retention(dtv, a.A[h]);
@@ -89,6 +106,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const int64_t bgN = (static_cast<int64_t>(b) * a.G + g) * N + n0;
     const float4 bdt = scale4(IO<T>::ld4(Bm, bgN), dtv);
     const float4 c = IO<T>::ld4(Cm, bgN);
+    const uint64_t sub = SR16 ? sr16_stream(a.seed, a.key) : 0ull;
 #pragma unroll
     for (int i = 0; i < MAXR; ++i) {
         if (i * RPW >= a.P) break;  // uniform: no row of this pass exists
@@ -97,7 +115,17 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         float acc = row_step(s[i], av, xp, bdt, c);
         acc = row_reduce<LPR>(acc);  // whole rows are active or inactive together
         if (p < a.P) {
-            *reinterpret_cast<float4 *>(st + static_cast<int64_t>(p) * N + n0) = s[i];
+            if constexpr (SR16) {
+                const uint64_t e0 = static_cast<uint64_t>(row_base + p) * N + n0;  // element index
+                u16x4 o;
+                o[0] = sr16_bits(s[i].x, sr16_entropy(sub, e0 + 0));
+                o[1] = sr16_bits(s[i].y, sr16_entropy(sub, e0 + 1));
+                o[2] = sr16_bits(s[i].z, sr16_entropy(sub, e0 + 2));
+                o[3] = sr16_bits(s[i].w, sr16_entropy(sub, e0 + 3));
+                *reinterpret_cast<u16x4 *>(st16 + static_cast<int64_t>(p) * N + n0) = o;
+            } else {
+                *reinterpret_cast<float4 *>(st + static_cast<int64_t>(p) * N + n0) = s[i];
+            }
             if ((tid % LPR) == 0)
                 IO<T>::st(static_cast<T *>(a.y), static_cast<int64_t>(bh) * a.P + p,
                           fmaf(Dh, xp, acc));
@@ -532,22 +560,24 @@ hipError_t launch_copy(float *dst, const float *src, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool SR16>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.Bsz * a.H)), block(256);
     switch (a.N) {
-        case 16: decode_kernel<16, 8, T><<<grid, block, 0, s>>>(a); break;
-        case 32: decode_kernel<32, 8, T><<<grid, block, 0, s>>>(a); break;
-        case 64: decode_kernel<64, 8, T><<<grid, block, 0, s>>>(a); break;
-        case 128: decode_kernel<128, 8, T><<<grid, block, 0, s>>>(a); break;
-        case 256: decode_kernel<256, 8, T><<<grid, block, 0, s>>>(a); break;
+        case 16: decode_kernel<16, 8, T, SR16><<<grid, block, 0, s>>>(a); break;
+        case 32: decode_kernel<32, 8, T, SR16><<<grid, block, 0, s>>>(a); break;
+        case 64: decode_kernel<64, 8, T, SR16><<<grid, block, 0, s>>>(a); break;
+        case 128: decode_kernel<128, 8, T, SR16><<<grid, block, 0, s>>>(a); break;
+        case 256: decode_kernel<256, 8, T, SR16><<<grid, block, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s) {
-    return bf16 ? launch_decode_t<bf16_t>(a, s) : launch_decode_t<float>(a, s);
+    if (a.state16 != nullptr)
+        return bf16 ? launch_decode_t<bf16_t, true>(a, s) : launch_decode_t<float, true>(a, s);
+    return bf16 ? launch_decode_t<bf16_t, false>(a, s) : launch_decode_t<float, false>(a, s);
 }
 
 template <typename T, typename CK, bool LIVE>

@@ -21,7 +21,8 @@ SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
 SSM_WS_FWD, SSM_WS_BWD, SSM_WS_REPLAY = 0, 1, 2
 _SIZE_MAX = ctypes.c_size_t(-1).value
 
-EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_decode_step", "ssm_checkpoint_sr16",
+EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_decode_step", "ssm_decode_step_sr16",
+           "ssm_checkpoint_sr16",
            "ssm_replay", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path",
            "ssm_profile_next_bwd_block")
 
@@ -57,6 +58,8 @@ def _load():
     lib.ssm_bwd.restype = i32
     lib.ssm_decode_step.argtypes = [D, i32] + [vp] * 8 + [vp]
     lib.ssm_decode_step.restype = i32
+    lib.ssm_decode_step_sr16.argtypes = [D, i32] + [vp] * 8 + [u64, u64, vp]
+    lib.ssm_decode_step_sr16.restype = i32
     lib.ssm_checkpoint_sr16.argtypes = [vp, vp, u64, u64, u64, u64, vp]
     lib.ssm_checkpoint_sr16.restype = i32
     lib.ssm_replay.argtypes = ([D, i32, vp, i32, vp] + [vp] * 6 + [i64, i64] + [vp] * 4
@@ -209,6 +212,24 @@ def ssm_decode_step(state, x, B, C, dt, A, D, y=None, stream=None):
     st = _lib.ssm_decode_step(ctypes.byref(dims), code, _ptr(state), _ptr(x), _ptr(B), _ptr(C),
                               _ptr(dt), _ptr(A), _ptr(D), _ptr(y), _stream(stream))
     _check(st, "ssm_decode_step")
+    return y
+
+
+def ssm_decode_step_sr16(state16, x, B, C, dt, A, D, seed, step, y=None, stream=None):
+    """In-place one-token update of a binary16 state cache [b,h,p,n] (int16 tensor
+    holding the bits), stochastically rounded under (seed, step); returns y [b,h,p]."""
+    if state16.dtype not in (torch.int16, torch.float16):
+        raise TypeError("state16 holds binary16 bits (int16 or float16 tensor)")
+    b, h, p, n = state16.shape
+    g = B.shape[1]
+    dims = make_dims(b, 1, h, p, n, g, 1)
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    st = _lib.ssm_decode_step_sr16(ctypes.byref(dims), code, _ptr(state16), _ptr(x), _ptr(B),
+                                   _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(y),
+                                   seed & (2**64 - 1), int(step) & (2**64 - 1), _stream(stream))
+    _check(st, "ssm_decode_step_sr16")
     return y
 
 

@@ -346,6 +346,28 @@ def secondary(dev):
     dec["ms_per_step_48_layers"] = round(ms / steps, 4)
     dec["tokens_per_s"] = round(w.batch * steps / (ms * 1e-3), 1)
     out["decode"] = dec
+    # the same decode on a binary16 state cache, stochastically rounded on store
+    s16 = torch.stack([pr["state"][l].half().view(torch.int16) for l in range(layers)])
+    for l in range(layers):
+        ssm.ssm_decode_step_sr16(s16[l], pr["x"][0, l], pr["B"][0, l], pr["C"][0, l],
+                                 pr["dt"][0, l], pr["A"][l], pr["D"][l], 1, l, y=y[l])
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(steps):
+        for l in range(layers):
+            ssm.ssm_decode_step_sr16(s16[l], pr["x"][s, l], pr["B"][s, l], pr["C"][s, l],
+                                     pr["dt"][s, l], pr["A"][l], pr["D"][l], 1,
+                                     (s + 1) * layers + l, y=y[l])
+    e1.record()
+    torch.cuda.synchronize()
+    ms16 = e0.elapsed_time(e1)
+    per_call16 = per_call - w.batch * w.nheads * 4 * PN
+    d16 = path_entry(steps * layers * w.batch * w.nheads * 5 * PN, steps * layers * per_call16,
+                     ms16, FP32_VALU_PEAK_TFLOPS)
+    d16["ms_per_step_48_layers"] = round(ms16 / steps, 4)
+    d16["tokens_per_s"] = round(w.batch * steps / (ms16 * 1e-3), 1)
+    out["decode_sr16_state"] = d16
+    del s16
     st = pr["state"][0]
     del pr
     bits = torch.empty(st.shape, dtype=torch.int16, device=dev)

@@ -139,6 +139,25 @@ ssm_status ssm_decode_step(const ssm_dims *d, ssm_dtype dtype, float *state, con
                            const float *D, void *y, ssm_stream stream);
 
 /*
+ * One-token decode with a binary16 state cache, in place.  "Nemotron 3 Ultra:
+ * replaying a rounded state", introduction (the quantized model keeps the
+ * recurrent state cache in FP16 and stores it with stochastic rounding) and
+ * section "Counting the state and attention cache" (FP16 halves the state
+ * bytes against float32).  state16 [batch,nheads,headdim,dstate] holds binary16
+ * bits (8-byte aligned); each element is widened exactly to float32, advanced
+ * by the same arithmetic as ssm_decode_step, and stored back with the rounding
+ * rule of ssm_checkpoint_sr16 keyed by (seed, step): element i (flat index of
+ * state16) uses u = high32( SM(SM(seed, step), i) ).  y is what ssm_decode_step
+ * writes from the widened state, bit for bit.  Inputs as for ssm_decode_step;
+ * the caller passes a distinct `step` per decode step so rounding choices are
+ * independent across steps and reproducible for replay.
+ */
+ssm_status ssm_decode_step_sr16(const ssm_dims *d, ssm_dtype dtype, uint16_t *state16,
+                                const void *x, const void *B, const void *C, const float *dt,
+                                const float *A, const float *D, void *y, uint64_t seed,
+                                uint64_t step, ssm_stream stream);
+
+/*
  * FP16 stochastically rounded checkpoint of a float32 state.  "Nemotron 3
  * Ultra: replaying a rounded state", sections "Stochastic rounding and the
  * mean state" (round up when the entropy residue is below the discarded

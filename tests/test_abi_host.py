@@ -101,6 +101,13 @@ def test_decode_replay_sr16_validation():
     args = [FAKE] * 8
     assert L.ssm_decode_step(ctypes.byref(d), ssm.SSM_BF16, None, *args[1:], None) == NULL
     assert L.ssm_decode_step(ctypes.byref(dims(dstate=48)), ssm.SSM_BF16, *args, None) == UNSUP
+    sr = L.ssm_decode_step_sr16
+    assert sr(ctypes.byref(d), ssm.SSM_BF16, None, *args[1:], 0, 0, None) == NULL
+    assert sr(ctypes.byref(d), ssm.SSM_BF16, FAKE + 2, *args[1:], 0, 0, None) == ALIGN
+    assert sr(ctypes.byref(d), 7, *args, 0, 0, None) == DTYPE
+    assert sr(ctypes.byref(dims(dstate=48)), ssm.SSM_BF16, *args, 0, 0, None) == UNSUP
+    assert sr(ctypes.byref(dims(batch=0)), ssm.SSM_BF16, None, None, None, None, None, FAKE,
+              FAKE, None, 0, 0, None) == OK
     assert L.ssm_checkpoint_sr16(None, FAKE, 10, 0, 0, 0, None) == NULL
     assert L.ssm_checkpoint_sr16(FAKE, FAKE + 1, 10, 0, 0, 0, None) == ALIGN
     assert L.ssm_checkpoint_sr16(FAKE, FAKE + 16, 10, 0, 0, 0, None) == DIMS  # aliasing

@@ -55,6 +55,70 @@ def test_decode_matches_oracle(ssm, shape, dtype):
     assert_close("state", st, ref_state, 1e-5)
 
 
+def _sr16_bracket(v64, M, seed, step):
+    """SR16 bits of every float32 value within 1e-6*M of the fp64 values v64:
+    the lowest and highest (SR16 is monotone in the value for a fixed entropy
+    word), from the oracle's rounding of the two ends of that interval."""
+    d = 1e-6 * M + 1e-38
+    lo = oracle.sr16(np.float32(v64 - d), seed, step)
+    hi = oracle.sr16(np.float32(v64 + d), seed, step)
+    return lo, hi
+
+
+@pytest.mark.parametrize("shape,dtype,seed,step", [((3, 16, 64, 128, 2), "bf16", 2, 0),
+                                                   ((2, 4, 32, 64, 2), "f32", 3, 7),
+                                                   ((1, 3, 5, 32, 1), "bf16", 5, 2 ** 40 + 3)])
+def test_decode_sr16_state_cache(ssm, shape, dtype, seed, step):
+    """Decode on a binary16 state cache ("Nemotron 3 Ultra: replaying a rounded
+    state", introduction): the stored bits are the SR16 rounding, keyed by
+    (seed, step, flat element index), of the one-step update of the widened
+    state.  Checked against the oracle's fp64 step: where every float32 value
+    within 1e-6 of the fp64 one rounds to the same bits those bits must be
+    stored; elsewhere the stored value must lie between the two possible
+    roundings.  The rounding error, in units of the binary16 spacing, must
+    average to zero; y equals the float32 decode of the widened state."""
+    b, h, p, n, g = shape
+    pr = _decode_inputs(b, h, p, n, g, dtype, 100 + seed, 1)
+    s16 = inputs.draw("h0", (b, h, p, n), 100 + seed).half()
+    bits0 = s16.view(torch.int16).to(dev)
+    wide = oracle.half_bits_to_double(s16.view(torch.int16).numpy().view(np.uint16))
+    x, B, C, dt = pr["x"][0], pr["B"][0], pr["C"][0], pr["dt"][0]
+
+    bits = bits0.clone()
+    y = ssm.ssm_decode_step_sr16(bits, x, B, C, dt, pr["A"], pr["D"], seed, step)
+    st32 = s16.float().to(dev)
+    y32 = ssm.ssm_decode_step(st32, x, B, C, dt, pr["A"], pr["D"])
+    again = bits0.clone()
+    ssm.ssm_decode_step_sr16(again, x, B, C, dt, pr["A"], pr["D"], seed, step)
+    other = bits0.clone()
+    ssm.ssm_decode_step_sr16(other, x, B, C, dt, pr["A"], pr["D"], seed, step + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y32)
+    assert torch.equal(bits, again)
+
+    ref = wide.copy()
+    ry = oracle.decode_step(ref, x, B, C, dt, pr["A"], pr["D"])
+    assert_close("y", y, ry, 2e-2 if dtype == "bf16" else 1e-5)
+    got = bits.cpu().numpy().view(np.uint16)
+    M = np.abs(wide) + np.abs(to_np(x)[..., None] * to_np(B).repeat(h // g, axis=1)[:, :, None, :]
+                              * to_np(dt)[..., None, None])
+    lo, hi = _sr16_bracket(ref, M, seed, step)
+    fixed = lo == hi
+    print(f"  decided by the oracle: {fixed.mean():.4f} of {fixed.size}", flush=True)
+    assert fixed.mean() > 0.95
+    assert np.array_equal(got[fixed], lo[fixed]), int(np.sum(got[fixed] != lo[fixed]))
+    gv, lv, hv = (oracle.half_bits_to_double(a) for a in (got, lo, hi))
+    assert np.all((gv >= lv) & (gv <= hv))
+    # unbiased: the signed rounding error averages to zero in binary16 spacings
+    spacing = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -14))) - 10)
+    z = (gv - ref) / spacing
+    assert np.all(np.abs(z) <= 1.0 + 1e-3)
+    if z.size > 100000:
+        assert abs(z.mean()) < 5e-3, z.mean()
+    # a different step key changes some rounding choices
+    assert not torch.equal(bits, other)
+
+
 def _seq_problem(b, t, h, p, n, g, dtype, seed, h0="randn"):
     return inputs.make_problem(b, t, h, p, n, g, dtype, seed, dev, h0=h0, dh_final=True)
 
