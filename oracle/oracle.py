@@ -21,6 +21,10 @@ state as small examples:
 * ``replay_additive`` -- same page, section "Recovering the state by replay":
   the s' = s + u example of replaying the pending buffer from a checkpoint.
 
+``dt_prep`` / ``dt_prep_bwd`` wrap the C preparation of the time step
+(softplus of raw + bias, clamped to a closed interval) and of the per-head rate
+A = -exp(logA), with their gradients.
+
 Parity of every function here is pinned by ``tests/test_oracle_*.py`` against
 closed forms, a textbook filter (scipy.signal.lfilter), central finite
 differences, brute force, and the pages' worked values under ``tests/golden``.
@@ -76,6 +80,11 @@ def _load():
             lib.oracle_sr16.restype = None
             lib.oracle_half_to_double_array.argtypes = [vp, vp, i64]
             lib.oracle_half_to_double_array.restype = None
+            f32 = ctypes.c_float
+            lib.oracle_dt_prep.argtypes = [i64, i64, vp, vp, vp, f32, f32, vp, vp]
+            lib.oracle_dt_prep.restype = None
+            lib.oracle_dt_prep_bwd.argtypes = [i64, i64, vp, vp, vp, f32, f32, vp, vp, vp, vp, vp]
+            lib.oracle_dt_prep_bwd.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -175,6 +184,37 @@ def replay(ckpt, x, B, C, dt, A, D, t0, r):
     sl = slice(t0, t0 + r)
     return fwd(_f64(x)[:, sl], _f64(B)[:, sl], _f64(C)[:, sl], _f64(dt)[:, sl], A, D,
                h0=ckpt)
+
+
+# ----------------------------------------------------------------------------
+# time-step and rate preparation ("Nemotron Kernels...", section "From Classical
+# State Space To A Selective Mamba State"; TorchLean page, "The Mamba state update")
+# ----------------------------------------------------------------------------
+
+def dt_prep(raw, bias, logA, lo=0.0, hi=float("inf")):
+    """dt = clamp(softplus(raw + bias[h]), lo, hi) [..., H] and A = -exp(logA) [H]."""
+    raw = _f64(raw)
+    H = raw.shape[-1]
+    rows = raw.size // H if H else 0
+    dt = np.empty(raw.shape, np.float64)
+    A = np.empty(H, np.float64)
+    _load().oracle_dt_prep(rows, H, _p(raw), _p(_f64(bias)), _p(_f64(logA)), ctypes.c_float(lo),
+                           ctypes.c_float(hi), _p(dt), _p(A))
+    return dt, A
+
+
+def dt_prep_bwd(raw, bias, logA, ddt, dA, lo=0.0, hi=float("inf")):
+    """Gradients (d_raw [..., H], d_bias [H], d_logA [H]) from ddt and dA."""
+    raw = _f64(raw)
+    H = raw.shape[-1]
+    rows = raw.size // H if H else 0
+    d_raw = np.empty(raw.shape, np.float64)
+    d_bias = np.empty(H, np.float64)
+    d_logA = np.empty(H, np.float64)
+    _load().oracle_dt_prep_bwd(rows, H, _p(raw), _p(_f64(bias)), _p(_f64(logA)),
+                               ctypes.c_float(lo), ctypes.c_float(hi), _p(_f64(ddt)),
+                               _p(_f64(dA)), _p(d_raw), _p(d_bias), _p(d_logA))
+    return d_raw, d_bias, d_logA
 
 
 # ----------------------------------------------------------------------------

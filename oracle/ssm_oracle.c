@@ -375,3 +375,63 @@ double oracle_half_to_double(uint16_t hbits) {
 void oracle_half_to_double_array(const uint16_t *in, double *out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_half_to_double(in[i]);
 }
+
+/*
+ * Time-step and rate preparation, with gradients.
+ *  - "Nemotron Kernels: From Inference To Backpropagation", section "From
+ *    Classical State Space To A Selective Mamba State": the time-step stream
+ *    goes through softplus and is then clamped to a configured interval; the
+ *    local derivative is the sigmoid inside the interval and zero where the
+ *    clamp has saturated; the boundary needs a declared convention.
+ *  - "Nemotron 3 Ultra: replaying a rounded state", section "The Mamba state
+ *    update": the time step is formed from the raw time step and a per-head
+ *    bias, and the per-head rate is A = -exp(logA).
+ * Readings: the bias is added before the softplus; the interval is closed and
+ * a value equal to either end passes its gradient (the clamp is the identity
+ * there); the inside/outside decision is taken on the float32 value of the
+ * softplus, the precision the time step is stored in.  softplus is the
+ * mathematical log(1 + e^v), evaluated as max(v, 0) + log1p(e^-|v|).
+ */
+static double softplus64(double v) { return (v > 0 ? v : 0.0) + log1p(exp(-fabs(v))); }
+
+static double sigmoid64(double v) {
+    if (v >= 0) return 1.0 / (1.0 + exp(-v));
+    const double e = exp(v);
+    return e / (1.0 + e);
+}
+
+static int inside(double sp, float lo, float hi) {
+    const float s32 = (float)sp;
+    return s32 >= lo && s32 <= hi;
+}
+
+/* raw [rows][H], bias [H], logA [H] -> dt [rows][H], A [H] */
+void oracle_dt_prep(int64_t rows, int64_t H, const double *raw, const double *bias,
+                    const double *logA, float lo, float hi, double *dt, double *A) {
+    for (int64_t h = 0; h < H; ++h) A[h] = -exp(logA[h]);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t h = 0; h < H; ++h) {
+            const double sp = softplus64(raw[r * H + h] + bias[h]);
+            dt[r * H + h] = sp < lo ? (double)lo : (sp > hi ? (double)hi : sp);
+        }
+}
+
+/* Chain rule back through the preparation: ddt [rows][H] and dA [H] are the
+ * gradients with respect to the prepared dt and A.  d_raw = ddt * sigmoid *
+ * [inside]; d_bias[h] = sum over rows of d_raw (rows ascending); d_logA = dA * A
+ * (the derivative of -exp(logA) is itself). */
+void oracle_dt_prep_bwd(int64_t rows, int64_t H, const double *raw, const double *bias,
+                        const double *logA, float lo, float hi, const double *ddt,
+                        const double *dA, double *d_raw, double *d_bias, double *d_logA) {
+    for (int64_t h = 0; h < H; ++h) {
+        d_logA[h] = dA[h] * -exp(logA[h]);
+        d_bias[h] = 0.0;
+    }
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t h = 0; h < H; ++h) {
+            const double v = raw[r * H + h] + bias[h];
+            const double g = inside(softplus64(v), lo, hi) ? ddt[r * H + h] * sigmoid64(v) : 0.0;
+            d_raw[r * H + h] = g;
+            d_bias[h] += g;
+        }
+}
