@@ -116,6 +116,20 @@ size_t replay_ws_bytes(const ssm_dims *d, int64_t r) {
     return 2 * round_up(static_cast<size_t>(r) * d->batch * d->nheads * 4 * sizeof(float));
 }
 
+// The preparation reads batch, seqlen and nheads only.
+ssm_status check_dt_prep_dims(const ssm_dims *d, float lo, float hi) {
+    if (d == nullptr) return SSM_ERR_NULL;
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->nheads > 65535) return SSM_ERR_DIMS;
+    if (d->seqlen > 0 && d->batch > (int64_t(1) << 62) / d->seqlen) return SSM_ERR_DIMS;
+    if (d->batch * d->seqlen > (int64_t(1) << 37)) return SSM_ERR_DIMS;  // row tiles fit a 32-bit grid
+    if (!(lo <= hi)) return SSM_ERR_DIMS;  // also rejects NaN bounds
+    return SSM_OK;
+}
+
+size_t dt_prep_ws_bytes(const ssm_dims *d) {
+    return round_up(static_cast<size_t>(dt_prep_row_tiles(d->batch * d->seqlen)) * d->nheads * sizeof(double));
+}
+
 hipError_t fill(float *p, int64_t n, hipStream_t s) { return launch_fill(p, n, 0.f, s); }
 
 std::atomic<void *> g_prof_begin{nullptr}, g_prof_end{nullptr};
@@ -159,6 +173,10 @@ size_t ssm_workspace_bytes(const ssm_dims *d, ssm_dtype dtype, int which, int64_
         if (check_dims(d, true) != SSM_OK) return static_cast<size_t>(-1);
         if (!mfma_bwd_path(d, dtype) && !serial_supported(d)) return static_cast<size_t>(-1);
         return bwd_ws_bytes(d, dtype);
+    }
+    if (which == SSM_WS_DT_PREP_BWD) {
+        if (check_dt_prep_dims(d, 0.f, 0.f) != SSM_OK) return static_cast<size_t>(-1);
+        return dt_prep_ws_bytes(d);
     }
     if (which == SSM_WS_REPLAY) {
         if (check_dims(d, false) != SSM_OK || r < 0 || !serial_supported(d))
@@ -389,6 +407,42 @@ ssm_status ssm_replay(const ssm_dims *d, ssm_dtype dtype, const void *ckpt, ssm_
                                 drift_mean, s);
     }
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_dt_prep(const ssm_dims *d, const float *dt_raw, const float *dt_bias,
+                       const float *logA, float dt_lo, float dt_hi, float *dt, float *A,
+                       ssm_stream stream) {
+    ssm_status st = check_dt_prep_dims(d, dt_lo, dt_hi);
+    if (st != SSM_OK) return st;
+    const int64_t rows = d->batch * d->seqlen;
+    if (!logA || !A || (rows > 0 && (!dt_raw || !dt_bias || !dt))) return SSM_ERR_NULL;
+    if (!check_align({}, {}, {}, {dt_raw, dt_bias, logA, dt, A}, SSM_F32, false)) return SSM_ERR_ALIGN;
+    DtPrepArgs a{};
+    a.rows = rows; a.H = static_cast<int>(d->nheads); a.lo = dt_lo; a.hi = dt_hi;
+    a.raw = dt_raw; a.bias = dt_bias; a.logA = logA; a.dt = dt; a.A = A;
+    return launch_dt_prep(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_dt_prep_bwd(const ssm_dims *d, const float *dt_raw, const float *dt_bias,
+                           const float *logA, float dt_lo, float dt_hi, const float *ddt,
+                           const float *dA, float *d_raw, float *d_bias, float *d_logA,
+                           void *workspace, size_t ws_bytes, ssm_stream stream) {
+    ssm_status st = check_dt_prep_dims(d, dt_lo, dt_hi);
+    if (st != SSM_OK) return st;
+    const int64_t rows = d->batch * d->seqlen;
+    if (!dt_bias || !logA || !dA || !d_bias || !d_logA) return SSM_ERR_NULL;
+    if (rows > 0 && (!dt_raw || !ddt || !d_raw)) return SSM_ERR_NULL;
+    if (!check_align({workspace}, {}, {}, {dt_raw, dt_bias, logA, ddt, dA, d_raw, d_bias, d_logA},
+                     SSM_F32, false))
+        return SSM_ERR_ALIGN;
+    const size_t need = dt_prep_ws_bytes(d);
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return SSM_ERR_WORKSPACE;
+    DtPrepArgs a{};
+    a.rows = rows; a.H = static_cast<int>(d->nheads); a.lo = dt_lo; a.hi = dt_hi;
+    a.raw = dt_raw; a.bias = dt_bias; a.logA = logA; a.ddt = ddt; a.dA = dA;
+    a.d_raw = d_raw; a.d_bias = d_bias; a.d_logA = d_logA;
+    a.part = static_cast<double *>(workspace);
+    return launch_dt_prep_bwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 }  // extern "C"

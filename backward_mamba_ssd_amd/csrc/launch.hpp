@@ -79,6 +79,18 @@ struct SsdBwdArgs {
     double *pA, *pD;  // [Bsz, H, nchunks, chunk/64] per-block partials of dA, dD
 };
 
+// Time-step and rate preparation (forward and backward share one block).
+struct DtPrepArgs {
+    int64_t rows;  // batch * seqlen
+    int H;
+    float lo, hi;  // closed clamp interval of the softplus
+    const float *raw, *bias, *logA;
+    float *dt, *A;                          // forward outputs
+    const float *ddt, *dA;                  // backward inputs
+    float *d_raw, *d_bias, *d_logA;         // backward outputs
+    double *part;                           // [row tiles][H] fp64 bias partials
+};
+
 hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);  // state or state16
@@ -89,5 +101,8 @@ hipError_t launch_scan_bwd(const ScanBwdArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_sr16(const Sr16Args &a, hipStream_t s);
 hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s);
 hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s);
+int64_t dt_prep_row_tiles(int64_t rows);
+hipError_t launch_dt_prep(const DtPrepArgs &a, hipStream_t s);
+hipError_t launch_dt_prep_bwd(const DtPrepArgs &a, hipStream_t s);
 
 }  // namespace ssm

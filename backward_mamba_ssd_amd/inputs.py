@@ -5,6 +5,9 @@ arithmetic.  The same tensors feed the GPU library and (copied to the host) the
 fp64 oracle, so both sides always see identical values.
 
 Distributions (one recipe for every workload):
+  time-step preparation inputs: dt_raw ~ N(0, 0.25), dt_bias ~ N(-2, 0.01) per
+  head (so dt_raw + dt_bias matches the N(-2, 0.5) spread below), logA ~ U(0, ln 16);
+  upstream ddt, dA ~ N(0, 1);
   x ~ N(0, 1); B, C ~ N(0, 1/N); dt = softplus(N(-2, 0.5)) (positive, float32);
   A = -exp(U(0, ln 16)) per head (float32); D ~ N(0, 1) per head (float32);
   dy ~ N(0, 1); optional h0 / dh_final ~ N(0, 1) (float32).
@@ -25,7 +28,7 @@ from dataclasses import dataclass, field
 import torch
 
 TENSOR_IDS = {"x": 1, "B": 2, "C": 3, "dt": 4, "A": 5, "D": 6, "dy": 7, "h0": 8,
-              "dh_final": 9}
+              "dh_final": 9, "dt_raw": 10, "dt_bias": 11, "logA": 12, "ddt": 13, "dA": 14}
 
 
 @dataclass(frozen=True)
@@ -88,6 +91,14 @@ def draw(name, shape, seed, device="cpu", dtype=torch.float32, dstate=None):
         v = torch.nn.functional.softplus(-2.0 + 0.5 * _randn(shape, s, device))
     elif name == "A":
         v = -torch.exp(_rand(shape, s, device) * math.log(16.0))
+    elif name == "dt_raw":   # raw + bias ~ N(-2, ~0.5), the spread of the prepared dt above
+        v = 0.5 * _randn(shape, s, device)
+    elif name == "dt_bias":
+        v = -2.0 + 0.1 * _randn(shape, s, device)
+    elif name == "logA":     # A = -exp(logA) = -exp(U(0, ln 16)) as above
+        v = _rand(shape, s, device) * math.log(16.0)
+    elif name in ("ddt", "dA"):
+        v = _randn(shape, s, device)
     else:
         raise KeyError(name)
     return v.to(dtype).contiguous()

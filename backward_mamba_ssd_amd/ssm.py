@@ -18,12 +18,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
 
 SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
-SSM_WS_FWD, SSM_WS_BWD, SSM_WS_REPLAY = 0, 1, 2
+SSM_WS_FWD, SSM_WS_BWD, SSM_WS_REPLAY, SSM_WS_DT_PREP_BWD = 0, 1, 2, 3
 _SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_decode_step", "ssm_decode_step_sr16",
            "ssm_checkpoint_sr16",
-           "ssm_replay", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path",
+           "ssm_replay", "ssm_dt_prep", "ssm_dt_prep_bwd", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path",
            "ssm_profile_next_bwd_block")
 
 
@@ -65,6 +65,11 @@ def _load():
     lib.ssm_replay.argtypes = ([D, i32, vp, i32, vp] + [vp] * 6 + [i64, i64] + [vp] * 4
                                + [vp, sz, vp])
     lib.ssm_replay.restype = i32
+    f32 = ctypes.c_float
+    lib.ssm_dt_prep.argtypes = [D, vp, vp, vp, f32, f32, vp, vp, vp]
+    lib.ssm_dt_prep.restype = i32
+    lib.ssm_dt_prep_bwd.argtypes = [D, vp, vp, vp, f32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssm_dt_prep_bwd.restype = i32
     lib.ssm_profile_next_bwd_block.argtypes = [vp, vp]
     lib.ssm_profile_next_bwd_block.restype = None
     return lib
@@ -269,3 +274,42 @@ def ssm_replay(ckpt, x, B, C, dt, A, D, t0, r, state_out=None, y=None, live=None
                          _ptr(live), _ptr(dmax), _ptr(dmean), _ptr(ws), wsb, _stream(stream))
     _check(st, "ssm_replay")
     return {"state": state_out, "drift_max": dmax, "drift_mean": dmean}
+
+
+def _dt_prep_dims(dt_raw):
+    if dt_raw.dim() != 3:
+        raise ValueError("dt_raw is [batch, seqlen, nheads]")
+    b, t, h = dt_raw.shape
+    return make_dims(b, t, h, 1, 1, 1, 1)
+
+
+def ssm_dt_prep(dt_raw, dt_bias, logA, dt_lo=0.0, dt_hi=float("inf"), dt=None, A=None,
+                stream=None):
+    """dt = clamp(softplus(dt_raw + dt_bias[h]), dt_lo, dt_hi) and A = -exp(logA).
+    Returns (dt [batch, seqlen, nheads], A [nheads]), float32."""
+    dims = _dt_prep_dims(dt_raw)
+    if dt is None:
+        dt = torch.empty_like(dt_raw)
+    if A is None:
+        A = torch.empty_like(logA)
+    st = _lib.ssm_dt_prep(ctypes.byref(dims), _ptr(dt_raw), _ptr(dt_bias), _ptr(logA),
+                          float(dt_lo), float(dt_hi), _ptr(dt), _ptr(A), _stream(stream))
+    _check(st, "ssm_dt_prep")
+    return dt, A
+
+
+def ssm_dt_prep_bwd(dt_raw, dt_bias, logA, ddt, dA, dt_lo=0.0, dt_hi=float("inf"), out=None,
+                    workspace=None, stream=None):
+    """Gradients through ssm_dt_prep: dict d_raw, d_bias, d_logA (float32)."""
+    dims = _dt_prep_dims(dt_raw)
+    if out is None:
+        out = {"d_raw": torch.empty_like(dt_raw), "d_bias": torch.empty_like(dt_bias),
+               "d_logA": torch.empty_like(logA)}
+    ws, wsb = _workspace(ssm_workspace_bytes(dims, SSM_F32, SSM_WS_DT_PREP_BWD), dt_raw.device,
+                         workspace)
+    st = _lib.ssm_dt_prep_bwd(ctypes.byref(dims), _ptr(dt_raw), _ptr(dt_bias), _ptr(logA),
+                              float(dt_lo), float(dt_hi), _ptr(ddt), _ptr(dA), _ptr(out["d_raw"]),
+                              _ptr(out["d_bias"]), _ptr(out["d_logA"]), _ptr(ws), wsb,
+                              _stream(stream))
+    _check(st, "ssm_dt_prep_bwd")
+    return out

@@ -312,6 +312,46 @@ def replay_sweep(dev):
     return res
 
 
+def dt_prep_rates(dev):
+    """Time-step preparation at the prefill workload's [batch, T, heads]: forward
+    (raw read, dt written: 8 B per element) and backward (raw and ddt read, d_raw
+    written: 12 B per element; the per-head bias partials are not counted)."""
+    import torch
+
+    from backward_mamba_ssd_amd import inputs, ssm
+
+    w = inputs.WORKLOADS["prefill_b4_t4096"]
+    shp = (w.batch, w.seqlen, w.nheads)
+    pr = {k: inputs.draw(k, s, w.seed, dev) for k, s in
+          (("dt_raw", shp), ("dt_bias", (w.nheads,)), ("logA", (w.nheads,)), ("ddt", shp),
+           ("dA", (w.nheads,)))}
+    dt, A = ssm.ssm_dt_prep(pr["dt_raw"], pr["dt_bias"], pr["logA"], 0.0, float("inf"))
+    g = ssm.ssm_dt_prep_bwd(pr["dt_raw"], pr["dt_bias"], pr["logA"], pr["ddt"], pr["dA"])
+    dims = ssm.make_dims(*shp, 1, 1, 1, 1)
+    ws = torch.empty(max(1, ssm.ssm_workspace_bytes(dims, ssm.SSM_F32, ssm.SSM_WS_DT_PREP_BWD)),
+                     dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    n = dt.numel()
+    for name, fn, nbytes in (
+            ("fwd", lambda: ssm.ssm_dt_prep(pr["dt_raw"], pr["dt_bias"], pr["logA"], 0.0,
+                                            float("inf"), dt=dt, A=A), 8 * n),
+            ("bwd", lambda: ssm.ssm_dt_prep_bwd(pr["dt_raw"], pr["dt_bias"], pr["logA"],
+                                                pr["ddt"], pr["dA"], out=g, workspace=ws),
+             12 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(50):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = path_entry(0, nbytes, e0.elapsed_time(e1) / 50)
+    del pr, dt, A, g, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def secondary(dev):
     """Decode (full 64 x 48 x 100 workload), SR16 and replay rates."""
     import torch
@@ -381,6 +421,7 @@ def secondary(dev):
     out["sr16"] = path_entry(0, st.numel() * 6, e0.elapsed_time(e1) / 20)
     del st, bits
     torch.cuda.empty_cache()
+    out["dt_prep"] = dt_prep_rates(dev)
     log("replay sweep ...")
     out["replay_sr16_b16"] = replay_sweep(dev)
     wl = inputs.WORKLOADS["long_b1_t131072"]

@@ -74,7 +74,7 @@ typedef struct {
 typedef void *ssm_stream; /* hipStream_t */
 
 /* Workspace kinds for ssm_workspace_bytes. */
-enum { SSM_WS_FWD = 0, SSM_WS_BWD = 1, SSM_WS_REPLAY = 2 };
+enum { SSM_WS_FWD = 0, SSM_WS_BWD = 1, SSM_WS_REPLAY = 2, SSM_WS_DT_PREP_BWD = 3 };
 
 /* Bytes of device workspace a call needs (0 is a valid answer).  `r` is the
  * replay length for SSM_WS_REPLAY and ignored otherwise.  Returns (size_t)-1
@@ -198,6 +198,44 @@ ssm_status ssm_replay(const ssm_dims *d, ssm_dtype dtype, const void *ckpt, ssm_
                       const float *dt, const float *A, const float *D, int64_t t0, int64_t r,
                       void *y, const float *live_ckpt, float *drift_max, float *drift_mean,
                       void *workspace, size_t ws_bytes, ssm_stream stream);
+
+/*
+ * Time-step and rate preparation.  "Nemotron Kernels: From Inference To
+ * Backpropagation", section "From Classical State Space To A Selective Mamba
+ * State" (the time step goes through softplus and is clamped to a configured
+ * interval); "Nemotron 3 Ultra: replaying a rounded state", section "The Mamba
+ * state update" (the time step is built from the raw value and a per-head
+ * bias; the rate is A = -exp(logA)).
+ *   dt[r,h] = min(max(softplus(dt_raw[r,h] + dt_bias[h]), dt_lo), dt_hi)
+ *   A[h]    = -exp(logA[h])
+ * Only d->batch, d->seqlen and d->nheads are read: rows r = batch * seqlen,
+ * layouts dt_raw, dt [batch, seqlen, nheads] and dt_bias, logA, A [nheads],
+ * all float32, 4-byte aligned, device memory.  dt_lo <= dt_hi (dt_hi may be
+ * +inf; neither may be NaN), else SSM_ERR_DIMS.  softplus is evaluated in
+ * float32 without a threshold branch (log(1+e^v) computed as
+ * max(v,0) + log1p(e^-|v|)).  dt may alias dt_raw.
+ */
+ssm_status ssm_dt_prep(const ssm_dims *d, const float *dt_raw, const float *dt_bias,
+                       const float *logA, float dt_lo, float dt_hi, float *dt, float *A,
+                       ssm_stream stream);
+
+/*
+ * Chain rule back through ssm_dt_prep (same passages: the derivative of the
+ * softplus is the sigmoid inside the interval and zero where the clamp
+ * saturates; the interval is closed, so a softplus equal to dt_lo or dt_hi
+ * passes its gradient).  ddt [batch, seqlen, nheads] and dA [nheads] are the
+ * gradients on the prepared dt and A (as returned by ssm_bwd).
+ *   d_raw[r,h]  = ddt[r,h] * sigmoid(dt_raw[r,h] + dt_bias[h]) * [inside]
+ *   d_bias[h]   = sum over r of d_raw[r,h]   (fp64 partial sums, fixed order)
+ *   d_logA[h]   = dA[h] * A[h] = -dA[h] * exp(logA[h])
+ * The inside test is taken on the float32 softplus that ssm_dt_prep stores.
+ *   workspace   ssm_workspace_bytes(d, SSM_F32, SSM_WS_DT_PREP_BWD, 0) bytes
+ * Same dims, layouts and alignment as ssm_dt_prep; d_raw may alias ddt.
+ */
+ssm_status ssm_dt_prep_bwd(const ssm_dims *d, const float *dt_raw, const float *dt_bias,
+                           const float *logA, float dt_lo, float dt_hi, const float *ddt,
+                           const float *dA, float *d_raw, float *d_bias, float *d_logA,
+                           void *workspace, size_t ws_bytes, ssm_stream stream);
 
 /*
  * Benchmark timing hook (no counterpart on the pages).  `begin` and `end` are

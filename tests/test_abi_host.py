@@ -149,3 +149,46 @@ def test_workspace_and_path_predicates():
                                       ssm.SSM_BF16)
     assert not ssm.ssm_uses_mfma_path(dims(batch=1, seqlen=256, nheads=8, ngroups=1, chunk=96),
                                       ssm.SSM_BF16)
+
+
+def prep_dims(batch=2, seqlen=100, nheads=256):
+    return ssm.make_dims(batch, seqlen, nheads, 1, 1, 1, 1)
+
+
+def test_dt_prep_rejects_bad_calls_before_any_work():
+    L = ssm.lib()
+    d = prep_dims()
+    inf, nan = float("inf"), float("nan")
+
+    def prep(dd, raw=FAKE, bias=FAKE, logA=FAKE, lo=0.0, hi=inf, dt=FAKE, A=FAKE):
+        return L.ssm_dt_prep(ctypes.byref(dd) if dd is not None else None, raw, bias, logA, lo,
+                             hi, dt, A, None)
+
+    assert prep(None) == NULL
+    assert prep(d, lo=0.2, hi=0.1) == DIMS          # empty interval
+    assert prep(d, lo=nan) == DIMS and prep(d, hi=nan) == DIMS
+    assert prep(prep_dims(nheads=0)) == DIMS
+    assert prep(prep_dims(batch=-1)) == DIMS
+    assert prep(d, raw=None) == NULL and prep(d, A=None) == NULL and prep(d, logA=None) == NULL
+    assert prep(d, dt=FAKE + 2) == ALIGN
+
+    def prep_bwd(dd, ws=None, wsb=0, **over):
+        a = dict(raw=FAKE, bias=FAKE, logA=FAKE, lo=0.0, hi=inf, ddt=FAKE, dA=FAKE, d_raw=FAKE,
+                 d_bias=FAKE, d_logA=FAKE)
+        a.update(over)
+        return L.ssm_dt_prep_bwd(ctypes.byref(dd), a["raw"], a["bias"], a["logA"], a["lo"],
+                                 a["hi"], a["ddt"], a["dA"], a["d_raw"], a["d_bias"],
+                                 a["d_logA"], ws, wsb, None)
+
+    need = ssm.ssm_workspace_bytes(d, ssm.SSM_F32, ssm.SSM_WS_DT_PREP_BWD)
+    # 200 rows -> 4 row tiles of 64, one fp64 partial per (tile, head), rounded to 256 B
+    assert need == 4 * 256 * 8
+    assert prep_bwd(d) == WS
+    assert prep_bwd(d, ws=FAKE, wsb=need - 1) == WS
+    assert prep_bwd(d, ws=FAKE, wsb=need, lo=1.0, hi=0.5) == DIMS
+    assert prep_bwd(d, ws=FAKE, wsb=need, dA=None) == NULL
+    assert prep_bwd(d, ws=FAKE, wsb=need, ddt=None) == NULL
+    assert prep_bwd(d, ws=FAKE + 4, wsb=need) == ALIGN
+    assert prep_bwd(d, ws=FAKE, wsb=need, d_bias=FAKE + 1) == ALIGN
+    # no rows: the per-row pointers may be NULL (the call still writes d_bias = 0, d_logA)
+    assert ssm.ssm_workspace_bytes(prep_dims(seqlen=0), ssm.SSM_F32, ssm.SSM_WS_DT_PREP_BWD) == 0
