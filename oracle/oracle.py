@@ -21,6 +21,10 @@ state as small examples:
 * ``replay_additive`` -- same page, section "Recovering the state by replay":
   the s' = s + u example of replaying the pending buffer from a checkpoint.
 
+``draft_snapshots`` / ``rollback`` -- same page, section "Rolling back rejected
+draft tokens": a snapshot after every draft step with the initial state first,
+and the restore that selects the snapshot after the accepted prefix.
+
 ``dt_prep`` / ``dt_prep_bwd`` wrap the C preparation of the time step
 (softplus of raw + bias, clamped to a closed interval) and of the per-head rate
 A = -exp(logA), with their gradients.
@@ -184,6 +188,37 @@ def replay(ckpt, x, B, C, dt, A, D, t0, r):
     sl = slice(t0, t0 + r)
     return fwd(_f64(x)[:, sl], _f64(B)[:, sl], _f64(C)[:, sl], _f64(dt)[:, sl], A, D,
                h0=ckpt)
+
+
+# ----------------------------------------------------------------------------
+# speculative drafts and rollback ("Nemotron 3 Ultra: replaying a rounded state",
+# section "Rolling back rejected draft tokens")
+# ----------------------------------------------------------------------------
+
+def draft_snapshots(state0, x, B, C, dt, A, D):
+    """The snapshot stack of a draft of Dr tokens: slot 0 is the initial state (the
+    page includes it, so rejecting the whole draft selects it) and slot k the state
+    after the first k draft tokens, each token taken by the one-step update.
+    x [Bsz,Dr,H,P], B/C [Bsz,Dr,G,N], dt [Bsz,Dr,H]; returns (snapshots
+    [Dr+1,Bsz,H,P,N], y [Bsz,Dr,H,P]), float64."""
+    s = np.array(_f64(state0), dtype=np.float64, order="C", copy=True)
+    x, B, C, dt = (_f64(v) for v in (x, B, C, dt))
+    Bsz, Dr, H, P = x.shape
+    snaps = np.empty((Dr + 1,) + s.shape, np.float64)
+    y = np.empty((Bsz, Dr, H, P), np.float64)
+    snaps[0] = s
+    for k in range(Dr):
+        y[:, k] = decode_step(s, np.ascontiguousarray(x[:, k]), np.ascontiguousarray(B[:, k]),
+                              np.ascontiguousarray(C[:, k]), np.ascontiguousarray(dt[:, k]), A, D)
+        snaps[k + 1] = s
+    return snaps, y
+
+
+def rollback(snapshots, accepted):
+    """The state to continue from after verification: for sequence b, the stored
+    snapshot after its accepted[b] draft tokens (the page's restore)."""
+    snapshots = _f64(snapshots)
+    return np.stack([snapshots[int(a), b] for b, a in enumerate(accepted)])
 
 
 # ----------------------------------------------------------------------------
