@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <climits>
 #include <cstring>
 #include <atomic>
 #include <initializer_list>
@@ -121,7 +122,7 @@ ssm_status check_dt_prep_dims(const ssm_dims *d, float lo, float hi) {
     if (d == nullptr) return SSM_ERR_NULL;
     if (d->batch < 0 || d->seqlen < 0 || d->nheads < 1 || d->nheads > 65535) return SSM_ERR_DIMS;
     if (d->seqlen > 0 && d->batch > (int64_t(1) << 62) / d->seqlen) return SSM_ERR_DIMS;
-    if (d->batch * d->seqlen > (int64_t(1) << 37)) return SSM_ERR_DIMS;  // row tiles fit a 32-bit grid
+    if (d->batch * d->seqlen > (int64_t(1) << 34)) return SSM_ERR_DIMS;  // 16-row tiles fit the grid
     if (!(lo <= hi)) return SSM_ERR_DIMS;  // also rejects NaN bounds
     return SSM_OK;
 }
@@ -443,6 +444,55 @@ ssm_status ssm_dt_prep_bwd(const ssm_dims *d, const float *dt_raw, const float *
     a.d_raw = d_raw; a.d_bias = d_bias; a.d_logA = d_logA;
     a.part = static_cast<double *>(workspace);
     return launch_dt_prep_bwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_draft_snapshots(const ssm_dims *d, ssm_dtype dtype, float *snapshots,
+                               const void *x, const void *B, const void *C, const float *dt,
+                               const float *A, const float *D, void *y, ssm_stream stream) {
+    ssm_status st = check_dims(d, false);
+    if (st != SSM_OK) return st;
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (!serial_supported(d)) return SSM_ERR_UNSUPPORTED;
+    if (!A || !D) return SSM_ERR_NULL;
+    if (d->batch > 0 && !snapshots) return SSM_ERR_NULL;
+    if (d->batch > 0 && d->seqlen > 0 && (!x || !B || !C || !dt)) return SSM_ERR_NULL;
+    if (!check_align({snapshots}, {B, C}, {x, y}, {dt, A, D}, dtype, false)) return SSM_ERR_ALIGN;
+    if (d->batch == 0 || d->seqlen == 0) return SSM_OK;
+    ScanArgs a{};
+    a.Bsz = d->batch; a.T = d->seqlen; a.H = static_cast<int>(d->nheads);
+    a.P = static_cast<int>(d->headdim); a.N = static_cast<int>(d->dstate);
+    a.G = static_cast<int>(d->ngroups); a.t0 = 0; a.r = d->seqlen; a.L = 1; a.nchunks = 0;
+    a.ckpt = snapshots; a.live = nullptr; a.state_out = nullptr;
+    a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.D = D; a.y = y; a.chunk_states = nullptr;
+    a.snap = snapshots;
+    a.snap_stride = d->batch * d->nheads * d->headdim * d->dstate;
+    return launch_scan(a, dtype == SSM_BF16, false, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSM_OK
+               : SSM_ERR_HIP;
+}
+
+ssm_status ssm_rollback(const ssm_dims *d, const float *snapshots, const int32_t *accepted,
+                        float *state_out, int32_t *err, ssm_stream stream) {
+    ssm_status st = check_dims(d, false);
+    if (st != SSM_OK) return st;
+    if (d->batch > 65535 || d->seqlen > INT32_MAX) return SSM_ERR_DIMS;
+    if (d->batch == 0) return SSM_OK;
+    if (!snapshots || !accepted || !state_out) return SSM_ERR_NULL;
+    if (!aligned(snapshots, 16) || !aligned(state_out, 16) || !aligned(accepted, 4) ||
+        !aligned(err, 4))
+        return SSM_ERR_ALIGN;
+    const int64_t per_seq = d->nheads * d->headdim * d->dstate;
+    if (per_seq % 4 != 0) return SSM_ERR_UNSUPPORTED;  // 16-byte copies
+    // state_out is one of the slots, or disjoint from the whole stack
+    const char *s0 = reinterpret_cast<const char *>(snapshots);
+    const size_t slot_bytes = static_cast<size_t>(d->batch) * per_seq * sizeof(float);
+    const char *s1 = s0 + (d->seqlen + 1) * slot_bytes;
+    const char *o = reinterpret_cast<const char *>(state_out);
+    if (o + slot_bytes > s0 && o < s1 && (o < s0 || (o - s0) % slot_bytes != 0)) return SSM_ERR_DIMS;
+    RollbackArgs a{};
+    a.Bsz = d->batch; a.per_seq = per_seq; a.ndraft = d->seqlen;
+    a.snap = snapshots; a.accepted = accepted; a.state_out = state_out; a.err = err;
+    return launch_rollback(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 }  // extern "C"

@@ -19,17 +19,18 @@
 //
 // Both directions are HBM-bound elementwise passes over [rows, H] float32
 // (8 B per element forward, 12 B backward).  The bias sum is deterministic:
-// each workgroup of the backward owns a tile of rows x 64 heads, sums its rows
-// per head in fp64 in a fixed order and writes one partial per head; a second
-// pass adds the partials of a head in ascending tile order.
+// each workgroup of the backward owns a tile of 16 rows x 256 heads, sums its
+// rows per head in fp64 in row order and writes one partial per head; a second
+// pass adds a head's partials in a fixed order (strided lane sums, then lanes in
+// order).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ssm {
 namespace {
 
-constexpr int kRowsPerTile = 64;  // rows of one backward workgroup
-constexpr int kHeadsPerTile = 64; // heads of one backward workgroup (one per lane)
+constexpr int kRowsPerTile = 16;   // rows of one workgroup (loads in flight together)
+constexpr int kHeadsPerTile = 256; // heads of one workgroup (one per thread)
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|); no overflow for any v.
 __device__ __forceinline__ float softplus32(float v) {
@@ -42,53 +43,68 @@ __device__ __forceinline__ float sigmoid32(float v) {
     return v >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
 }
 
+// Tile (row tile rt, head tile ht): thread t takes head ht*256 + t and the tile's
+// rows; a wave reads 64 consecutive heads of one row (256 contiguous bytes).
 __global__ void __launch_bounds__(256) dt_prep_kernel(DtPrepArgs a) {
-    const int64_t n = a.rows * a.H;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const int h = static_cast<int>(i % a.H);
-        const float sp = softplus32(a.raw[i] + a.bias[h]);
-        a.dt[i] = fminf(fmaxf(sp, a.lo), a.hi);
-    }
-    if (blockIdx.x == 0)
-        for (int h = threadIdx.x; h < a.H; h += blockDim.x) a.A[h] = -expf(a.logA[h]);
+    const int h = blockIdx.y * kHeadsPerTile + threadIdx.x;
+    if (blockIdx.x == 0 && h < a.H) a.A[h] = -expf(a.logA[h]);
+    if (h >= a.H) return;
+    const float bh = a.bias[h];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRowsPerTile;
+    const int nr = a.rows - r0 < kRowsPerTile ? static_cast<int>(a.rows - r0) : kRowsPerTile;
+    float v[kRowsPerTile];
+#pragma unroll
+    for (int r = 0; r < kRowsPerTile; ++r)
+        if (r < nr) v[r] = a.raw[(r0 + r) * a.H + h];
+#pragma unroll
+    for (int r = 0; r < kRowsPerTile; ++r)
+        if (r < nr) a.dt[(r0 + r) * a.H + h] = fminf(fmaxf(softplus32(v[r] + bh), a.lo), a.hi);
 }
 
-// Tile (row tile rt, head tile ht): wave w takes rows rt*64 + w, +4, ...; lane l
-// takes head ht*64 + l.  The four waves' fp64 sums meet in LDS in wave order.
+// Same tiling; each thread sums its head's d_raw over the tile's rows in fp64, in
+// row order, and writes one partial per (row tile, head).
 __global__ void __launch_bounds__(256) dt_prep_bwd_kernel(DtPrepArgs a) {
-    __shared__ double part[4][kHeadsPerTile];
-    const int rt = blockIdx.x, ht = blockIdx.y;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int h = ht * kHeadsPerTile + lane;
+    const int h = blockIdx.y * kHeadsPerTile + threadIdx.x;
+    if (h >= a.H) return;
+    const float bh = a.bias[h];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRowsPerTile;
+    const int nr = a.rows - r0 < kRowsPerTile ? static_cast<int>(a.rows - r0) : kRowsPerTile;
+    float v[kRowsPerTile], gi[kRowsPerTile];
+#pragma unroll
+    for (int r = 0; r < kRowsPerTile; ++r)
+        if (r < nr) {
+            v[r] = a.raw[(r0 + r) * a.H + h];
+            gi[r] = a.ddt[(r0 + r) * a.H + h];
+        }
     double acc = 0.0;
-    if (h < a.H) {
-        const float bh = a.bias[h];
-        const int64_t r0 = static_cast<int64_t>(rt) * kRowsPerTile;
-        const int64_t r1 = r0 + kRowsPerTile < a.rows ? r0 + kRowsPerTile : a.rows;
-        for (int64_t r = r0 + wave; r < r1; r += 4) {
-            const int64_t i = r * a.H + h;
-            const float v = a.raw[i] + bh;
-            const float sp = softplus32(v);
+#pragma unroll
+    for (int r = 0; r < kRowsPerTile; ++r)
+        if (r < nr) {
+            const float u = v[r] + bh;
+            const float sp = softplus32(u);
             const bool inside = sp >= a.lo && sp <= a.hi;
-            const float g = inside ? a.ddt[i] * sigmoid32(v) : 0.f;
-            a.d_raw[i] = g;
+            const float g = inside ? gi[r] * sigmoid32(u) : 0.f;
+            a.d_raw[(r0 + r) * a.H + h] = g;
             acc += static_cast<double>(g);
         }
-    }
-    part[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0 && h < a.H)
-        a.part[static_cast<int64_t>(rt) * a.H + h] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    a.part[static_cast<int64_t>(blockIdx.x) * a.H + h] = acc;
 }
 
-__global__ void __launch_bounds__(256) dt_prep_bwd_heads_kernel(DtPrepArgs a, int ntiles) {
-    const int h = blockIdx.x * blockDim.x + threadIdx.x;
-    if (h >= a.H) return;
+// One 64-lane workgroup per head: lane l adds the partials of tiles l, l+64, ... in
+// order, then lane 0 adds the 64 lane sums in lane order (a fixed order).
+__global__ void __launch_bounds__(64) dt_prep_bwd_heads_kernel(DtPrepArgs a, int64_t ntiles) {
+    __shared__ double red[64];
+    const int h = blockIdx.x, lane = threadIdx.x;
     double s = 0.0;
-    for (int t = 0; t < ntiles; ++t) s += a.part[static_cast<int64_t>(t) * a.H + h];
-    a.d_bias[h] = static_cast<float>(s);
-    a.d_logA[h] = a.dA[h] * -expf(a.logA[h]);
+    for (int64_t t = lane; t < ntiles; t += 64) s += a.part[t * a.H + h];
+    red[lane] = s;
+    __syncthreads();
+    if (lane == 0) {
+        double tot = 0.0;
+        for (int l = 0; l < 64; ++l) tot += red[l];
+        a.d_bias[h] = static_cast<float>(tot);
+        a.d_logA[h] = a.dA[h] * -expf(a.logA[h]);
+    }
 }
 
 }  // namespace
@@ -96,11 +112,10 @@ __global__ void __launch_bounds__(256) dt_prep_bwd_heads_kernel(DtPrepArgs a, in
 int64_t dt_prep_row_tiles(int64_t rows) { return (rows + kRowsPerTile - 1) / kRowsPerTile; }
 
 hipError_t launch_dt_prep(const DtPrepArgs &a, hipStream_t s) {
-    const int64_t n = a.rows * a.H;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
-    if (blocks < 1) blocks = 1;          // A is written even with no rows
-    dt_prep_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(a);
+    int64_t nt = dt_prep_row_tiles(a.rows);
+    if (nt < 1) nt = 1;  // A is written even with no rows
+    const dim3 grid(static_cast<unsigned>(nt), static_cast<unsigned>((a.H + kHeadsPerTile - 1) / kHeadsPerTile));
+    dt_prep_kernel<<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -112,7 +127,7 @@ hipError_t launch_dt_prep_bwd(const DtPrepArgs &a, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dt_prep_bwd_heads_kernel<<<static_cast<unsigned>((a.H + 255) / 256), 256, 0, s>>>(a, static_cast<int>(nt));
+    dt_prep_bwd_heads_kernel<<<static_cast<unsigned>(a.H), 64, 0, s>>>(a, nt);
     return hipGetLastError();
 }
 

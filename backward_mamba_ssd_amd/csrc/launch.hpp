@@ -31,6 +31,18 @@ struct ScanArgs {
     void *y;
     float *chunk_states;
     float *part_max, *part_sum;  // [r][Bsz*H*4] per-wave drift partials
+    float *snap;                 // nullptr, or a snapshot stack: slot k+1 <- state after token t0+k
+    int64_t snap_stride;         // floats between slots
+};
+
+// Rollback: state_out[b] <- snapshots[accepted[b]][b]
+struct RollbackArgs {
+    int64_t Bsz, per_seq;  // per_seq: floats per sequence (H*P*N), a multiple of 4
+    int64_t ndraft;        // slots 0..ndraft
+    const float *snap;
+    const int32_t *accepted;
+    float *state_out;
+    int32_t *err;          // nullptr, or set to 1 when an accepted count is out of range
 };
 
 struct ScanBwdArgs {
@@ -97,6 +109,7 @@ hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);  // sta
 hipError_t launch_scan(const ScanArgs &a, bool bf16, bool ckpt_f16, hipStream_t s);
 hipError_t launch_drift_reduce(const float *pm, const float *ps, int64_t nwaves, int64_t r,
                                double inv_count, float *dmax, float *dmean, hipStream_t s);
+hipError_t launch_rollback(const RollbackArgs &a, hipStream_t s);
 hipError_t launch_scan_bwd(const ScanBwdArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_sr16(const Sr16Args &a, hipStream_t s);
 hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s);

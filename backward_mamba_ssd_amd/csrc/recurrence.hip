@@ -288,6 +288,14 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
 #pragma unroll
                 for (int i = 0; i < MAXR; ++i) row_update(s[i], av, xv[i], bdt);
             }
+            if (a.snap != nullptr) {  // snapshot stack: the state after this token
+                float *sp = a.snap + (k + 1) * a.snap_stride + bh * PN;
+#pragma unroll
+                for (int i = 0; i < MAXR; ++i) {
+                    const int p = r0 + i * RPW;
+                    if (p < a.P) *reinterpret_cast<float4 *>(sp + static_cast<int64_t>(p) * N + n0) = s[i];
+                }
+            }
             if constexpr (LIVE) {
 #pragma unroll
                 for (int i = 0; i < MAXR; ++i) {
@@ -315,6 +323,36 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
                 *reinterpret_cast<float4 *>(a.state_out + bh * PN + static_cast<int64_t>(p) * N + n0) = s[i];
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Rollback after verification of a draft ("Nemotron 3 Ultra: replaying a rounded
+// state", section "Rolling back rejected draft tokens": the selected snapshot is
+// the state after the accepted prefix).  A gather copy, 16 bytes per lane: grid
+// (chunks of a sequence's state, sequence).  An accepted count outside
+// [0, ndraft] writes nothing for that sequence and raises the error flag.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) rollback_kernel(RollbackArgs a) {
+    const int64_t b = blockIdx.y;
+    const int32_t acc = a.accepted[b];
+    if (acc < 0 || acc > a.ndraft) {
+        if (a.err != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.err = 1;
+        return;
+    }
+    const int64_t n4 = a.per_seq / 4;
+    const float4 *src = reinterpret_cast<const float4 *>(a.snap + (static_cast<int64_t>(acc) * a.Bsz + b) * a.per_seq);
+    float4 *dst = reinterpret_cast<float4 *>(a.state_out + b * a.per_seq);
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride)
+        dst[i] = src[i];
+}
+
+hipError_t launch_rollback(const RollbackArgs &a, hipStream_t s) {
+    if (a.Bsz == 0 || a.per_seq == 0) return hipSuccess;
+    int64_t chunks = (a.per_seq / 4 + 255) / 256;
+    if (chunks > 4096) chunks = 4096;  // grid-stride beyond this
+    rollback_kernel<<<dim3(static_cast<unsigned>(chunks), static_cast<unsigned>(a.Bsz)), 256, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 // Fixed-order reduction of the per-wave drift partials: one thread per step.

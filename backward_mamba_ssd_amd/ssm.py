@@ -23,7 +23,7 @@ _SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_decode_step", "ssm_decode_step_sr16",
            "ssm_checkpoint_sr16",
-           "ssm_replay", "ssm_dt_prep", "ssm_dt_prep_bwd", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path",
+           "ssm_replay", "ssm_draft_snapshots", "ssm_rollback", "ssm_dt_prep", "ssm_dt_prep_bwd", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path",
            "ssm_profile_next_bwd_block")
 
 
@@ -66,6 +66,10 @@ def _load():
                                + [vp, sz, vp])
     lib.ssm_replay.restype = i32
     f32 = ctypes.c_float
+    lib.ssm_draft_snapshots.argtypes = [D, i32] + [vp] * 8 + [vp]
+    lib.ssm_draft_snapshots.restype = i32
+    lib.ssm_rollback.argtypes = [D, vp, vp, vp, vp, vp]
+    lib.ssm_rollback.restype = i32
     lib.ssm_dt_prep.argtypes = [D, vp, vp, vp, f32, f32, vp, vp, vp]
     lib.ssm_dt_prep.restype = i32
     lib.ssm_dt_prep_bwd.argtypes = [D, vp, vp, vp, f32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -313,3 +317,33 @@ def ssm_dt_prep_bwd(dt_raw, dt_bias, logA, ddt, dA, dt_lo=0.0, dt_hi=float("inf"
                               _stream(stream))
     _check(st, "ssm_dt_prep_bwd")
     return out
+
+
+def ssm_draft_snapshots(state0, x, B, C, dt, A, D, y=True, snapshots=None, stream=None):
+    """Draft Dr tokens (x [batch, Dr, H, P], ...) from state0 [batch, H, P, N] with a
+    snapshot after every step.  Returns (snapshots [Dr+1, batch, H, P, N] float32 with
+    slot 0 = state0, y [batch, Dr, H, P] or None)."""
+    b, dr, h, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    dims = make_dims(b, dr, h, p, n, g, 1)
+    if snapshots is None:
+        snapshots = torch.empty((dr + 1, b, h, p, n), dtype=torch.float32, device=x.device)
+        snapshots[0].copy_(state0)
+    yt = torch.empty_like(x) if y is True else (y if isinstance(y, torch.Tensor) else None)
+    st = _lib.ssm_draft_snapshots(ctypes.byref(dims), _dtype_code(x), _ptr(snapshots), _ptr(x),
+                                  _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(yt),
+                                  _stream(stream))
+    _check(st, "ssm_draft_snapshots")
+    return snapshots, yt
+
+
+def ssm_rollback(snapshots, accepted, state_out=None, err=None, stream=None):
+    """state_out[b] = snapshots[accepted[b], b]; accepted is a device int32 [batch]."""
+    s1, b, h, p, n = snapshots.shape
+    dims = make_dims(b, s1 - 1, h, p, n, 1, 1)
+    if state_out is None:
+        state_out = torch.empty((b, h, p, n), dtype=torch.float32, device=snapshots.device)
+    st = _lib.ssm_rollback(ctypes.byref(dims), _ptr(snapshots), _ptr(accepted), _ptr(state_out),
+                           _ptr(err), _stream(stream))
+    _check(st, "ssm_rollback")
+    return state_out

@@ -352,6 +352,50 @@ def dt_prep_rates(dev):
     return res
 
 
+def draft_rollback_rates(dev, layers=8, ndraft=4):
+    """Speculative draft with per-step snapshots and the rollback, at the decode
+    workload's per-layer shape (64 sequences x 256 heads x [64, 128] fp32 states),
+    `layers` layers, a draft of `ndraft` tokens.  Draft bytes per layer: slot 0 read,
+    `ndraft` slots written, inputs and outputs; rollback: one state read + one written."""
+    import torch
+
+    from backward_mamba_ssd_amd import inputs, ssm
+
+    w = inputs.WORKLOADS["decode_s64_l48"]
+    b, h, p, n, g = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    snaps = [torch.empty((ndraft + 1, b, h, p, n), dtype=torch.float32, device=dev)
+             for _ in range(layers)]
+    for l in range(layers):
+        snaps[l][0].copy_(inputs.draw("h0", (b, h, p, n), w.seed + l, dev))
+    pr = inputs.make_problem(b, ndraft, h, p, n, g, "bf16", w.seed, dev, with_dy=False)
+    y = torch.empty_like(pr["x"])
+    acc = torch.tensor([i % (ndraft + 1) for i in range(b)], dtype=torch.int32, device=dev)
+    out = torch.empty((b, h, p, n), dtype=torch.float32, device=dev)
+    args = [pr[k] for k in ("x", "B", "C", "dt", "A", "D")]
+    state_b = b * h * p * n * 4
+    io_b = ndraft * (b * h * (2 * p * 2 + 4) + b * g * 2 * 2 * n)
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, fn, nbytes in (
+            ("draft", lambda l: ssm.ssm_draft_snapshots(None, *args, y=y, snapshots=snaps[l]),
+             (1 + ndraft) * state_b + io_b),
+            ("rollback", lambda l: ssm.ssm_rollback(snaps[l], acc, state_out=out), 2 * state_b)):
+        fn(0)
+        torch.cuda.synchronize()
+        e0.record()
+        for rep in range(3):
+            for l in range(layers):
+                fn(l)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (3 * layers)
+        res[name] = path_entry(0, nbytes, ms)
+    res["shape"] = f"{b} sequences x {h} heads x [{p},{n}], draft of {ndraft}, per layer call"
+    del snaps, pr, y, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def secondary(dev):
     """Decode (full 64 x 48 x 100 workload), SR16 and replay rates."""
     import torch
@@ -422,6 +466,7 @@ def secondary(dev):
     del st, bits
     torch.cuda.empty_cache()
     out["dt_prep"] = dt_prep_rates(dev)
+    out["draft_rollback"] = draft_rollback_rates(dev)
     log("replay sweep ...")
     out["replay_sr16_b16"] = replay_sweep(dev)
     wl = inputs.WORKLOADS["long_b1_t131072"]

@@ -200,6 +200,44 @@ ssm_status ssm_replay(const ssm_dims *d, ssm_dtype dtype, const void *ckpt, ssm_
                       void *workspace, size_t ws_bytes, ssm_stream stream);
 
 /*
+ * Speculative draft with a snapshot after every step.  "Nemotron 3 Ultra:
+ * replaying a rounded state", section "Rolling back rejected draft tokens": a
+ * Mamba update overwrites its fixed-size state, so a snapshot is kept at every
+ * draft step, the initial state included, so that rejecting the whole draft
+ * selects it.  d->seqlen is the draft length Dr (d->chunk is ignored).
+ *   snapshots  float [Dr+1][batch][nheads][headdim][dstate], 16-byte aligned:
+ *              slot 0 holds the state before the draft (read, not written);
+ *              slot k (1..Dr) receives the state after draft tokens 0..k-1
+ *   x          [batch, Dr, nheads, headdim] (dtype); B, C [batch, Dr, ngroups,
+ *              dstate] (dtype); dt [batch, Dr, nheads] float
+ *   y          NULL, or [batch, Dr, nheads, headdim] (dtype): the draft outputs
+ * Each token is the update of ssm_decode_step, bit for bit: slot k equals the
+ * state after k ssm_decode_step calls on the same inputs.  Supported dims and
+ * alignment are those of ssm_decode_step.
+ */
+ssm_status ssm_draft_snapshots(const ssm_dims *d, ssm_dtype dtype, float *snapshots,
+                               const void *x, const void *B, const void *C, const float *dt,
+                               const float *A, const float *D, void *y, ssm_stream stream);
+
+/*
+ * Rollback after verification (same section): the state to continue from is
+ * the snapshot after the accepted prefix, per sequence.
+ *   snapshots  from ssm_draft_snapshots with the same dims (d->seqlen = Dr)
+ *   accepted   device int32 [batch], each in [0, Dr]: the number of accepted
+ *              draft tokens of that sequence
+ *   state_out  float [batch][nheads][headdim][dstate], 16-byte aligned;
+ *              state_out[b] <- snapshots[accepted[b]][b] (a copy, bit for bit).
+ *              It may be one of the snapshot slots (for example slot 0, so the
+ *              next draft starts from it); otherwise it must not overlap them.
+ *   err        NULL, or a device int32 set to 1 when some accepted[b] lies
+ *              outside [0, Dr]; that sequence's state_out is then not written
+ *              (the value is only known on the device, so it cannot be rejected
+ *              before the launch).  The flag is never cleared by the call.
+ */
+ssm_status ssm_rollback(const ssm_dims *d, const float *snapshots, const int32_t *accepted,
+                        float *state_out, int32_t *err, ssm_stream stream);
+
+/*
  * Time-step and rate preparation.  "Nemotron Kernels: From Inference To
  * Backpropagation", section "From Classical State Space To A Selective Mamba
  * State" (the time step goes through softplus and is clamped to a configured

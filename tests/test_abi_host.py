@@ -181,8 +181,8 @@ def test_dt_prep_rejects_bad_calls_before_any_work():
                                  a["d_logA"], ws, wsb, None)
 
     need = ssm.ssm_workspace_bytes(d, ssm.SSM_F32, ssm.SSM_WS_DT_PREP_BWD)
-    # 200 rows -> 4 row tiles of 64, one fp64 partial per (tile, head), rounded to 256 B
-    assert need == 4 * 256 * 8
+    # 200 rows -> 13 row tiles of 16, one fp64 partial per (tile, head), rounded to 256 B
+    assert need == 13 * 256 * 8
     assert prep_bwd(d) == WS
     assert prep_bwd(d, ws=FAKE, wsb=need - 1) == WS
     assert prep_bwd(d, ws=FAKE, wsb=need, lo=1.0, hi=0.5) == DIMS
@@ -192,3 +192,32 @@ def test_dt_prep_rejects_bad_calls_before_any_work():
     assert prep_bwd(d, ws=FAKE, wsb=need, d_bias=FAKE + 1) == ALIGN
     # no rows: the per-row pointers may be NULL (the call still writes d_bias = 0, d_logA)
     assert ssm.ssm_workspace_bytes(prep_dims(seqlen=0), ssm.SSM_F32, ssm.SSM_WS_DT_PREP_BWD) == 0
+
+
+def test_draft_and_rollback_reject_bad_calls_before_any_work():
+    L = ssm.lib()
+    d = dims(batch=3, seqlen=4, nheads=4, headdim=64, dstate=128, ngroups=2)
+
+    def draft(dd, snaps=FAKE, x=FAKE, B=FAKE, C=FAKE, dt=FAKE, A=FAKE, D=FAKE, y=None,
+              dtype=ssm.SSM_BF16):
+        return L.ssm_draft_snapshots(ctypes.byref(dd), dtype, snaps, x, B, C, dt, A, D, y, None)
+
+    assert draft(d, snaps=None) == NULL
+    assert draft(d, x=None) == NULL
+    assert draft(d, A=None) == NULL
+    assert draft(d, snaps=FAKE + 4) == ALIGN
+    assert draft(d, dtype=9) == DTYPE
+    assert draft(dims(dstate=100)) == UNSUP
+
+    def rb(dd, snaps=FAKE, acc=FAKE, out=FAKE + (1 << 30), err=None):
+        return L.ssm_rollback(ctypes.byref(dd), snaps, acc, out, err, None)
+
+    assert rb(d, snaps=None) == NULL and rb(d, acc=None) == NULL and rb(d, out=None) == NULL
+    assert rb(d, out=FAKE + (1 << 30) + 8) == ALIGN
+    assert rb(d, acc=FAKE + 2) == ALIGN
+    assert rb(d, err=FAKE + 1) == ALIGN
+    assert rb(dims(batch=70000, seqlen=4)) == DIMS
+    slot = 3 * 4 * 64 * 128 * 4
+    assert rb(d, out=FAKE + slot // 2) == DIMS          # straddles two slots
+    assert rb(d, out=FAKE - slot // 2) == DIMS          # overlaps slot 0 from below
+    assert rb(dims(batch=0)) == OK                        # nothing to do
