@@ -25,6 +25,10 @@ state as small examples:
 draft tokens": a snapshot after every draft step with the initial state first,
 and the restore that selects the snapshot after the accepted prefix.
 
+``conv1d_silu`` / ``gated_rmsnorm`` (and their ``_bwd``) wrap the C versions of
+the stages around the scan: the short causal depthwise convolution with SiLU,
+and the SiLU-gated RMSNorm over groups of channels.
+
 ``dt_prep`` / ``dt_prep_bwd`` wrap the C preparation of the time step
 (softplus of raw + bias, clamped to a closed interval) and of the per-head rate
 A = -exp(logA), with their gradients.
@@ -89,6 +93,15 @@ def _load():
             lib.oracle_dt_prep.restype = None
             lib.oracle_dt_prep_bwd.argtypes = [i64, i64, vp, vp, vp, f32, f32, vp, vp, vp, vp, vp]
             lib.oracle_dt_prep_bwd.restype = None
+            lib.oracle_conv1d_silu.argtypes = [i64] * 4 + [vp] * 6
+            lib.oracle_conv1d_silu.restype = None
+            lib.oracle_conv1d_silu_bwd.argtypes = [i64] * 4 + [vp] * 9
+            lib.oracle_conv1d_silu_bwd.restype = None
+            f64 = ctypes.c_double
+            lib.oracle_gated_rmsnorm.argtypes = [i64] * 3 + [vp] * 3 + [f64, vp]
+            lib.oracle_gated_rmsnorm.restype = None
+            lib.oracle_gated_rmsnorm_bwd.argtypes = [i64] * 3 + [vp] * 3 + [f64] + [vp] * 4
+            lib.oracle_gated_rmsnorm_bwd.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = ctypes.c_int
             _lib = lib
@@ -219,6 +232,59 @@ def rollback(snapshots, accepted):
     snapshot after its accepted[b] draft tokens (the page's restore)."""
     snapshots = _f64(snapshots)
     return np.stack([snapshots[int(a), b] for b, a in enumerate(accepted)])
+
+
+# ----------------------------------------------------------------------------
+# the stages around the scan ("Nemotron Kernels...", Kernel 1 "Forward And
+# Inference": causal Conv1D + SiLU before the scan, gated group RMSNorm after it)
+# ----------------------------------------------------------------------------
+
+def conv1d_silu(u, w, bias, init=None):
+    """SiLU of the short causal depthwise convolution.  u [Bsz,T,C], w [C,K],
+    bias [C], init [Bsz,K-1,C] or None (zeros).  Returns (out [Bsz,T,C],
+    final [Bsz,K-1,C]: the last K-1 samples, the next call's init)."""
+    u, w, bias, init = _f64(u), _f64(w), _f64(bias), _f64(init)
+    Bsz, T, C = u.shape
+    K = w.shape[1]
+    out = np.empty((Bsz, T, C), np.float64)
+    fin = np.empty((Bsz, K - 1, C), np.float64)
+    _load().oracle_conv1d_silu(Bsz, T, C, K, _p(u), _p(w), _p(bias), _p(init), _p(out), _p(fin))
+    return out, fin
+
+
+def conv1d_silu_bwd(u, w, bias, dout, init=None):
+    """Gradients of sum(dout * out): dict du [Bsz,T,C], dw [C,K], dbias [C],
+    dinit [Bsz,K-1,C]."""
+    u, w, bias, init, dout = _f64(u), _f64(w), _f64(bias), _f64(init), _f64(dout)
+    Bsz, T, C = u.shape
+    K = w.shape[1]
+    g = {"du": np.empty((Bsz, T, C)), "dw": np.empty((C, K)), "dbias": np.empty(C),
+         "dinit": np.empty((Bsz, K - 1, C))}
+    _load().oracle_conv1d_silu_bwd(Bsz, T, C, K, _p(u), _p(w), _p(bias), _p(init), _p(dout),
+                                   _p(g["du"]), _p(g["dw"]), _p(g["dbias"]), _p(g["dinit"]))
+    return g
+
+
+def gated_rmsnorm(y, z, w, ngroups, eps=1e-5):
+    """out = g / rms_group(g) * w with g = y * SiLU(z), groups of C/ngroups
+    consecutive channels.  y, z [..., C], w [C]."""
+    y, z, w = _f64(y), _f64(z), _f64(w)
+    C = y.shape[-1]
+    rows = y.size // C if C else 0
+    out = np.empty(y.shape, np.float64)
+    _load().oracle_gated_rmsnorm(rows, C, ngroups, _p(y), _p(z), _p(w), float(eps), _p(out))
+    return out
+
+
+def gated_rmsnorm_bwd(y, z, w, dout, ngroups, eps=1e-5):
+    """Gradients of sum(dout * out): dict dy, dz [..., C], dw [C]."""
+    y, z, w, dout = _f64(y), _f64(z), _f64(w), _f64(dout)
+    C = y.shape[-1]
+    rows = y.size // C if C else 0
+    g = {"dy": np.empty(y.shape), "dz": np.empty(y.shape), "dw": np.empty(C)}
+    _load().oracle_gated_rmsnorm_bwd(rows, C, ngroups, _p(y), _p(z), _p(w), float(eps), _p(dout),
+                                     _p(g["dy"]), _p(g["dz"]), _p(g["dw"]))
+    return g
 
 
 # ----------------------------------------------------------------------------

@@ -435,3 +435,165 @@ void oracle_dt_prep_bwd(int64_t rows, int64_t H, const double *raw, const double
             d_bias[h] += g;
         }
 }
+
+/*
+ * Short causal depthwise convolution followed by SiLU, and its backward.
+ * "Nemotron Kernels: From Inference To Backpropagation", Kernel 1 "Forward And
+ * Inference": the hidden stream passes a causal Conv1D + SiLU before the scan;
+ * each output multiplies a short weight vector with the current sample and the
+ * ones before it (never a later one) and adds the products; the decode kernel
+ * applies SiLU to the convolution sum.  Section "What Conv1D Gives The Mamba
+ * Block": in the backward every output gradient reaches the inputs of its window,
+ * the weights that touched them and the bias, and overlapping windows add at one
+ * input; the SiLU derivative is applied first.
+ * Per batch b and channel c, with the K-1 samples before token 0 taken from
+ * init [Bsz][K-1][Cch] (zero when init is NULL):
+ *   ext[j] = init[j] (j < K-1),  ext[K-1+t] = u[t]
+ *   v[t]   = bias[c] + sum_{k=0..K-1} w[c][k] * ext[t+k]      (w[c][K-1] meets u[t])
+ *   out[t] = v[t] * sigmoid(v[t])
+ * final [Bsz][K-1][Cch] receives ext[T .. T+K-2] (the samples the next call
+ * needs).  Layouts: u, out [Bsz][T][Cch]; w [Cch][K]; bias [Cch].
+ */
+static double silu64(double v) { return v * sigmoid64(v); }
+static double silu_grad64(double v) {
+    const double s = sigmoid64(v);
+    return s * (1.0 + v * (1.0 - s));
+}
+
+static void conv_window(int64_t T, int64_t Cch, int64_t K, const double *u, const double *init,
+                        int64_t b, int64_t c, double *ext) {
+    for (int64_t j = 0; j < K - 1; ++j) ext[j] = init ? init[(b * (K - 1) + j) * Cch + c] : 0.0;
+    for (int64_t t = 0; t < T; ++t) ext[K - 1 + t] = u[(b * T + t) * Cch + c];
+}
+
+void oracle_conv1d_silu(int64_t Bsz, int64_t T, int64_t Cch, int64_t K, const double *u,
+                        const double *w, const double *bias, const double *init, double *out,
+                        double *final_state) {
+#pragma omp parallel
+    {
+        double *ext = malloc(sizeof(double) * (size_t)(T + K));
+#pragma omp for collapse(2) schedule(static)
+        for (int64_t b = 0; b < Bsz; ++b)
+            for (int64_t c = 0; c < Cch; ++c) {
+                conv_window(T, Cch, K, u, init, b, c, ext);
+                for (int64_t t = 0; t < T; ++t) {
+                    double v = bias[c];
+                    for (int64_t k = 0; k < K; ++k) v += w[c * K + k] * ext[t + k];
+                    out[(b * T + t) * Cch + c] = silu64(v);
+                }
+                if (final_state)
+                    for (int64_t j = 0; j < K - 1; ++j) final_state[(b * (K - 1) + j) * Cch + c] = ext[T + j];
+            }
+        free(ext);
+    }
+}
+
+/* dv = dout * SiLU'(v); d ext[t+k] += w[c][k] dv[t]; dw[c][k] += dv[t] ext[t+k];
+ * dbias[c] += dv[t]; du[t] = d ext[K-1+t]; dinit[j] = d ext[j].  Sums over (b, t)
+ * ascending.  dinit may be NULL. */
+void oracle_conv1d_silu_bwd(int64_t Bsz, int64_t T, int64_t Cch, int64_t K, const double *u,
+                            const double *w, const double *bias, const double *init,
+                            const double *dout, double *du, double *dw, double *dbias,
+                            double *dinit) {
+#pragma omp parallel
+    {
+        double *ext = malloc(sizeof(double) * (size_t)(T + K));
+        double *dext = malloc(sizeof(double) * (size_t)(T + K));
+#pragma omp for schedule(static)
+        for (int64_t c = 0; c < Cch; ++c) {
+            double db = 0.0;
+            for (int64_t k = 0; k < K; ++k) dw[c * K + k] = 0.0;
+            for (int64_t b = 0; b < Bsz; ++b) {
+                conv_window(T, Cch, K, u, init, b, c, ext);
+                for (int64_t j = 0; j < T + K - 1; ++j) dext[j] = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    double v = bias[c];
+                    for (int64_t k = 0; k < K; ++k) v += w[c * K + k] * ext[t + k];
+                    const double dv = dout[(b * T + t) * Cch + c] * silu_grad64(v);
+                    db += dv;
+                    for (int64_t k = 0; k < K; ++k) {
+                        dext[t + k] += w[c * K + k] * dv;
+                        dw[c * K + k] += dv * ext[t + k];
+                    }
+                }
+                for (int64_t t = 0; t < T; ++t) du[(b * T + t) * Cch + c] = dext[K - 1 + t];
+                if (dinit)
+                    for (int64_t j = 0; j < K - 1; ++j) dinit[(b * (K - 1) + j) * Cch + c] = dext[j];
+            }
+            dbias[c] = db;
+        }
+        free(ext);
+        free(dext);
+    }
+}
+
+/*
+ * Gated group RMSNorm after the scan, and its backward.  Same page, Kernel 1
+ * pipeline "selective scan -> gated group RMSNorm" and section "From Classical
+ * State Space To A Selective Mamba State": a learned SiLU gate controls how much
+ * signal passes; the page's RMSNorm remark: its backward needs the input, the
+ * learned scale, the inverse RMS and the reduction.  Reading: the gate multiplies
+ * before the normalisation and the mean square is taken over each group of
+ * Cch/G consecutive channels:
+ *   g = y * SiLU(z);  r = 1/sqrt(mean_group(g^2) + eps);  out = g * r * w[c]
+ * Layouts: y, z, out [rows][Cch]; w [Cch].
+ */
+void oracle_gated_rmsnorm(int64_t rows, int64_t Cch, int64_t G, const double *y, const double *z,
+                          const double *w, double eps, double *out) {
+    const int64_t S = Cch / G;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t gi = 0; gi < G; ++gi) {
+            const int64_t o = r * Cch + gi * S;
+            double ms = 0.0;
+            for (int64_t i = 0; i < S; ++i) {
+                const double g = y[o + i] * silu64(z[o + i]);
+                ms += g * g;
+            }
+            const double rs = 1.0 / sqrt(ms / (double)S + eps);
+            for (int64_t i = 0; i < S; ++i) out[o + i] = y[o + i] * silu64(z[o + i]) * rs * w[gi * S + i];
+        }
+}
+
+/* n = g r;  dw[c] = sum over rows of dout n;  dn = dout w;
+ * dg = r (dn - n mean_group(dn n));  dy = dg SiLU(z);  dz = dg y SiLU'(z). */
+void oracle_gated_rmsnorm_bwd(int64_t rows, int64_t Cch, int64_t G, const double *y,
+                              const double *z, const double *w, double eps, const double *dout,
+                              double *dy, double *dz, double *dw) {
+    const int64_t S = Cch / G;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t gi = 0; gi < G; ++gi) {
+            const int64_t o = r * Cch + gi * S;
+            double ms = 0.0;
+            for (int64_t i = 0; i < S; ++i) {
+                const double g = y[o + i] * silu64(z[o + i]);
+                ms += g * g;
+            }
+            const double rs = 1.0 / sqrt(ms / (double)S + eps);
+            double m = 0.0;
+            for (int64_t i = 0; i < S; ++i) {
+                const double n = y[o + i] * silu64(z[o + i]) * rs;
+                m += dout[o + i] * w[gi * S + i] * n;
+            }
+            m /= (double)S;
+            for (int64_t i = 0; i < S; ++i) {
+                const double n = y[o + i] * silu64(z[o + i]) * rs;
+                const double dg = rs * (dout[o + i] * w[gi * S + i] - n * m);
+                dy[o + i] = dg * silu64(z[o + i]);
+                dz[o + i] = dg * y[o + i] * silu_grad64(z[o + i]);
+            }
+        }
+    for (int64_t c = 0; c < Cch; ++c) dw[c] = 0.0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t gi = 0; gi < G; ++gi) {
+            const int64_t o = r * Cch + gi * S;
+            double ms = 0.0;
+            for (int64_t i = 0; i < S; ++i) {
+                const double g = y[o + i] * silu64(z[o + i]);
+                ms += g * g;
+            }
+            const double rs = 1.0 / sqrt(ms / (double)S + eps);
+            for (int64_t i = 0; i < S; ++i) dw[gi * S + i] += dout[o + i] * y[o + i] * silu64(z[o + i]) * rs;
+        }
+}
