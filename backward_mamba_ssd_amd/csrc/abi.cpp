@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <climits>
+#include <cmath>
 #include <cstring>
 #include <atomic>
 #include <initializer_list>
@@ -129,6 +130,34 @@ ssm_status check_dt_prep_dims(const ssm_dims *d, float lo, float hi) {
 
 size_t dt_prep_ws_bytes(const ssm_dims *d) {
     return round_up(static_cast<size_t>(dt_prep_row_tiles(d->batch * d->seqlen)) * d->nheads * sizeof(double));
+}
+
+bool conv_sizes_ok(int64_t batch, int64_t seqlen, int64_t channels, int64_t width) {
+    return batch >= 0 && batch <= 65535 && seqlen >= 0 && seqlen <= (int64_t(1) << 36) &&
+           channels >= 4 && channels % 4 == 0 && channels <= (int64_t(1) << 32) && width >= 1 &&
+           width <= 8;
+}
+
+size_t conv_ws_bytes(int64_t batch, int64_t seqlen, int64_t channels, int64_t width) {
+    return round_up(static_cast<size_t>(batch) * conv_bwd_tiles(seqlen) * (width + 1) * channels *
+                    sizeof(double));
+}
+
+bool norm_sizes_ok(int64_t rows, int64_t channels, int64_t ngroups) {
+    if (rows < 0 || rows > INT32_MAX || channels < 1 || ngroups < 1 || ngroups > 65535) return false;
+    if (channels % ngroups != 0) return false;
+    const int64_t S = channels / ngroups;
+    return S % 8 == 0 && S <= 8192;
+}
+
+size_t norm_ws_bytes(int64_t rows, int64_t channels) {
+    return round_up(static_cast<size_t>(norm_row_tiles(rows)) * channels * sizeof(double));
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b) return false;
+    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+    return x < y + nb && y < x + na;
 }
 
 hipError_t fill(float *p, int64_t n, hipStream_t s) { return launch_fill(p, n, 0.f, s); }
@@ -493,6 +522,113 @@ ssm_status ssm_rollback(const ssm_dims *d, const float *snapshots, const int32_t
     a.Bsz = d->batch; a.per_seq = per_seq; a.ndraft = d->seqlen;
     a.snap = snapshots; a.accepted = accepted; a.state_out = state_out; a.err = err;
     return launch_rollback(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_conv1d_silu(int64_t batch, int64_t seqlen, int64_t channels, int64_t width,
+                           ssm_dtype dtype, const void *u, const float *w, const float *bias,
+                           const void *conv_init, void *out, void *conv_final,
+                           ssm_stream stream) {
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (!conv_sizes_ok(batch, seqlen, channels, width)) return SSM_ERR_DIMS;
+    if (!w || !bias) return SSM_ERR_NULL;
+    if (batch > 0 && seqlen > 0 && (!u || !out)) return SSM_ERR_NULL;
+    if (!aligned(u, 16) || !aligned(out, 16) || !aligned(bias, 16) || !aligned(conv_init, 16) ||
+        !aligned(conv_final, 16) || !aligned(w, 4))
+        return SSM_ERR_ALIGN;
+    const size_t es = esize(dtype);
+    const size_t nout = static_cast<size_t>(batch) * seqlen * channels * es;
+    const size_t ninit = static_cast<size_t>(batch) * (width - 1) * channels * es;
+    if (overlaps(out, nout, u, nout) || overlaps(out, nout, conv_init, ninit)) return SSM_ERR_DIMS;
+    ConvArgs a{};
+    a.Bsz = batch; a.T = seqlen; a.C = channels; a.K = static_cast<int>(width);
+    a.u = u; a.init = conv_init; a.w = w; a.bias = bias; a.out = out; a.final_state = conv_final;
+    return launch_conv(a, dtype == SSM_BF16, false, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSM_OK
+               : SSM_ERR_HIP;
+}
+
+size_t ssm_conv1d_silu_workspace_bytes(int64_t batch, int64_t seqlen, int64_t channels,
+                                       int64_t width) {
+    if (!conv_sizes_ok(batch, seqlen, channels, width)) return static_cast<size_t>(-1);
+    return conv_ws_bytes(batch, seqlen, channels, width);
+}
+
+ssm_status ssm_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t channels, int64_t width,
+                               ssm_dtype dtype, const void *u, const float *w, const float *bias,
+                               const void *conv_init, const void *dout, void *du, float *dw,
+                               float *dbias, void *dconv_init, void *workspace, size_t ws_bytes,
+                               ssm_stream stream) {
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (!conv_sizes_ok(batch, seqlen, channels, width)) return SSM_ERR_DIMS;
+    if (!w || !bias || !dw || !dbias) return SSM_ERR_NULL;
+    if (batch > 0 && seqlen > 0 && (!u || !dout || !du)) return SSM_ERR_NULL;
+    if (!aligned(u, 16) || !aligned(dout, 16) || !aligned(du, 16) || !aligned(bias, 16) ||
+        !aligned(conv_init, 16) || !aligned(dconv_init, 16) || !aligned(workspace, 16) ||
+        !aligned(w, 4) || !aligned(dw, 4) || !aligned(dbias, 4))
+        return SSM_ERR_ALIGN;
+    const size_t need = conv_ws_bytes(batch, seqlen, channels, width);
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return SSM_ERR_WORKSPACE;
+    const size_t es = esize(dtype);
+    const size_t nrow = static_cast<size_t>(batch) * seqlen * channels * es;
+    if (overlaps(du, nrow, u, nrow) || overlaps(du, nrow, dout, nrow)) return SSM_ERR_DIMS;
+    ConvArgs a{};
+    a.Bsz = batch; a.T = seqlen; a.C = channels; a.K = static_cast<int>(width);
+    a.ntiles = conv_bwd_tiles(seqlen);
+    a.u = u; a.init = conv_init; a.w = w; a.bias = bias; a.dout = dout; a.du = du;
+    a.dinit = dconv_init; a.dw = dw; a.dbias = dbias; a.part = static_cast<double *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (batch == 0 || seqlen == 0) {  // no tokens: zero parameter gradients and dconv_init
+        if (fill(dw, channels * width, s) != hipSuccess || fill(dbias, channels, s) != hipSuccess)
+            return SSM_ERR_HIP;
+        if (dconv_init && batch > 0 && width > 1) {
+            // a float fill covers the bytes of either storage dtype (zero bits are zero)
+            const int64_t nbytes = batch * (width - 1) * channels * static_cast<int64_t>(es);
+            if (fill(static_cast<float *>(dconv_init), nbytes / 4, s) != hipSuccess) return SSM_ERR_HIP;
+        }
+        return SSM_OK;
+    }
+    return launch_conv(a, dtype == SSM_BF16, true, s) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status ssm_gated_rmsnorm(int64_t rows, int64_t channels, int64_t ngroups, ssm_dtype dtype,
+                             const void *y, const void *z, const float *w, float eps, void *out,
+                             ssm_stream stream) {
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (!norm_sizes_ok(rows, channels, ngroups) || !(eps >= 0.f) || eps == INFINITY)
+        return SSM_ERR_DIMS;
+    if (!w || (rows > 0 && (!y || !z || !out))) return SSM_ERR_NULL;
+    if (!aligned(y, 16) || !aligned(z, 16) || !aligned(w, 16) || !aligned(out, 16)) return SSM_ERR_ALIGN;
+    NormArgs a{};
+    a.rows = rows; a.C = channels; a.G = ngroups; a.eps = eps; a.y = y; a.z = z; a.w = w; a.out = out;
+    return launch_norm(a, dtype == SSM_BF16, false, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSM_OK
+               : SSM_ERR_HIP;
+}
+
+size_t ssm_gated_rmsnorm_workspace_bytes(int64_t rows, int64_t channels, int64_t ngroups) {
+    if (!norm_sizes_ok(rows, channels, ngroups)) return static_cast<size_t>(-1);
+    return norm_ws_bytes(rows, channels);
+}
+
+ssm_status ssm_gated_rmsnorm_bwd(int64_t rows, int64_t channels, int64_t ngroups,
+                                 ssm_dtype dtype, const void *y, const void *z, const float *w,
+                                 float eps, const void *dout, void *dy, void *dz, float *dw,
+                                 void *workspace, size_t ws_bytes, ssm_stream stream) {
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (!norm_sizes_ok(rows, channels, ngroups) || !(eps >= 0.f) || eps == INFINITY)
+        return SSM_ERR_DIMS;
+    if (!w || !dw || (rows > 0 && (!y || !z || !dout || !dy || !dz))) return SSM_ERR_NULL;
+    if (!aligned(y, 16) || !aligned(z, 16) || !aligned(w, 16) || !aligned(dout, 16) ||
+        !aligned(dy, 16) || !aligned(dz, 16) || !aligned(dw, 4) || !aligned(workspace, 16))
+        return SSM_ERR_ALIGN;
+    const size_t need = norm_ws_bytes(rows, channels);
+    if (need > 0 && (workspace == nullptr || ws_bytes < need)) return SSM_ERR_WORKSPACE;
+    NormArgs a{};
+    a.rows = rows; a.C = channels; a.G = ngroups; a.eps = eps; a.y = y; a.z = z; a.w = w;
+    a.dout = dout; a.dy = dy; a.dz = dz; a.dw = dw; a.part = static_cast<double *>(workspace);
+    return launch_norm(a, dtype == SSM_BF16, true, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SSM_OK
+               : SSM_ERR_HIP;
 }
 
 }  // extern "C"

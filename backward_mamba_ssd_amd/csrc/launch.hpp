@@ -103,6 +103,33 @@ struct DtPrepArgs {
     double *part;                           // [row tiles][H] fp64 bias partials
 };
 
+// Causal depthwise convolution + SiLU (forward and backward share one block).
+struct ConvArgs {
+    int64_t Bsz, T, C;
+    int K;                    // taps, 1..8
+    int64_t ntiles;           // backward token tiles per sequence
+    const void *u, *init;     // [Bsz][T][C], [Bsz][K-1][C] or nullptr (storage dtype)
+    const float *w, *bias;    // [C][K], [C]
+    void *out, *final_state;  // [Bsz][T][C], [Bsz][K-1][C] or nullptr
+    const void *dout;         // backward: [Bsz][T][C]
+    void *du, *dinit;         // [Bsz][T][C], [Bsz][K-1][C] or nullptr
+    float *dw, *dbias;        // [C][K], [C]
+    double *part;             // [Bsz*ntiles][K+1][C] fp64 partials
+};
+
+// SiLU-gated group RMSNorm.
+struct NormArgs {
+    int64_t rows, C, G;
+    float eps;
+    const void *y, *z;   // [rows][C] (storage dtype)
+    const float *w;      // [C]
+    void *out;           // [rows][C]
+    const void *dout;    // backward
+    void *dy, *dz;
+    float *dw;
+    double *part;        // [row tiles][C] fp64 partials
+};
+
 hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);  // state or state16
@@ -115,6 +142,10 @@ hipError_t launch_sr16(const Sr16Args &a, hipStream_t s);
 hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s);
 hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s);
 int64_t dt_prep_row_tiles(int64_t rows);
+int64_t conv_bwd_tiles(int64_t T);
+int64_t norm_row_tiles(int64_t rows);
+hipError_t launch_conv(const ConvArgs &a, bool bf16, bool bwd, hipStream_t s);
+hipError_t launch_norm(const NormArgs &a, bool bf16, bool bwd, hipStream_t s);
 hipError_t launch_dt_prep(const DtPrepArgs &a, hipStream_t s);
 hipError_t launch_dt_prep_bwd(const DtPrepArgs &a, hipStream_t s);
 

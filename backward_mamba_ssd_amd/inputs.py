@@ -8,6 +8,8 @@ Distributions (one recipe for every workload):
   time-step preparation inputs: dt_raw ~ N(0, 0.25), dt_bias ~ N(-2, 0.01) per
   head (so dt_raw + dt_bias matches the N(-2, 0.5) spread below), logA ~ U(0, ln 16);
   upstream ddt, dA ~ N(0, 1);
+  stages around the scan: conv input, initial samples, gate z, upstream dout ~ N(0, 1);
+  conv weights [channels, K] ~ N(0, 1/K), conv bias ~ N(0, 0.01), norm scale ~ N(1, 0.01);
   x ~ N(0, 1); B, C ~ N(0, 1/N); dt = softplus(N(-2, 0.5)) (positive, float32);
   A = -exp(U(0, ln 16)) per head (float32); D ~ N(0, 1) per head (float32);
   dy ~ N(0, 1); optional h0 / dh_final ~ N(0, 1) (float32).
@@ -28,7 +30,9 @@ from dataclasses import dataclass, field
 import torch
 
 TENSOR_IDS = {"x": 1, "B": 2, "C": 3, "dt": 4, "A": 5, "D": 6, "dy": 7, "h0": 8,
-              "dh_final": 9, "dt_raw": 10, "dt_bias": 11, "logA": 12, "ddt": 13, "dA": 14}
+              "dh_final": 9, "dt_raw": 10, "dt_bias": 11, "logA": 12, "ddt": 13, "dA": 14,
+              "conv_u": 15, "conv_w": 16, "conv_b": 17, "conv_init": 18, "gate_z": 19,
+              "norm_w": 20, "dout": 21}
 
 
 @dataclass(frozen=True)
@@ -97,8 +101,14 @@ def draw(name, shape, seed, device="cpu", dtype=torch.float32, dstate=None):
         v = -2.0 + 0.1 * _randn(shape, s, device)
     elif name == "logA":     # A = -exp(logA) = -exp(U(0, ln 16)) as above
         v = _rand(shape, s, device) * math.log(16.0)
-    elif name in ("ddt", "dA"):
+    elif name in ("ddt", "dA", "conv_u", "conv_init", "gate_z", "dout"):
         v = _randn(shape, s, device)
+    elif name == "conv_w":   # [channels, K]: N(0, 1/K), a unit-gain filter on average
+        v = _randn(shape, s, device) / math.sqrt(shape[-1])
+    elif name == "conv_b":
+        v = 0.1 * _randn(shape, s, device)
+    elif name == "norm_w":
+        v = 1.0 + 0.1 * _randn(shape, s, device)
     else:
         raise KeyError(name)
     return v.to(dtype).contiguous()

@@ -23,7 +23,9 @@ _SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_decode_step", "ssm_decode_step_sr16",
            "ssm_checkpoint_sr16",
-           "ssm_replay", "ssm_draft_snapshots", "ssm_rollback", "ssm_dt_prep", "ssm_dt_prep_bwd", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path",
+           "ssm_replay", "ssm_draft_snapshots", "ssm_rollback", "ssm_conv1d_silu",
+           "ssm_conv1d_silu_bwd", "ssm_conv1d_silu_workspace_bytes", "ssm_gated_rmsnorm",
+           "ssm_gated_rmsnorm_bwd", "ssm_gated_rmsnorm_workspace_bytes", "ssm_dt_prep", "ssm_dt_prep_bwd", "ssm_workspace_bytes", "ssm_status_string", "ssm_uses_mfma_path",
            "ssm_profile_next_bwd_block")
 
 
@@ -46,6 +48,7 @@ def _load():
     vp, sz, i64, u64, i32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_uint64,
                              ctypes.c_int)
     D = ctypes.POINTER(ssm_dims)
+    f32 = ctypes.c_float
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_workspace_bytes.argtypes = [D, i32, i32, i64]
@@ -65,7 +68,18 @@ def _load():
     lib.ssm_replay.argtypes = ([D, i32, vp, i32, vp] + [vp] * 6 + [i64, i64] + [vp] * 4
                                + [vp, sz, vp])
     lib.ssm_replay.restype = i32
-    f32 = ctypes.c_float
+    lib.ssm_conv1d_silu.argtypes = [i64] * 4 + [i32] + [vp] * 7
+    lib.ssm_conv1d_silu.restype = i32
+    lib.ssm_conv1d_silu_workspace_bytes.argtypes = [i64] * 4
+    lib.ssm_conv1d_silu_workspace_bytes.restype = sz
+    lib.ssm_conv1d_silu_bwd.argtypes = [i64] * 4 + [i32] + [vp] * 10 + [sz, vp]
+    lib.ssm_conv1d_silu_bwd.restype = i32
+    lib.ssm_gated_rmsnorm.argtypes = [i64] * 3 + [i32] + [vp] * 3 + [f32, vp, vp]
+    lib.ssm_gated_rmsnorm.restype = i32
+    lib.ssm_gated_rmsnorm_workspace_bytes.argtypes = [i64] * 3
+    lib.ssm_gated_rmsnorm_workspace_bytes.restype = sz
+    lib.ssm_gated_rmsnorm_bwd.argtypes = [i64] * 3 + [i32] + [vp] * 3 + [f32] + [vp] * 5 + [sz, vp]
+    lib.ssm_gated_rmsnorm_bwd.restype = i32
     lib.ssm_draft_snapshots.argtypes = [D, i32] + [vp] * 8 + [vp]
     lib.ssm_draft_snapshots.restype = i32
     lib.ssm_rollback.argtypes = [D, vp, vp, vp, vp, vp]
@@ -347,3 +361,67 @@ def ssm_rollback(snapshots, accepted, state_out=None, err=None, stream=None):
                            _ptr(err), _stream(stream))
     _check(st, "ssm_rollback")
     return state_out
+
+
+def ssm_conv1d_silu(u, w, bias, conv_init=None, out=None, conv_final=True, stream=None):
+    """SiLU of the short causal depthwise convolution.  u [batch, T, C] (fp32 or
+    bf16), w [C, K], bias [C] float32, conv_init [batch, K-1, C] or None.
+    Returns (out [batch, T, C], conv_final [batch, K-1, C] or None)."""
+    b, t, c = u.shape
+    k = w.shape[1]
+    if out is None:
+        out = torch.empty_like(u)
+    fin = (torch.empty((b, k - 1, c), dtype=u.dtype, device=u.device) if conv_final is True
+           else (conv_final if isinstance(conv_final, torch.Tensor) else None))
+    st = _lib.ssm_conv1d_silu(b, t, c, k, _dtype_code(u), _ptr(u), _ptr(w), _ptr(bias),
+                              _ptr(conv_init), _ptr(out), _ptr(fin), _stream(stream))
+    _check(st, "ssm_conv1d_silu")
+    return out, fin
+
+
+def ssm_conv1d_silu_bwd(u, w, bias, dout, conv_init=None, want_dinit=True, workspace=None,
+                        stream=None):
+    """Gradients of sum(dout * out): dict du, dw, dbias, dconv_init."""
+    b, t, c = u.shape
+    k = w.shape[1]
+    g = {"du": torch.empty_like(u), "dw": torch.empty_like(w), "dbias": torch.empty_like(bias),
+         "dconv_init": (torch.empty((b, k - 1, c), dtype=u.dtype, device=u.device)
+                        if want_dinit else None)}
+    need = _lib.ssm_conv1d_silu_workspace_bytes(b, t, c, k)
+    if need == _SIZE_MAX:
+        raise SsmError(2, "ssm_conv1d_silu_workspace_bytes")
+    ws, wsb = _workspace(int(need), u.device, workspace)
+    st = _lib.ssm_conv1d_silu_bwd(b, t, c, k, _dtype_code(u), _ptr(u), _ptr(w), _ptr(bias),
+                                  _ptr(conv_init), _ptr(dout), _ptr(g["du"]), _ptr(g["dw"]),
+                                  _ptr(g["dbias"]), _ptr(g["dconv_init"]), _ptr(ws), wsb,
+                                  _stream(stream))
+    _check(st, "ssm_conv1d_silu_bwd")
+    return g
+
+
+def ssm_gated_rmsnorm(y, z, w, ngroups, eps=1e-5, out=None, stream=None):
+    """out = y*SiLU(z) / rms over groups of C/ngroups channels * w.  y, z [..., C]."""
+    c = y.shape[-1]
+    rows = y.numel() // c if c else 0
+    if out is None:
+        out = torch.empty_like(y)
+    st = _lib.ssm_gated_rmsnorm(rows, c, ngroups, _dtype_code(y), _ptr(y), _ptr(z), _ptr(w),
+                                float(eps), _ptr(out), _stream(stream))
+    _check(st, "ssm_gated_rmsnorm")
+    return out
+
+
+def ssm_gated_rmsnorm_bwd(y, z, w, dout, ngroups, eps=1e-5, workspace=None, stream=None):
+    """Gradients of sum(dout * out): dict dy, dz, dw."""
+    c = y.shape[-1]
+    rows = y.numel() // c if c else 0
+    g = {"dy": torch.empty_like(y), "dz": torch.empty_like(z), "dw": torch.empty_like(w)}
+    need = _lib.ssm_gated_rmsnorm_workspace_bytes(rows, c, ngroups)
+    if need == _SIZE_MAX:
+        raise SsmError(2, "ssm_gated_rmsnorm_workspace_bytes")
+    ws, wsb = _workspace(int(need), y.device, workspace)
+    st = _lib.ssm_gated_rmsnorm_bwd(rows, c, ngroups, _dtype_code(y), _ptr(y), _ptr(z), _ptr(w),
+                                    float(eps), _ptr(dout), _ptr(g["dy"]), _ptr(g["dz"]),
+                                    _ptr(g["dw"]), _ptr(ws), wsb, _stream(stream))
+    _check(st, "ssm_gated_rmsnorm_bwd")
+    return g

@@ -396,6 +396,66 @@ def draft_rollback_rates(dev, layers=8, ndraft=4):
     return res
 
 
+def around_scan_rates(dev):
+    """The stages around the scan at the prefill layer's size (batch 4 x 4096 tokens):
+    the causal conv1d + SiLU over 18,432 channels (256 heads x 64 + 2 x 8 groups x 128),
+    4 taps, and the gated RMSNorm over 16,384 channels in 8 groups, bf16 storage.
+    Bytes: conv forward u read + out written (4 B per element), backward u, dout read +
+    du written (6 B); norm forward y, z read + out written (6 B), backward y, z, dout
+    read + dy, dz written (10 B).  Parameter partials are not counted."""
+    import torch
+
+    from backward_mamba_ssd_amd import inputs, ssm
+
+    b, t, k = 4, 4096, 4
+    c = 256 * 64 + 2 * 8 * 128
+    seed = 9000
+    bf = torch.bfloat16
+    u = inputs.draw("conv_u", (b, t, c), seed, dev, bf)
+    w = inputs.draw("conv_w", (c, k), seed, dev)
+    bias = inputs.draw("conv_b", (c,), seed, dev)
+    dout = inputs.draw("dout", (b, t, c), seed, dev, bf)
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = torch.empty_like(u)
+    n = u.numel()
+    res["conv_fwd"] = path_entry(0, 4 * n, timed(lambda: ssm.ssm_conv1d_silu(u, w, bias, out=out,
+                                                                               conv_final=None)))
+    ws = torch.empty(ssm.lib().ssm_conv1d_silu_workspace_bytes(b, t, c, k), dtype=torch.uint8,
+                     device=dev)
+    res["conv_bwd"] = path_entry(0, 6 * n, timed(lambda: ssm.ssm_conv1d_silu_bwd(
+        u, w, bias, dout, want_dinit=False, workspace=ws)))
+    del u, dout, out, ws
+    rows, cn, g = b * t, 256 * 64, 8
+    y = inputs.draw("conv_u", (rows, cn), seed, dev, bf)
+    z = inputs.draw("gate_z", (rows, cn), seed, dev, bf)
+    nw = inputs.draw("norm_w", (cn,), seed, dev)
+    do = inputs.draw("dout", (rows, cn), seed, dev, bf)
+    o = torch.empty_like(y)
+    m = y.numel()
+    res["norm_fwd"] = path_entry(0, 6 * m, timed(lambda: ssm.ssm_gated_rmsnorm(y, z, nw, g, out=o)))
+    ws = torch.empty(ssm.lib().ssm_gated_rmsnorm_workspace_bytes(rows, cn, g), dtype=torch.uint8,
+                     device=dev)
+    res["norm_bwd"] = path_entry(0, 10 * m, timed(lambda: ssm.ssm_gated_rmsnorm_bwd(
+        y, z, nw, do, g, workspace=ws)))
+    res["shape"] = (f"conv: batch {b} x {t} tokens x {c} channels, {k} taps; norm: {rows} rows x "
+                    f"{cn} channels, {g} groups; bf16 storage")
+    del y, z, do, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def secondary(dev):
     """Decode (full 64 x 48 x 100 workload), SR16 and replay rates."""
     import torch
@@ -467,6 +527,7 @@ def secondary(dev):
     torch.cuda.empty_cache()
     out["dt_prep"] = dt_prep_rates(dev)
     out["draft_rollback"] = draft_rollback_rates(dev)
+    out["around_scan"] = around_scan_rates(dev)
     log("replay sweep ...")
     out["replay_sr16_b16"] = replay_sweep(dev)
     wl = inputs.WORKLOADS["long_b1_t131072"]

@@ -238,6 +238,81 @@ ssm_status ssm_rollback(const ssm_dims *d, const float *snapshots, const int32_t
                         float *state_out, int32_t *err, ssm_stream stream);
 
 /*
+ * Short causal depthwise convolution followed by SiLU, the stage before the
+ * scan.  "Nemotron Kernels: From Inference To Backpropagation", Kernel 1
+ * "Forward And Inference" (the hidden stream passes a causal Conv1D + SiLU; an
+ * output reads the present and past samples of its channel, never a future
+ * one; the decode kernel applies SiLU to the convolution sum).  Per batch b and
+ * channel c with `width` = K taps and the K-1 samples before token 0 taken from
+ * conv_init (zero when NULL):
+ *   v[t]   = bias[c] + sum_{k<K} w[c][k] * ext[t+k],  ext = (conv_init, u)
+ *   out[t] = v[t] * sigmoid(v[t])
+ * Layouts: u, out [batch][seqlen][channels] (dtype); w [channels][K] float;
+ * bias [channels] float; conv_init, conv_final [batch][K-1][channels] (dtype).
+ * conv_final (may be NULL) receives the last K-1 samples of (conv_init, u): the
+ * conv_init of the next call (seqlen = 1 is the decode step).
+ * Constraints: 1 <= width <= 8; channels a positive multiple of 4; batch <=
+ * 65535; u, out, bias, conv_init, conv_final 16-byte aligned, w 4-byte aligned.
+ * out must not overlap u or conv_init.
+ */
+ssm_status ssm_conv1d_silu(int64_t batch, int64_t seqlen, int64_t channels, int64_t width,
+                           ssm_dtype dtype, const void *u, const float *w, const float *bias,
+                           const void *conv_init, void *out, void *conv_final,
+                           ssm_stream stream);
+
+/* Workspace bytes of ssm_conv1d_silu_bwd ((size_t)-1 for invalid sizes). */
+size_t ssm_conv1d_silu_workspace_bytes(int64_t batch, int64_t seqlen, int64_t channels,
+                                       int64_t width);
+
+/*
+ * Backward of ssm_conv1d_silu (same page, section "What Conv1D Gives The Mamba
+ * Block": the SiLU derivative first, then each output gradient reaches the
+ * inputs of its window, the weights that touched them and the bias; overlapping
+ * windows add at one input).  With dv = dout * SiLU'(v):
+ *   du[t] = sum_k w[c][k] dv[t+K-1-k];  dw[c][k] = sum_{b,t} dv[t] ext[t+k];
+ *   dbias[c] = sum_{b,t} dv[t];  dconv_init[j] = sum_{k<=j} w[c][k] dv[j-k]
+ * du, dconv_init (NULL to skip) in dtype; dw [channels][K], dbias float (fp64
+ * partial sums in a fixed order).  Same layouts and constraints as the forward.
+ */
+ssm_status ssm_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t channels, int64_t width,
+                               ssm_dtype dtype, const void *u, const float *w, const float *bias,
+                               const void *conv_init, const void *dout, void *du, float *dw,
+                               float *dbias, void *dconv_init, void *workspace, size_t ws_bytes,
+                               ssm_stream stream);
+
+/*
+ * SiLU-gated group RMSNorm, the stage after the scan.  Same page, Kernel 1
+ * pipeline ("selective scan -> gated group RMSNorm") and section "From
+ * Classical State Space To A Selective Mamba State" (a learned SiLU gate
+ * controls how much signal passes).  Over groups of S = channels/ngroups
+ * consecutive channels of each row:
+ *   g = y * SiLU(z);  out = g / sqrt(mean_group(g^2) + eps) * w[c]
+ * Layouts: y, z, out [rows][channels] (dtype); w [channels] float.
+ * Constraints: S a multiple of 8 and at most 8192; rows < 2^31; ngroups <=
+ * 65535; eps >= 0 and finite (with eps = 0 an all-zero group divides by zero);
+ * all pointers 16-byte aligned.
+ */
+ssm_status ssm_gated_rmsnorm(int64_t rows, int64_t channels, int64_t ngroups, ssm_dtype dtype,
+                             const void *y, const void *z, const float *w, float eps, void *out,
+                             ssm_stream stream);
+
+/* Workspace bytes of ssm_gated_rmsnorm_bwd ((size_t)-1 for invalid sizes). */
+size_t ssm_gated_rmsnorm_workspace_bytes(int64_t rows, int64_t channels, int64_t ngroups);
+
+/*
+ * Backward of ssm_gated_rmsnorm (the page's RMSNorm remark: the backward needs
+ * the input, the learned scale, the inverse RMS and the reduction).  With
+ * r = 1/sqrt(mean_group(g^2) + eps), n = g r, dn = dout w:
+ *   dg = r (dn - n mean_group(dn n));  dy = dg SiLU(z);  dz = dg y SiLU'(z)
+ *   dw[c] = sum over rows of dout n   (fp64 partial sums, fixed order)
+ * dy, dz in dtype; dw float.  The inverse RMS is recomputed from y and z.
+ */
+ssm_status ssm_gated_rmsnorm_bwd(int64_t rows, int64_t channels, int64_t ngroups,
+                                 ssm_dtype dtype, const void *y, const void *z, const float *w,
+                                 float eps, const void *dout, void *dy, void *dz, float *dw,
+                                 void *workspace, size_t ws_bytes, ssm_stream stream);
+
+/*
  * Time-step and rate preparation.  "Nemotron Kernels: From Inference To
  * Backpropagation", section "From Classical State Space To A Selective Mamba
  * State" (the time step goes through softplus and is clamped to a configured

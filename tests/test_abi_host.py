@@ -221,3 +221,47 @@ def test_draft_and_rollback_reject_bad_calls_before_any_work():
     assert rb(d, out=FAKE + slot // 2) == DIMS          # straddles two slots
     assert rb(d, out=FAKE - slot // 2) == DIMS          # overlaps slot 0 from below
     assert rb(dims(batch=0)) == OK                        # nothing to do
+
+
+def test_conv_and_norm_reject_bad_calls_before_any_work():
+    L = ssm.lib()
+    B16, F32 = ssm.SSM_BF16, ssm.SSM_F32
+
+    def conv(b=2, t=10, c=16, k=4, dtype=B16, u=FAKE, w=FAKE, bias=FAKE, init=None,
+             out=FAKE + (1 << 30), fin=None):
+        return L.ssm_conv1d_silu(b, t, c, k, dtype, u, w, bias, init, out, fin, None)
+
+    assert conv(dtype=7) == DTYPE
+    assert conv(k=0) == DIMS and conv(k=9) == DIMS and conv(c=6) == DIMS and conv(b=70000) == DIMS
+    assert conv(u=None) == NULL and conv(w=None) == NULL and conv(bias=None) == NULL
+    assert conv(out=FAKE + 8) == ALIGN and conv(bias=FAKE + 4) == ALIGN
+    assert conv(out=FAKE + 64) == DIMS  # overlaps the input
+    need = L.ssm_conv1d_silu_workspace_bytes(2, 600, 16, 4)
+    assert need == 2 * 3 * 5 * 16 * 8  # 3 tiles of 256 tokens, K + 1 partial rows
+    assert L.ssm_conv1d_silu_workspace_bytes(2, 600, 16, 9) == ctypes.c_size_t(-1).value
+
+    def conv_bwd(ws=None, wsb=0, **kw):
+        a = dict(u=FAKE, w=FAKE, bias=FAKE, init=None, dout=FAKE + (2 << 30), du=FAKE + (1 << 30),
+                 dw=FAKE, dbias=FAKE, dinit=None)
+        a.update(kw)
+        return L.ssm_conv1d_silu_bwd(2, 600, 16, 4, B16, a["u"], a["w"], a["bias"], a["init"],
+                                     a["dout"], a["du"], a["dw"], a["dbias"], a["dinit"], ws, wsb,
+                                     None)
+
+    assert conv_bwd() == WS and conv_bwd(ws=FAKE, wsb=need - 8) == WS
+    assert conv_bwd(ws=FAKE, wsb=need, dw=None) == NULL
+    assert conv_bwd(ws=FAKE, wsb=need, du=FAKE) == DIMS  # du overlaps u
+
+    def norm(rows=8, c=64, g=4, eps=1e-5, dtype=F32, y=FAKE, z=FAKE, w=FAKE, out=FAKE):
+        return L.ssm_gated_rmsnorm(rows, c, g, dtype, y, z, w, eps, out, None)
+
+    assert norm(c=60) == DIMS          # 60 / 4 = 15 channels per group, not a multiple of 8
+    assert norm(c=64, g=3) == DIMS     # groups do not divide the channels
+    assert norm(c=2 * 8200, g=2) == DIMS  # group wider than 8192
+    assert norm(eps=-1.0) == DIMS and norm(eps=float("nan")) == DIMS and norm(eps=float("inf")) == DIMS
+    assert norm(y=None) == NULL and norm(w=None) == NULL
+    assert norm(out=FAKE + 4) == ALIGN
+    nneed = L.ssm_gated_rmsnorm_workspace_bytes(100, 64, 4)
+    assert nneed == 4 * 64 * 8  # 4 tiles of 32 rows
+    assert L.ssm_gated_rmsnorm_bwd(100, 64, 4, F32, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE,
+                                   FAKE, None, 0, None) == WS
