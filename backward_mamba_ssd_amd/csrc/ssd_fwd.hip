@@ -24,9 +24,12 @@
 // the state once per saved chunk.  chunk_states[c] (state entering chunk c)
 // is stored whenever a block starts a chunk of L tokens (L % 64 == 0).
 //
-// One 256-thread workgroup (4 waves) per (batch, head); workgroup ids are
-// remapped so the heads of one group run on the same XCD and share B/C in
-// that XCD's L2.
+// One 512-thread workgroup (8 waves) per (batch, head), two per CU (LDS 71 KB,
+// at most 128 VGPRs: 16 waves per CU to hide the latency of the serial block
+// loop).  Wave w holds n-tile w of the state for all four p-tiles; the 10 causal
+// Gram tiles are spread so no wave computes more than two; each wave computes
+// two output tiles.  Workgroup ids are remapped so the heads of one group run on
+// the same XCD and share B/C in that XCD's L2.
 //
 // MFMA tiles follow the "NT" convention of ssd_common.hpp.
 #include "common.hpp"
@@ -45,47 +48,42 @@ struct __align__(16) FwdSmem {
     float2 ld[2][kLs];        // (Lam, dt) per token, double-buffered by block parity
 };
 
-__global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
+__global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     FwdSmem &sm = *reinterpret_cast<FwdSmem *>(smem_raw);
-
     const int nwg = gridDim.x;
     const int bh = xcd_remap(blockIdx.x, nwg);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int lr = lane & 15;          // operand row within a 16-row tile
-    const int lk = (lane >> 4) * 8;    // operand k offset within a 32-wide step
-    const int lq = (lane >> 4) * 4;    // accumulator row offset
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
     const int64_t T = a.T;
     const float Ah = a.A[h], Dh = a.D[h];
     const bf16_t *x = static_cast<const bf16_t *>(a.x);
     const bf16_t *Bm = static_cast<const bf16_t *>(a.B);
     const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
     bf16_t *y = static_cast<bf16_t *>(a.y);
+    const bool lowhalf = wave < 4;          // waves 0-3 stage B; waves 4-7 stage C and x
+    const int sid = tid & 255;
 
-    // state H^T in accumulators: wave w owns n-tiles 2w, 2w+1 and all 4 p-tiles;
-    // tile q: nt = 2w + q/4, pt = q%4; element v: n = 16nt + lq + v, p = 16pt + lr
-    f32x4 H[8];
+    // state H^T: wave w owns n-tile w, all 4 p-tiles: n = 16w + lq + v, p = 16pt + lr
+    f32x4 H[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+    for (int pt = 0; pt < 4; ++pt) {
+        const int n = 16 * wave + lq, p = 16 * pt + lr;
         if (a.h0 != nullptr) {
             const float4 v = *reinterpret_cast<const float4 *>(a.h0 + (static_cast<int64_t>(bh) * kP + p) * kN + n);
-            H[q] = f32x4{v.x, v.y, v.z, v.w};
+            H[pt] = f32x4{v.x, v.y, v.z, v.w};
         } else {
-            H[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            H[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-
-    // cooperative load mapping
-    const int xt0 = map64_tok(tid), xp0 = map64_col(tid);    // x: 2 tokens x 8 channels
-    const int bt0 = map128_tok(tid), bn0 = map128_col(tid);  // B, C: 4 tokens x 8 coords
-    u16x8 xr[2], br[4], cr[4];
+    const int xt0 = map64_tok(sid), xp0 = map64_col(sid);
+    const int bt0 = map128_tok(sid), bn0 = map128_col(sid);
+    u16x8 pre[6];   // low half: B rows (4); high half: C rows (4), x rows (2)
     float dtr = 0.f;
-    // Per-block buffer descriptors: offsets at or past the block's valid tokens read
-    // zero (loads) or are dropped (stores); byte offsets stay 32-bit at any T.
-    const uint32_t tokx = static_cast<uint32_t>(a.H) * kP * 2;   // bytes between tokens of x, y
-    const uint32_t tokbc = static_cast<uint32_t>(a.G) * kN * 2;  // ... of B, C
+    const uint32_t tokx = static_cast<uint32_t>(a.H) * kP * 2;
+    const uint32_t tokbc = static_cast<uint32_t>(a.G) * kN * 2;
     auto nvalid_of = [&](int64_t t0) { return static_cast<uint32_t>(T - t0 < kLs ? T - t0 : kLs); };
     auto rows_x = [&](const bf16_t *base, int64_t t0) {
         return make_rsrc(base + ((b * T + t0) * a.H + h) * kP, nvalid_of(t0) * tokx);
@@ -93,21 +91,28 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
     auto rows_bc = [&](const bf16_t *base, int64_t t0) {
         return make_rsrc(base + ((b * T + t0) * a.G + g) * kN, nvalid_of(t0) * tokbc);
     };
-
     auto prefetch = [&](int64_t t0) {
-        const rsrc_t rx = rows_x(x, t0), rb = rows_bc(Bm, t0), rc = rows_bc(Cm, t0);
+        if (lowhalf) {
+            const rsrc_t rb = rows_bc(Bm, t0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) xr[i] = buf_ld_16b(rx, (xt0 + i) * tokx + xp0 * 2);
+            for (int i = 0; i < 4; ++i) pre[i] = buf_ld_16b(rb, (bt0 + i) * tokbc + bn0 * 2);
+        } else {
+            const rsrc_t rc = rows_bc(Cm, t0), rx = rows_x(x, t0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            br[i] = buf_ld_16b(rb, (bt0 + i) * tokbc + bn0 * 2);
-            cr[i] = buf_ld_16b(rc, (bt0 + i) * tokbc + bn0 * 2);
+            for (int i = 0; i < 4; ++i) pre[i] = buf_ld_16b(rc, (bt0 + i) * tokbc + bn0 * 2);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) pre[4 + i] = buf_ld_16b(rx, (xt0 + i) * tokx + xp0 * 2);
         }
         if (tid < kLs) {
             const rsrc_t rd = make_rsrc(a.dt + (b * T + t0) * a.H + h, nvalid_of(t0) * a.H * 4u);
             dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
         }
     };
+    // Gram tile assignment (i-tile, j-tiles): every tile with j <= i once, plus the two
+    // zero tiles (0,1) and (2,3) that the output products read
+    const int gi = (wave < 2) ? 3 : (wave < 4) ? 2 : (wave < 6) ? 1 : 0;
+    const int gj0 = (wave == 0) ? 0 : (wave == 1) ? 2 : (wave == 2) ? 0 : (wave == 3) ? 2 : (wave == 4) ? 0 : (wave == 5) ? 1 : 0;
+    const int gnj = (wave <= 3) ? 2 : (wave == 6) ? 2 : (wave == 7) ? 0 : 1;  // waves 3, 6 write a zero second tile
 
     const int64_t nblk = (T + kLs - 1) / kLs;
     prefetch(0);
@@ -115,21 +120,16 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         const int64_t t0 = s * kLs;
         const int buf = static_cast<int>(s & 1);
         // (1) cumulative log-retention of the block (one wave, one token per lane)
-        if (wave == 0) {
-            sm.ld[buf][lane] = make_float2(wave_prefix_sum(dtr * Ah), dtr);
-        }
+        if (wave == 0) sm.ld[buf][lane] = make_float2(wave_prefix_sum(dtr * Ah), dtr);
         __syncthreads();
         const float2 *ld = sm.ld[buf];
         const float lam_end = ld[kLs - 1].x;
-        // (2) stage the block in LDS
+        // (2) stage the block in LDS: waves 0-3 B and Bs^T, waves 4-7 C and X^T
+        if (lowhalf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u16x8 *>(&sm.C[(bt0 + i) * kS128 + bn0]) = cr[i];
-            *reinterpret_cast<u16x8 *>(&sm.B[(bt0 + i) * kS128 + bn0]) = br[i];
-        }
-        {
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u16x8 *>(&sm.B[(bt0 + i) * kS128 + bn0]) = pre[i];
             float coef[4];
-            const float4 l01 = *reinterpret_cast<const float4 *>(&ld[bt0]);      // (Lam, dt) of 2 tokens
+            const float4 l01 = *reinterpret_cast<const float4 *>(&ld[bt0]);
             const float4 l23 = *reinterpret_cast<const float4 *>(&ld[bt0 + 2]);
             coef[0] = __expf(lam_end - l01.x) * l01.y;
             coef[1] = __expf(lam_end - l01.z) * l01.w;
@@ -138,11 +138,14 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 *reinterpret_cast<u16x4 *>(&sm.BsT[(bn0 + e) * kS64 + bt0]) =
-                    pack4(bf16_to_f32(br[0][e]) * coef[0], bf16_to_f32(br[1][e]) * coef[1],
-                          bf16_to_f32(br[2][e]) * coef[2], bf16_to_f32(br[3][e]) * coef[3]);
+                    pack4(bf16_to_f32(pre[0][e]) * coef[0], bf16_to_f32(pre[1][e]) * coef[1],
+                          bf16_to_f32(pre[2][e]) * coef[2], bf16_to_f32(pre[3][e]) * coef[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u16x8 *>(&sm.C[(bt0 + i) * kS128 + bn0]) = pre[i];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t pr = static_cast<uint32_t>(xr[0][e]) | (static_cast<uint32_t>(xr[1][e]) << 16);
+                const uint32_t pr = static_cast<uint32_t>(pre[4][e]) | (static_cast<uint32_t>(pre[5][e]) << 16);
                 *reinterpret_cast<uint32_t *>(&sm.XT[(xp0 + e) * kS64 + xt0]) = pr;
             }
         }
@@ -150,26 +153,27 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         if (a.chunk_states != nullptr && (t0 % a.L) == 0) {
             float *cs = a.chunk_states + (static_cast<int64_t>(bh) * a.nchunks + t0 / a.L) * (kP * kN);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
-                *reinterpret_cast<float4 *>(cs + p * kN + n) = make_float4(H[q][0], H[q][1], H[q][2], H[q][3]);
+            for (int pt = 0; pt < 4; ++pt) {
+                const int n = 16 * wave + lq, p = 16 * pt + lr;
+                *reinterpret_cast<float4 *>(cs + p * kN + n) = make_float4(H[pt][0], H[pt][1], H[pt][2], H[pt][3]);
             }
         }
         if (s + 1 < nblk) prefetch(t0 + kLs);
         __syncthreads();
-
-        // (3) masked, decayed Gram rows of this wave: i in [16w, 16w+16); the wave's C
-        //     fragments are read once for the four j-tiles
-        {
-            const int i = 16 * wave + lr;
+        // (3) masked, decayed Gram tiles (i-tile gi, j-tiles gj0, gj0+1); the wave's C
+        //     fragments are read once for both
+        if (gnj > 0) {
+            const int i = 16 * gi + lr;
             const float lam_i = ld[i].x;
             bf16x8 fc[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) fc[kk] = frag_row(&sm.C[i * kS128 + 32 * kk + lk]);
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
+            for (int q = 0; q < 2; ++q) {
+                if (q >= gnj) break;
+                const int jt = gj0 + q;
                 float gv[4] = {0.f, 0.f, 0.f, 0.f};
-                if (jt <= wave) {
+                if (jt <= gi) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
@@ -183,7 +187,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
                         const int j = 16 * jt + lq + v;
                         const float2 lj = ljs[v];
                         gv[v] = (j <= i) ? acc[v] * __expf(lam_i - lj.x) * lj.y : 0.f;
-                        if (j == i) gv[v] += Dh;  // skip term: Y = (Gm + D I) X
+                        if (j == i) gv[v] += Dh;
                     }
                 }
                 *reinterpret_cast<u16x4 *>(&sm.Gm[i * kS64 + 16 * jt + lq]) = pack4(gv[0], gv[1], gv[2], gv[3]);
@@ -193,23 +197,25 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
         // (4) H in bf16 over the consumed B rows: [p][n]
         bf16_t *Hb = sm.B;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
-            *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(H[q][0], H[q][1], H[q][2], H[q][3]);
+        for (int pt = 0; pt < 4; ++pt) {
+            const int n = 16 * wave + lq, p = 16 * pt + lr;
+            *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(H[pt][0], H[pt][1], H[pt][2], H[pt][3]);
         }
         __syncthreads();
-        // (5) outputs: Y^T rows p in [16w, 16w+16), 16 tokens at a time; the wave's
-        //     H and X^T fragments are read once for the four token tiles
+        // (5) outputs Y^T: p-tile (w & 3), token tiles 2*(w >> 2) + {0, 1}; the wave's H and
+        //     X^T fragments are read once for both
         {
             const rsrc_t ry = rows_x(y, t0);
-            const int prow = 16 * wave + lr;
+            const int pw = wave & 3, ih = wave >> 2;
+            const int prow = 16 * pw + lr;
             bf16x8 fh[4], fx[2];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) fh[kk] = frag_row(&Hb[prow * kS128 + 32 * kk + lk]);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) fx[kk] = frag_row(&sm.XT[prow * kS64 + 32 * kk + lk]);
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+            for (int q = 0; q < 2; ++q) {
+                const int tt = 2 * ih + q;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
@@ -219,37 +225,35 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(SsdFwdArgs a) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[v] *= el;
 #pragma unroll
-                for (int kk = 0; kk <= tt / 2; ++kk)
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (kk > ih) break;
                     acc = mfma(fx[kk], frag_row(&sm.Gm[(16 * tt + lr) * kS64 + 32 * kk + lk]), acc);
-                buf_st_8b(ry, tok * tokx + (16 * wave + lq) * 2, pack4(acc[0], acc[1], acc[2], acc[3]));
+                }
+                buf_st_8b(ry, tok * tokx + (16 * pw + lq) * 2, pack4(acc[0], acc[1], acc[2], acc[3]));
             }
         }
-        // (6) state update H^T = exp(Lam_63) H^T + Bs^T X
+        // (6) state update H^T = exp(Lam_63) H^T + Bs^T X on the wave's n-tile
         {
             const float el = __expf(lam_end);
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
+            for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) H[q][v] *= el;
-            // each of the wave's 2 Bs^T and 4 X^T fragments is read once per 32-token step
+                for (int v = 0; v < 4; ++v) H[pt][v] *= el;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 fb[2], fx[4];
+                const bf16x8 fb = frag_row(&sm.BsT[(16 * wave + lr) * kS64 + 32 * kk + lk]);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) fb[t] = frag_row(&sm.BsT[(16 * (2 * wave + t) + lr) * kS64 + 32 * kk + lk]);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) fx[t] = frag_row(&sm.XT[(16 * t + lr) * kS64 + 32 * kk + lk]);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) H[q] = mfma(fb[q / 4], fx[q % 4], H[q]);
+                for (int pt = 0; pt < 4; ++pt)
+                    H[pt] = mfma(fb, frag_row(&sm.XT[(16 * pt + lr) * kS64 + 32 * kk + lk]), H[pt]);
             }
         }
     }
     if (a.h_final != nullptr) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+        for (int pt = 0; pt < 4; ++pt) {
+            const int n = 16 * wave + lq, p = 16 * pt + lr;
             *reinterpret_cast<float4 *>(a.h_final + (static_cast<int64_t>(bh) * kP + p) * kN + n) =
-                make_float4(H[q][0], H[q][1], H[q][2], H[q][3]);
+                make_float4(H[pt][0], H[pt][1], H[pt][2], H[pt][3]);
         }
     }
 }
@@ -267,7 +271,7 @@ hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s) {
         configured = true;
     }
     const unsigned grid = static_cast<unsigned>(a.Bsz * a.H);
-    ssd_fwd_kernel<<<grid, 256, smem, s>>>(a);
+    ssd_fwd_kernel<<<grid, 512, smem, s>>>(a);
     return hipGetLastError();
 }
 
