@@ -31,9 +31,12 @@
 namespace ssm {
 namespace {
 
+// sigmoid from the hardware exp2 and reciprocal (about 1 ulp each); these
+// kernels stream memory, and the library expf and IEEE division would make the
+// activation's instruction count, not the bytes, their bound.
 __device__ __forceinline__ float sigm(float v) {
-    const float e = expf(-fabsf(v));
-    const float s = 1.f / (1.f + e);
+    const float e = __expf(-fabsf(v));
+    const float s = __builtin_amdgcn_rcpf(1.f + e);
     return v >= 0.f ? s : e * s;
 }
 __device__ __forceinline__ float silu(float v) { return v * sigm(v); }
@@ -56,6 +59,7 @@ __device__ __forceinline__ float get(const float4 &v, int i) { return i == 0 ? v
 
 constexpr int kConvFwdTile = 64;   // tokens per forward thread (window halo K-1)
 constexpr int kConvBwdTile = 256;  // tokens per backward thread (fp64 partials per tile)
+constexpr int kConvUnroll = 8;     // forward: tokens whose loads are in flight together
 
 // ---------------------------------------------------------------------------
 // convolution + SiLU, forward: thread = (batch, 4 channels, token tile)
@@ -84,82 +88,16 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvArgs a) {
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) win[j] = sample(t0 - (K - 1) + j);
     const int64_t tend = (t0 + kConvFwdTile < a.T) ? t0 + kConvFwdTile : a.T;
-    for (int64_t t = t0; t < tend; ++t) {
-        const float4 xv = ld4(u + (b * a.T + t) * a.C + c0);
-        float4 v = bias;
+    // kConvUnroll tokens at a time: all their loads are issued before the first use
+    for (int64_t tb = t0; tb < tend; tb += kConvUnroll) {
+        float4 xs[kConvUnroll];
 #pragma unroll
-        for (int k = 0; k < K - 1; ++k) {
-            v.x = fmaf(w[k].x, win[k].x, v.x);
-            v.y = fmaf(w[k].y, win[k].y, v.y);
-            v.z = fmaf(w[k].z, win[k].z, v.z);
-            v.w = fmaf(w[k].w, win[k].w, v.w);
-        }
-        v.x = fmaf(w[K - 1].x, xv.x, v.x);
-        v.y = fmaf(w[K - 1].y, xv.y, v.y);
-        v.z = fmaf(w[K - 1].z, xv.z, v.z);
-        v.w = fmaf(w[K - 1].w, xv.w, v.w);
-        st4(out + (b * a.T + t) * a.C + c0, make_float4(silu(v.x), silu(v.y), silu(v.z), silu(v.w)));
+        for (int q = 0; q < kConvUnroll; ++q)
+            xs[q] = (tb + q < tend) ? ld4(u + (b * a.T + tb + q) * a.C + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
-        if (K > 1) win[K > 1 ? K - 2 : 0] = xv;
-    }
-    // the samples the next call needs: ext[T .. T+K-2] (the tile holding the last token,
-    // or tile 0 when there are no tokens)
-    if (a.final_state != nullptr && ((t0 < a.T && tend == a.T) || (a.T == 0 && t0 == 0))) {
-        T *fin = static_cast<T *>(a.final_state);
-#pragma unroll
-        for (int j = 0; j < K - 1; ++j) st4(fin + (b * (K - 1) + j) * a.C + c0, win[j]);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// convolution + SiLU, backward: thread = (batch, 4 channels, token tile); the
-// tile's dv are recomputed with a K-1 token look-ahead so every du of the tile is
-// complete; dw, dbias partials cover the tile's own tokens.
-// ---------------------------------------------------------------------------
-template <typename T, int K>
-__global__ void __launch_bounds__(256) conv_bwd_kernel(ConvArgs a) {
-    const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (c0 >= a.C) return;
-    const int64_t b = blockIdx.z;
-    const int64_t tile = blockIdx.y;
-    const int64_t t0 = tile * kConvBwdTile;
-    const T *u = static_cast<const T *>(a.u);
-    const T *init = static_cast<const T *>(a.init);
-    const T *dout = static_cast<const T *>(a.dout);
-    T *du = static_cast<T *>(a.du);
-    float4 w[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        w[k] = make_float4(a.w[(c0 + 0) * K + k], a.w[(c0 + 1) * K + k], a.w[(c0 + 2) * K + k], a.w[(c0 + 3) * K + k]);
-    const float4 bias = *reinterpret_cast<const float4 *>(a.bias + c0);
-    auto sample = [&](int64_t t) -> float4 {
-        if (t >= 0) return ld4(u + (b * a.T + t) * a.C + c0);
-        if (init != nullptr) return ld4(init + (b * (K - 1) + (K - 1 + t)) * a.C + c0);
-        return make_float4(0.f, 0.f, 0.f, 0.f);
-    };
-    float4 win[K > 1 ? K - 1 : 1];
-#pragma unroll
-    for (int j = 0; j < K - 1; ++j) win[j] = sample(t0 - (K - 1) + j);
-    float4 ring[K];  // ring[j] = dv[m - (K-1) + j] after step m
-#pragma unroll
-    for (int j = 0; j < K; ++j) ring[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 first[K > 1 ? K - 1 : 1];  // dv[0 .. K-2] (tile 0 only, for dinit)
-#pragma unroll
-    for (int j = 0; j < K - 1; ++j) first[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    double pw[K][4], pb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        pb[i] = 0.0;
-#pragma unroll
-        for (int k = 0; k < K; ++k) pw[k][i] = 0.0;
-    }
-    const int64_t tend = (t0 + kConvBwdTile < a.T) ? t0 + kConvBwdTile : a.T;
-    for (int64_t m = t0; m < tend + K - 1; ++m) {
-        float4 dv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (m < a.T) {
-            const float4 xv = ld4(u + (b * a.T + m) * a.C + c0);
-            const float4 go = ld4(dout + (b * a.T + m) * a.C + c0);
+        for (int q = 0; q < kConvUnroll; ++q) {
+            if (tb + q >= tend) break;  // uniform across the workgroup
+            const float4 xv = xs[q];
             float4 v = bias;
 #pragma unroll
             for (int k = 0; k < K - 1; ++k) {
@@ -172,64 +110,160 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvArgs a) {
             v.y = fmaf(w[K - 1].y, xv.y, v.y);
             v.z = fmaf(w[K - 1].z, xv.z, v.z);
             v.w = fmaf(w[K - 1].w, xv.w, v.w);
-            dv = make_float4(go.x * silu_grad(v.x), go.y * silu_grad(v.y), go.z * silu_grad(v.z), go.w * silu_grad(v.w));
-            if (m < tend) {  // the tile's own token: parameter partials
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const double d = static_cast<double>(get(dv, i));
-                    pb[i] += d;
-#pragma unroll
-                    for (int k = 0; k < K - 1; ++k) pw[k][i] += d * static_cast<double>(get(win[k], i));
-                    pw[K - 1][i] += d * static_cast<double>(get(xv, i));
-                }
-            }
+            st4(out + (b * a.T + tb + q) * a.C + c0, make_float4(silu(v.x), silu(v.y), silu(v.z), silu(v.w)));
 #pragma unroll
             for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
             if (K > 1) win[K > 1 ? K - 2 : 0] = xv;
         }
-        if (t0 == 0 && m < K - 1) {
+    }
+    // the samples the next call needs: ext[T .. T+K-2] (the tile holding the last token,
+    // or tile 0 when there are no tokens)
+    if (a.final_state != nullptr && ((t0 < a.T && tend == a.T) || (a.T == 0 && t0 == 0))) {
+        T *fin = static_cast<T *>(a.final_state);
 #pragma unroll
-            for (int j = 0; j < K - 1; ++j)
-                if (j == m) first[j] = dv;
-        }
+        for (int j = 0; j < K - 1; ++j) st4(fin + (b * (K - 1) + j) * a.C + c0, win[j]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// convolution + SiLU, backward.  Workgroup = 64 channels x 256 tokens of one
+// sequence: thread (4 channels, 16-token sub-tile), so a wave reads 4 tokens x
+// 128 contiguous bytes per access and each thread's loop is short.  A sub-tile's
+// dv are recomputed with a K-1 token look-ahead so every du of it is complete.
+// A thread sums its 16 tokens' weight/bias terms in float32; the 16 sub-tile sums
+// are added in fp64 in LDS in sub-tile order and written as one partial per
+// (sequence, 256-token tile).
+// ---------------------------------------------------------------------------
+constexpr int kConvSub = 16;                       // tokens per thread
+constexpr int kConvSubs = kConvBwdTile / kConvSub;  // sub-tiles per workgroup (16)
+
+template <typename T, int K>
+__global__ void __launch_bounds__(256) conv_bwd_kernel(ConvArgs a) {
+    __shared__ double red[kConvSubs][K + 1][64];
+    const int cg = threadIdx.x & 15, sub = threadIdx.x >> 4;
+    const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64 + cg * 4;
+    const bool cvalid = c0 < a.C;
+    const int64_t b = blockIdx.z;
+    const int64_t tile = blockIdx.y;
+    const int64_t t0 = tile * kConvBwdTile + sub * kConvSub;
+    const T *u = static_cast<const T *>(a.u);
+    const T *init = static_cast<const T *>(a.init);
+    const T *dout = static_cast<const T *>(a.dout);
+    T *du = static_cast<T *>(a.du);
+    float pw[K][4], pb[4];  // float32 over the 16 tokens of the sub-tile, fp64 beyond
 #pragma unroll
-        for (int j = 0; j + 1 < K; ++j) ring[j] = ring[j + 1];
-        ring[K - 1] = dv;
-        const int64_t t = m - (K - 1);  // du[t] = sum_j w[K-1-j] dv[t+j] is complete
-        if (t >= t0 && t < tend) {
-            float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < 4; ++i) {
+        pb[i] = 0.f;
 #pragma unroll
-            for (int j = 0; j < K; ++j) {
-                g.x = fmaf(w[K - 1 - j].x, ring[j].x, g.x);
-                g.y = fmaf(w[K - 1 - j].y, ring[j].y, g.y);
-                g.z = fmaf(w[K - 1 - j].z, ring[j].z, g.z);
-                g.w = fmaf(w[K - 1 - j].w, ring[j].w, g.w);
+        for (int k = 0; k < K; ++k) pw[k][i] = 0.f;
+    }
+    if (cvalid && t0 < a.T) {
+        float4 w[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            w[k] = make_float4(a.w[(c0 + 0) * K + k], a.w[(c0 + 1) * K + k], a.w[(c0 + 2) * K + k], a.w[(c0 + 3) * K + k]);
+        const float4 bias = *reinterpret_cast<const float4 *>(a.bias + c0);
+        auto sample = [&](int64_t t) -> float4 {
+            if (t >= 0) return ld4(u + (b * a.T + t) * a.C + c0);
+            if (init != nullptr) return ld4(init + (b * (K - 1) + (K - 1 + t)) * a.C + c0);
+            return make_float4(0.f, 0.f, 0.f, 0.f);
+        };
+        float4 win[K > 1 ? K - 1 : 1];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) win[j] = sample(t0 - (K - 1) + j);
+        float4 ring[K];  // ring[j] = dv[m - (K-1) + j] after step m
+#pragma unroll
+        for (int j = 0; j < K; ++j) ring[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 first[K > 1 ? K - 1 : 1];  // dv[0 .. K-2] (the sub-tile at token 0, for dinit)
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) first[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int64_t tend = (t0 + kConvSub < a.T) ? t0 + kConvSub : a.T;
+        for (int64_t m = t0; m < tend + K - 1; ++m) {
+            float4 dv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (m < a.T) {
+                const float4 xv = ld4(u + (b * a.T + m) * a.C + c0);
+                const float4 go = ld4(dout + (b * a.T + m) * a.C + c0);
+                float4 v = bias;
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k) {
+                    v.x = fmaf(w[k].x, win[k].x, v.x);
+                    v.y = fmaf(w[k].y, win[k].y, v.y);
+                    v.z = fmaf(w[k].z, win[k].z, v.z);
+                    v.w = fmaf(w[k].w, win[k].w, v.w);
+                }
+                v.x = fmaf(w[K - 1].x, xv.x, v.x);
+                v.y = fmaf(w[K - 1].y, xv.y, v.y);
+                v.z = fmaf(w[K - 1].z, xv.z, v.z);
+                v.w = fmaf(w[K - 1].w, xv.w, v.w);
+                dv = make_float4(go.x * silu_grad(v.x), go.y * silu_grad(v.y), go.z * silu_grad(v.z), go.w * silu_grad(v.w));
+                if (m < tend) {  // the sub-tile's own token: parameter partials
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float d = get(dv, i);
+                        pb[i] += d;
+#pragma unroll
+                        for (int k = 0; k < K - 1; ++k) pw[k][i] = fmaf(d, get(win[k], i), pw[k][i]);
+                        pw[K - 1][i] = fmaf(d, get(xv, i), pw[K - 1][i]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+                if (K > 1) win[K > 1 ? K - 2 : 0] = xv;
             }
-            st4(du + (b * a.T + t) * a.C + c0, g);
+            if (t0 == 0 && m < K - 1) {
+#pragma unroll
+                for (int j = 0; j < K - 1; ++j)
+                    if (j == m) first[j] = dv;
+            }
+#pragma unroll
+            for (int j = 0; j + 1 < K; ++j) ring[j] = ring[j + 1];
+            ring[K - 1] = dv;
+            const int64_t t = m - (K - 1);  // du[t] = sum_j w[K-1-j] dv[t+j] is complete
+            if (t >= t0 && t < tend) {
+                float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    g.x = fmaf(w[K - 1 - j].x, ring[j].x, g.x);
+                    g.y = fmaf(w[K - 1 - j].y, ring[j].y, g.y);
+                    g.z = fmaf(w[K - 1 - j].z, ring[j].z, g.z);
+                    g.w = fmaf(w[K - 1 - j].w, ring[j].w, g.w);
+                }
+                st4(du + (b * a.T + t) * a.C + c0, g);
+            }
+        }
+        if (t0 == 0 && a.dinit != nullptr) {
+            T *dinit = static_cast<T *>(a.dinit);
+#pragma unroll
+            for (int j = 0; j < K - 1; ++j) {
+                float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int k = 0; k <= j; ++k) {
+                    g.x = fmaf(w[k].x, first[j - k].x, g.x);
+                    g.y = fmaf(w[k].y, first[j - k].y, g.y);
+                    g.z = fmaf(w[k].z, first[j - k].z, g.z);
+                    g.w = fmaf(w[k].w, first[j - k].w, g.w);
+                }
+                st4(dinit + (b * (K - 1) + j) * a.C + c0, g);
+            }
         }
     }
+    // sub-tile partials meet in LDS; the tile's partial is their sum in sub-tile order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) red[sub][k][cg * 4 + i] = static_cast<double>(pw[k][i]);
+        red[sub][K][cg * 4 + i] = static_cast<double>(pb[i]);
+    }
+    __syncthreads();
     // partials [b * ntiles + tile][K + 1][C]: K weight taps, then the bias
     const int64_t pi = (b * a.ntiles + tile) * (K + 1);
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a.part[(pi + k) * a.C + c0 + i] = pw[k][i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a.part[(pi + K) * a.C + c0 + i] = pb[i];
-    if (t0 == 0 && a.dinit != nullptr) {
-        T *dinit = static_cast<T *>(a.dinit);
-#pragma unroll
-        for (int j = 0; j < K - 1; ++j) {
-            float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-            for (int k = 0; k <= j; ++k) {
-                g.x = fmaf(w[k].x, first[j - k].x, g.x);
-                g.y = fmaf(w[k].y, first[j - k].y, g.y);
-                g.z = fmaf(w[k].z, first[j - k].z, g.z);
-                g.w = fmaf(w[k].w, first[j - k].w, g.w);
-            }
-            st4(dinit + (b * (K - 1) + j) * a.C + c0, g);
-        }
+    for (int e = threadIdx.x; e < (K + 1) * 64; e += 256) {
+        const int k = e / 64, cc = e % 64;
+        const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cc;
+        if (c >= a.C) continue;
+        double acc = 0.0;
+        for (int sb = 0; sb < kConvSubs; ++sb) acc += red[sb][k][cc];
+        a.part[(pi + k) * a.C + c] = acc;
     }
 }
 
@@ -334,34 +368,49 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormArgs a) {
     const T *dout = static_cast<const T *>(a.dout);
     T *dy = static_cast<T *>(a.dy);
     T *dz = static_cast<T *>(a.dz);
-    double pw[NQ][8];
+    float pw[NQ][8];  // float32 over the tile's rows, fp64 across tiles
     float wv[NQ][8];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int64_t i = 8 * (threadIdx.x + 256 * q);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pw[q][e] = 0.0;
+            pw[q][e] = 0.f;
             wv[q][e] = (i < S) ? a.w[grp * S + i + e] : 0.f;
         }
     }
     const int64_t r0 = rt * kNormRows;
     const int64_t r1 = (r0 + kNormRows < a.rows) ? r0 + kNormRows : a.rows;
-    for (int64_t row = r0; row < r1; ++row) {
+    // Rows alternate between two register sets so the next row's loads are in flight
+    // while the current row is reduced (a copy of a loaded register would wait for it).
+    struct Row {
+        float y[NQ][8], z[NQ][8], g[NQ][8];
+    };
+    auto load = [&](Row &R, int64_t row) {
         const int64_t base = row * a.C + grp * S;
-        float yv[NQ][8], zv[NQ][8], go[NQ][8];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int64_t i = 8 * (threadIdx.x + 256 * q);
+            if (i < S) {
+                ld8(y + base + i, R.y[q]);
+                ld8(z + base + i, R.z[q]);
+                ld8(dout + base + i, R.g[q]);
+            }
+        }
+    };
+    auto process = [&](const Row &R, int64_t row) {
+        const int64_t base = row * a.C + grp * S;
+        float sg[NQ][8], gg[NQ][8];  // sigmoid(z) and the gated value g = y SiLU(z)
         float ss = 0.f;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int64_t i = 8 * (threadIdx.x + 256 * q);
             if (i < S) {
-                ld8(y + base + i, yv[q]);
-                ld8(z + base + i, zv[q]);
-                ld8(dout + base + i, go[q]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float g = yv[q][e] * silu(zv[q][e]);
-                    ss = fmaf(g, g, ss);
+                    sg[q][e] = sigm(R.z[q][e]);
+                    gg[q][e] = R.y[q][e] * (R.z[q][e] * sg[q][e]);
+                    ss = fmaf(gg[q][e], gg[q][e], ss);
                 }
             }
         }
@@ -373,9 +422,9 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormArgs a) {
             if (i < S) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float n = yv[q][e] * silu(zv[q][e]) * r;
-                    dn_n = fmaf(go[q][e] * wv[q][e], n, dn_n);
-                    pw[q][e] += static_cast<double>(go[q][e]) * static_cast<double>(n);
+                    const float n = gg[q][e] * r;
+                    dn_n = fmaf(R.g[q][e] * wv[q][e], n, dn_n);
+                    pw[q][e] = fmaf(R.g[q][e], n, pw[q][e]);
                 }
             }
         }
@@ -387,15 +436,25 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormArgs a) {
                 float oy[8], oz[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float sz = silu(zv[q][e]);
-                    const float n = yv[q][e] * sz * r;
-                    const float dg = r * (go[q][e] * wv[q][e] - n * m);
-                    oy[e] = dg * sz;
-                    oz[e] = dg * yv[q][e] * silu_grad(zv[q][e]);
+                    const float zv = R.z[q][e], sv = sg[q][e];
+                    const float n = gg[q][e] * r;
+                    const float dg = r * (R.g[q][e] * wv[q][e] - n * m);
+                    oy[e] = dg * (zv * sv);
+                    oz[e] = dg * R.y[q][e] * (sv * (1.f + zv * (1.f - sv)));
                 }
                 st8(dy + base + i, oy);
                 st8(dz + base + i, oz);
             }
+        }
+    };
+    Row RA, RB;
+    if (r0 < r1) load(RA, r0);
+    for (int64_t row = r0; row < r1; row += 2) {
+        if (row + 1 < r1) load(RB, row + 1);
+        process(RA, row);
+        if (row + 1 < r1) {
+            if (row + 2 < r1) load(RA, row + 2);
+            process(RB, row + 1);
         }
     }
     // partials [row tile][C]
@@ -404,7 +463,7 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormArgs a) {
         const int64_t i = 8 * (threadIdx.x + 256 * q);
         if (i < S)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a.part[rt * a.C + grp * S + i + e] = pw[q][e];
+            for (int e = 0; e < 8; ++e) a.part[rt * a.C + grp * S + i + e] = static_cast<double>(pw[q][e]);
     }
 }
 
@@ -425,7 +484,8 @@ hipError_t conv_launch(const ConvArgs &a, bool bwd, hipStream_t s) {
         return hipGetLastError();
     }
     if (a.ntiles > 0) {
-        conv_bwd_kernel<T, K><<<dim3(cx, static_cast<unsigned>(a.ntiles), static_cast<unsigned>(a.Bsz)), 256, 0, s>>>(a);
+        const unsigned cb = static_cast<unsigned>((a.C + 63) / 64);
+        conv_bwd_kernel<T, K><<<dim3(cb, static_cast<unsigned>(a.ntiles), static_cast<unsigned>(a.Bsz)), 256, 0, s>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
