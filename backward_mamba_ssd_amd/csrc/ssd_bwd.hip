@@ -85,30 +85,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
         u16x8 yr[2], cr[4];
         float dtr;
     };
-    // per-block buffer descriptors: rows at or past the end of the sequence read zero
+    // per-block buffer descriptors: rows at or past the end of the sequence read zero.
+    // Block s starts at base + s * stride; 32-bit block counts keep 64-bit multiplies
+    // and divides out of the loop.
     const uint32_t toky = static_cast<uint32_t>(a.H) * kP * 2, tokc = static_cast<uint32_t>(a.G) * kN * 2;
-    auto prefetch = [&](Rows &R, int64_t t0) {
-        const uint32_t nv = static_cast<uint32_t>(T - t0 < kLs ? T - t0 : kLs);
-        const rsrc_t ry = make_rsrc(dy + ((b * T + t0) * a.H + h) * kP, nv * toky);
-        const rsrc_t rc = make_rsrc(Cm + ((b * T + t0) * a.G + g) * kN, nv * tokc);
+    const bf16_t *dy0 = dy + (b * T * a.H + h) * kP;
+    const bf16_t *C0 = Cm + (b * T * a.G + g) * kN;
+    const float *dt0 = a.dt + b * T * a.H + h;
+    const int64_t sy = static_cast<int64_t>(kLs) * a.H * kP, sc = static_cast<int64_t>(kLs) * a.G * kN;
+    const int64_t sd = static_cast<int64_t>(kLs) * a.H;
+    auto prefetch = [&](Rows &R, int s) {
+        const int64_t rem = T - static_cast<int64_t>(s) * kLs;
+        const uint32_t nv = static_cast<uint32_t>(rem < kLs ? rem : kLs);
+        const rsrc_t ry = make_rsrc(dy0 + s * sy, nv * toky);
+        const rsrc_t rc = make_rsrc(C0 + s * sc, nv * tokc);
 #pragma unroll
         for (int i = 0; i < 2; ++i) R.yr[i] = buf_ld_16b(ry, (yt0 + i) * toky + yp0 * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) R.cr[i] = buf_ld_16b(rc, (ct0 + i) * tokc + cn0 * 2);
         R.dtr = 0.f;
         if (tid < kLs) {
-            const rsrc_t rd = make_rsrc(a.dt + (b * T + t0) * a.H + h, nv * a.H * 4u);
+            const rsrc_t rd = make_rsrc(dt0 + s * sd, nv * a.H * 4u);
             R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
         }
     };
-    const int64_t nblk = (T + kLs - 1) / kLs;
+    const int nblk = static_cast<int>((T + kLs - 1) / kLs);
+    const int bpc = static_cast<int>(a.L / kLs);  // blocks per chunk
+    float *const dst0 = a.dstates + static_cast<int64_t>(bh) * a.nchunks * PN;
     // one block of the reverse walk; R is refilled with block s - 2 once staged
-    auto step = [&](int64_t s, Rows &R) {
-        const int64_t t0 = s * kLs;
-        const int buf = static_cast<int>(s & 1);
-        if (s == nblk - 1 || ((t0 + kLs) % a.L) == 0) {
+    auto step = [&](int s, Rows &R) {
+        const int buf = s & 1;
+        if (s == nblk - 1 || (s + 1) % bpc == 0) {
             // gradient on the state leaving chunk c (everything after it)
-            float *dst = a.dstates + (static_cast<int64_t>(bh) * a.nchunks + t0 / a.L) * PN;
+            float *dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
@@ -132,7 +141,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
                 *reinterpret_cast<u16x4 *>(&sm.CT[(cn0 + e) * kS64 + ct0]) = v;
             }
         }
-        if (s >= 2) prefetch(R, t0 - 2 * kLs);
+        if (s >= 2) prefetch(R, s - 2);
         __syncthreads();
         const float el = __expf(lam_end);
 #pragma unroll
@@ -149,9 +158,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
         }
     };
     Rows RA, RB;
-    prefetch(RA, (nblk - 1) * kLs);
-    if (nblk >= 2) prefetch(RB, (nblk - 2) * kLs);
-    for (int64_t s = nblk - 1; s >= 0; s -= 2) {
+    prefetch(RA, nblk - 1);
+    if (nblk >= 2) prefetch(RB, nblk - 2);
+    for (int s = nblk - 1; s >= 0; s -= 2) {
         step(s, RA);
         if (s >= 1) step(s - 1, RB);
     }

@@ -84,29 +84,38 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     float dtr = 0.f;
     const uint32_t tokx = static_cast<uint32_t>(a.H) * kP * 2;
     const uint32_t tokbc = static_cast<uint32_t>(a.G) * kN * 2;
-    auto nvalid_of = [&](int64_t t0) { return static_cast<uint32_t>(T - t0 < kLs ? T - t0 : kLs); };
-    auto rows_x = [&](const bf16_t *base, int64_t t0) {
-        return make_rsrc(base + ((b * T + t0) * a.H + h) * kP, nvalid_of(t0) * tokx);
-    };
-    auto rows_bc = [&](const bf16_t *base, int64_t t0) {
-        return make_rsrc(base + ((b * T + t0) * a.G + g) * kN, nvalid_of(t0) * tokbc);
-    };
-    auto prefetch = [&](int64_t t0) {
+    // Per-block pointers advance by a fixed stride (no 64-bit multiply or divide in the
+    // loop); the buffer range check zeroes / drops the ragged tail.
+    const int64_t sx = static_cast<int64_t>(kLs) * a.H * kP;   // elements between blocks of x, y
+    const int64_t sbc = static_cast<int64_t>(kLs) * a.G * kN;  // ... of B, C
+    const int64_t sdt = static_cast<int64_t>(kLs) * a.H;       // ... of dt
+    const bf16_t *px = x + (b * T * a.H + h) * kP;  // next block to prefetch
+    const bf16_t *pB = Bm + (b * T * a.G + g) * kN;
+    const bf16_t *pC = Cm + (b * T * a.G + g) * kN;
+    const float *pdt = a.dt + b * T * a.H + h;
+    bf16_t *py = y + (b * T * a.H + h) * kP;        // block being computed
+    auto nvalid_of = [&](int64_t rem) { return static_cast<uint32_t>(rem < kLs ? rem : kLs); };
+    auto prefetch = [&](int64_t rem) {  // rem: tokens from the prefetched block to the end
+        const uint32_t nv = nvalid_of(rem);
         if (lowhalf) {
-            const rsrc_t rb = rows_bc(Bm, t0);
+            const rsrc_t rb = make_rsrc(pB, nv * tokbc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) pre[i] = buf_ld_16b(rb, (bt0 + i) * tokbc + bn0 * 2);
         } else {
-            const rsrc_t rc = rows_bc(Cm, t0), rx = rows_x(x, t0);
+            const rsrc_t rc = make_rsrc(pC, nv * tokbc), rx = make_rsrc(px, nv * tokx);
 #pragma unroll
             for (int i = 0; i < 4; ++i) pre[i] = buf_ld_16b(rc, (bt0 + i) * tokbc + bn0 * 2);
 #pragma unroll
             for (int i = 0; i < 2; ++i) pre[4 + i] = buf_ld_16b(rx, (xt0 + i) * tokx + xp0 * 2);
         }
         if (tid < kLs) {
-            const rsrc_t rd = make_rsrc(a.dt + (b * T + t0) * a.H + h, nvalid_of(t0) * a.H * 4u);
+            const rsrc_t rd = make_rsrc(pdt, nv * a.H * 4u);
             dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
         }
+        px += sx;
+        pB += sbc;
+        pC += sbc;
+        pdt += sdt;
     };
     // Gram tile assignment (i-tile, j-tiles): every tile with j <= i once, plus the two
     // zero tiles (0,1) and (2,3) that the output products read
@@ -115,7 +124,10 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     const int gnj = (wave <= 3) ? 2 : (wave == 6) ? 2 : (wave == 7) ? 0 : 1;  // waves 3, 6 write a zero second tile
 
     const int64_t nblk = (T + kLs - 1) / kLs;
-    prefetch(0);
+    const int bpc = static_cast<int>(a.L / kLs);  // blocks per chunk
+    int kc = 0;                                   // block index within its chunk
+    float *cs = (a.chunk_states != nullptr) ? a.chunk_states + static_cast<int64_t>(bh) * a.nchunks * (kP * kN) : nullptr;
+    prefetch(T);
     for (int64_t s = 0; s < nblk; ++s) {
         const int64_t t0 = s * kLs;
         const int buf = static_cast<int>(s & 1);
@@ -150,15 +162,16 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
             }
         }
         // state entering a chunk of L tokens
-        if (a.chunk_states != nullptr && (t0 % a.L) == 0) {
-            float *cs = a.chunk_states + (static_cast<int64_t>(bh) * a.nchunks + t0 / a.L) * (kP * kN);
+        if (cs != nullptr && kc == 0) {
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 const int n = 16 * wave + lq, p = 16 * pt + lr;
                 *reinterpret_cast<float4 *>(cs + p * kN + n) = make_float4(H[pt][0], H[pt][1], H[pt][2], H[pt][3]);
             }
+            cs += kP * kN;
         }
-        if (s + 1 < nblk) prefetch(t0 + kLs);
+        if (++kc == bpc) kc = 0;
+        if (s + 1 < nblk) prefetch(T - t0 - kLs);
         __syncthreads();
         // (3) masked, decayed Gram tiles (i-tile gi, j-tiles gj0, gj0+1); the wave's C
         //     fragments are read once for both
@@ -205,7 +218,7 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
         // (5) outputs Y^T: p-tile (w & 3), token tiles 2*(w >> 2) + {0, 1}; the wave's H and
         //     X^T fragments are read once for both
         {
-            const rsrc_t ry = rows_x(y, t0);
+            const rsrc_t ry = make_rsrc(py, nvalid_of(T - t0) * tokx);
             const int pw = wave & 3, ih = wave >> 2;
             const int prow = 16 * pw + lr;
             bf16x8 fh[4], fx[2];
@@ -232,6 +245,7 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
                 buf_st_8b(ry, tok * tokx + (16 * pw + lq) * 2, pack4(acc[0], acc[1], acc[2], acc[3]));
             }
         }
+        py += sx;
         // (6) state update H^T = exp(Lam_63) H^T + Bs^T X on the wave's n-tile
         {
             const float el = __expf(lam_end);
