@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssd_common.hpp"
+
 namespace ssm {
 
 struct DecodeArgs {
@@ -66,30 +68,7 @@ struct Sr16Args {
     uint64_t n, seed, ckpt, offset;
 };
 
-// Chunked MFMA path (bf16 operands, P = 64, N = 128, chunk % 64 == 0).
-struct SsdFwdArgs {
-    int64_t Bsz, T;
-    int H, G;
-    int64_t L, nchunks;
-    const void *x, *B, *C;
-    const float *dt, *A, *D, *h0;
-    void *y;
-    float *h_final, *chunk_states;
-};
-
-struct SsdBwdArgs {
-    int64_t Bsz, T;
-    int H, G;
-    int64_t L, nchunks;
-    const void *x, *B, *C, *dy;
-    const float *dt, *A, *D, *chunk_states, *dh_final;
-    void *dx;
-    float *dB, *dC, *ddt, *dA, *dD, *dh0;
-    hipEvent_t ev_begin, ev_end;  // optional: recorded around the per-block kernel
-    // workspace
-    float *dstates;   // [Bsz, H, nchunks, 64, 128]: gradient on the state leaving chunk c
-    double *pA, *pD;  // [Bsz, H, nchunks, chunk/64] per-block partials of dA, dD
-};
+// SsdFwdArgs, SsdBwdArgs (the chunked MFMA path) are in ssd_common.hpp.
 
 // Time-step and rate preparation (forward and backward share one block).
 struct DtPrepArgs {

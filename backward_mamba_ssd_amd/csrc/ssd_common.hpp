@@ -11,6 +11,32 @@
 
 namespace ssm {
 
+// Argument blocks of the chunked MFMA path (bf16 operands, P = 64, N = 128,
+// chunk % 64 == 0).
+struct SsdFwdArgs {
+    int64_t Bsz, T;
+    int H, G;
+    int64_t L, nchunks;
+    const void *x, *B, *C;
+    const float *dt, *A, *D, *h0;
+    void *y;
+    float *h_final, *chunk_states;
+};
+
+struct SsdBwdArgs {
+    int64_t Bsz, T;
+    int H, G;
+    int64_t L, nchunks;
+    const void *x, *B, *C, *dy;
+    const float *dt, *A, *D, *chunk_states, *dh_final;
+    void *dx;
+    float *dB, *dC, *ddt, *dA, *dD, *dh0;
+    hipEvent_t ev_begin, ev_end;  // optional: recorded around the per-block kernel
+    // workspace
+    float *dstates;   // [Bsz, H, nchunks, 64, 128]: gradient on the state leaving chunk c
+    double *pA, *pD;  // [Bsz, H, nchunks, chunk/64] per-block partials of dA, dD
+};
+
 constexpr int kP = 64;          // value channels per head
 constexpr int kN = 128;         // state coordinates
 constexpr int kLs = 64;         // tokens per block

@@ -92,9 +92,11 @@ def path_entry(flops, nbytes, ms, flop_peak_tflops=None):
     return e
 
 
+# the files a kernel's code comes from (launch.hpp only declares host launchers; the
+# chunked path's argument blocks live in ssd_common.hpp)
 KERNEL_SOURCES = {
-    "ssd_fwd_kernel": ("ssd_fwd.hip", "ssd_common.hpp", "common.hpp", "launch.hpp"),
-    "ssd_bwd_block_kernel": ("ssd_bwd.hip", "ssd_common.hpp", "common.hpp", "launch.hpp"),
+    "ssd_fwd_kernel": ("ssd_fwd.hip", "ssd_common.hpp", "common.hpp"),
+    "ssd_bwd_block_kernel": ("ssd_bwd.hip", "ssd_common.hpp", "common.hpp"),
 }
 
 
