@@ -467,12 +467,20 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormArgs a) {
     }
 }
 
+// dw[c]: 64 channels per workgroup, four waves each adding every fourth tile's
+// partial (tiles ascending), then the four wave sums in wave order
 __global__ void __launch_bounds__(256) norm_param_sum_kernel(NormArgs a, int64_t ntiles) {
-    const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (c >= a.C) return;
+    __shared__ double red[4][64];
+    const int cl = threadIdx.x & 63, qt = threadIdx.x >> 6;
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
     double s = 0.0;
-    for (int64_t t = 0; t < ntiles; ++t) s += a.part[t * a.C + c];
-    a.dw[c] = static_cast<float>(s);
+    if (c < a.C) {
+#pragma unroll 8
+        for (int64_t t = qt; t < ntiles; t += 4) s += a.part[t * a.C + c];
+    }
+    red[qt][cl] = s;
+    __syncthreads();
+    if (qt == 0 && c < a.C) a.dw[c] = static_cast<float>(((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl]);
 }
 
 template <typename T, int K>
@@ -520,7 +528,7 @@ hipError_t norm_launch(const NormArgs &a, bool bwd, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    norm_param_sum_kernel<<<static_cast<unsigned>((a.C + 255) / 256), 256, 0, s>>>(a, nt);
+    norm_param_sum_kernel<<<static_cast<unsigned>((a.C + 63) / 64), 256, 0, s>>>(a, nt);
     return hipGetLastError();
 }
 
