@@ -30,6 +30,17 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
+// Streaming (nontemporal) 16-byte access for data touched once per call, such as a
+// state streamed through HBM: the load does not allocate in L2, which measured ~9%
+// more HBM bandwidth for the in-place decode update than ordinary loads.
+__device__ __forceinline__ float4 nt_ld4(const float *p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void nt_st4(float *p, const float4 &v) {
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4 *>(p));
+}
+
 // Scalar load/store of a storage dtype as float.
 template <typename T> struct IO;
 template <> struct IO<float> {

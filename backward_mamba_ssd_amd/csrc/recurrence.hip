@@ -92,11 +92,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
             if constexpr (SR16) {
                 // binary16 -> float32 is exact; convert the whole vector (an element-wise
                 // bit_cast of a vector subscript is not reliable here)
-                const h16x4 hv = *reinterpret_cast<const h16x4 *>(st16 + static_cast<int64_t>(p) * N + n0);
+                const h16x4 hv = __builtin_nontemporal_load(reinterpret_cast<const h16x4 *>(st16 + static_cast<int64_t>(p) * N + n0));
                 const f32x4 fv = __builtin_convertvector(hv, f32x4);
                 s[i] = make_float4(fv[0], fv[1], fv[2], fv[3]);
             } else {
-                s[i] = *reinterpret_cast<const float4 *>(st + static_cast<int64_t>(p) * N + n0);
+                s[i] = nt_ld4(st + static_cast<int64_t>(p) * N + n0);
             }
         }
     }
@@ -122,9 +122,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
                 o[1] = sr16_bits(s[i].y, sr16_entropy(sub, e0 + 1));
                 o[2] = sr16_bits(s[i].z, sr16_entropy(sub, e0 + 2));
                 o[3] = sr16_bits(s[i].w, sr16_entropy(sub, e0 + 3));
-                *reinterpret_cast<u16x4 *>(st16 + static_cast<int64_t>(p) * N + n0) = o;
+                __builtin_nontemporal_store(o, reinterpret_cast<u16x4 *>(st16 + static_cast<int64_t>(p) * N + n0));
             } else {
-                *reinterpret_cast<float4 *>(st + static_cast<int64_t>(p) * N + n0) = s[i];
+                nt_st4(st + static_cast<int64_t>(p) * N + n0, s[i]);
             }
             if ((tid % LPR) == 0)
                 IO<T>::st(static_cast<T *>(a.y), static_cast<int64_t>(bh) * a.P + p,
@@ -183,14 +183,14 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
             if (a.ckpt != nullptr) {
                 const CK *ck = static_cast<const CK *>(a.ckpt);
                 if constexpr (sizeof(CK) == 4) {
-                    s[i] = *reinterpret_cast<const float4 *>(ck + off);
+                    s[i] = nt_ld4(ck + off);
                 } else {
                     const _Float16 *hk = reinterpret_cast<const _Float16 *>(ck + off);
                     s[i] = make_float4(static_cast<float>(hk[0]), static_cast<float>(hk[1]),
                                        static_cast<float>(hk[2]), static_cast<float>(hk[3]));
                 }
             }
-            if constexpr (LIVE) l[i] = *reinterpret_cast<const float4 *>(a.live + off);
+            if constexpr (LIVE) l[i] = nt_ld4(a.live + off);
         }
     }
     const float Ah = a.A[h];
@@ -340,11 +340,11 @@ __global__ void __launch_bounds__(256) rollback_kernel(RollbackArgs a) {
         return;
     }
     const int64_t n4 = a.per_seq / 4;
-    const float4 *src = reinterpret_cast<const float4 *>(a.snap + (static_cast<int64_t>(acc) * a.Bsz + b) * a.per_seq);
-    float4 *dst = reinterpret_cast<float4 *>(a.state_out + b * a.per_seq);
+    const float *src = a.snap + (static_cast<int64_t>(acc) * a.Bsz + b) * a.per_seq;
+    float *dst = a.state_out + b * a.per_seq;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride)
-        dst[i] = src[i];
+        nt_st4(dst + 4 * i, nt_ld4(src + 4 * i));
 }
 
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t s) {

@@ -15,8 +15,8 @@ __global__ void __launch_bounds__(256) sr16_kernel(Sr16Args a) {
     if (i0 >= a.n) return;
     if (i0 + 8 <= a.n && (reinterpret_cast<uintptr_t>(a.in + i0) & 15u) == 0 &&
         (reinterpret_cast<uintptr_t>(a.out + i0) & 15u) == 0) {
-        const float4 v0 = *reinterpret_cast<const float4 *>(a.in + i0);
-        const float4 v1 = *reinterpret_cast<const float4 *>(a.in + i0 + 4);
+        const float4 v0 = nt_ld4(a.in + i0);
+        const float4 v1 = nt_ld4(a.in + i0 + 4);
         const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
         u16x8 o;
 #pragma unroll
@@ -25,7 +25,7 @@ __global__ void __launch_bounds__(256) sr16_kernel(Sr16Args a) {
             const uint32_t u = static_cast<uint32_t>(sm64_mix(sub + (e + 1ull) * kGamma) >> 32);
             o[j] = sr16_bits(vv[j], u);
         }
-        *reinterpret_cast<u16x8 *>(a.out + i0) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<u16x8 *>(a.out + i0));
     } else {
         for (uint64_t i = i0; i < a.n && i < i0 + 8; ++i) {
             const uint64_t e = a.offset + i;
