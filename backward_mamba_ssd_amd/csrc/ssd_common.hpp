@@ -105,6 +105,10 @@ __device__ __forceinline__ void buf_st_8b(rsrc_t r, uint32_t off, u16x4 v) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_st_16b(rsrc_t r, uint32_t off, u16x8 v) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
 __device__ __forceinline__ void buf_st_f32(rsrc_t r, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }

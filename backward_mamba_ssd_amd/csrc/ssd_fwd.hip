@@ -46,6 +46,7 @@ struct __align__(16) FwdSmem {
     bf16_t XT[kP * kS64];     // [p][tok]
     bf16_t Gm[kLs * kS64];    // [i][j] = (C_i.B_j) exp(Lam_i - Lam_j) dt_j for j <= i, else 0
     float2 ld[2][kLs];        // (Lam, dt) per token, double-buffered by block parity
+    bf16_t Y[kLs * kS64];     // [tok][p]: the block's outputs, stored to HBM as whole rows
 };
 
 __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
@@ -117,6 +118,16 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
         pC += sbc;
         pdt += sdt;
     };
+    // Outputs leave through LDS: each thread stores 16 bytes of one token row, so a
+    // wave writes 8 tokens x 128 B (whole rows of this head) per instruction instead
+    // of 16 tokens x 32 B from the MFMA accumulator layout.
+    const int yt = tid >> 3, yc = (tid & 7) * 8;  // token, first channel
+    auto store_y = [&](int64_t tb) {
+        const rsrc_t ry = make_rsrc(py, nvalid_of(T - tb) * tokx);
+        const u16x8 v = *reinterpret_cast<const u16x8 *>(&sm.Y[yt * kS64 + yc]);
+        buf_st_16b(ry, static_cast<uint32_t>(yt) * tokx + yc * 2, v);
+        py += sx;
+    };
     // Gram tile assignment (i-tile, j-tiles): every tile with j <= i once, plus the two
     // zero tiles (0,1) and (2,3) that the output products read
     const int gi = (wave < 2) ? 3 : (wave < 4) ? 2 : (wave < 6) ? 1 : 0;
@@ -134,6 +145,7 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
         // (1) cumulative log-retention of the block (one wave, one token per lane)
         if (wave == 0) sm.ld[buf][lane] = make_float2(wave_prefix_sum(dtr * Ah), dtr);
         __syncthreads();
+        if (s > 0) store_y(t0 - kLs);  // the previous block's outputs, complete since the barrier
         const float2 *ld = sm.ld[buf];
         const float lam_end = ld[kLs - 1].x;
         // (2) stage the block in LDS: waves 0-3 B and Bs^T, waves 4-7 C and X^T
@@ -218,7 +230,6 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
         // (5) outputs Y^T: p-tile (w & 3), token tiles 2*(w >> 2) + {0, 1}; the wave's H and
         //     X^T fragments are read once for both
         {
-            const rsrc_t ry = make_rsrc(py, nvalid_of(T - t0) * tokx);
             const int pw = wave & 3, ih = wave >> 2;
             const int prow = 16 * pw + lr;
             bf16x8 fh[4], fx[2];
@@ -242,10 +253,9 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
                     if (kk > ih) break;
                     acc = mfma(fx[kk], frag_row(&sm.Gm[(16 * tt + lr) * kS64 + 32 * kk + lk]), acc);
                 }
-                buf_st_8b(ry, tok * tokx + (16 * pw + lq) * 2, pack4(acc[0], acc[1], acc[2], acc[3]));
+                *reinterpret_cast<u16x4 *>(&sm.Y[tok * kS64 + 16 * pw + lq]) = pack4(acc[0], acc[1], acc[2], acc[3]);
             }
         }
-        py += sx;
         // (6) state update H^T = exp(Lam_63) H^T + Bs^T X on the wave's n-tile
         {
             const float el = __expf(lam_end);
@@ -262,6 +272,8 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
             }
         }
     }
+    __syncthreads();
+    if (nblk > 0) store_y((nblk - 1) * kLs);
     if (a.h_final != nullptr) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
