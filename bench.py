@@ -458,8 +458,9 @@ def around_scan_rates(dev):
     return res
 
 
-def secondary(dev):
-    """Decode (full 64 x 48 x 100 workload), SR16 and replay rates."""
+def decode_rates(dev):
+    """Decode on the full 64 x 48 x 100 workload (float32 state and FP16-SR state cache)
+    and the SR16 checkpoint rate."""
     import torch
 
     from backward_mamba_ssd_amd import inputs, ssm
@@ -527,11 +528,13 @@ def secondary(dev):
     out["sr16"] = path_entry(0, st.numel() * 6, e0.elapsed_time(e1) / 20)
     del st, bits
     torch.cuda.empty_cache()
-    out["dt_prep"] = dt_prep_rates(dev)
-    out["draft_rollback"] = draft_rollback_rates(dev)
-    out["around_scan"] = around_scan_rates(dev)
-    log("replay sweep ...")
-    out["replay_sr16_b16"] = replay_sweep(dev)
+    return out
+
+
+def long_context_rates(dev):
+    """fwd+bwd on the T = 131,072 long-context workload (512 saved states per head)."""
+    from backward_mamba_ssd_amd import inputs
+
     wl = inputs.WORKLOADS["long_b1_t131072"]
     log(f"long context: {wl.name}")
     r = time_fwd_bwd(wl, dev, steps=3, warmup=1)
@@ -540,7 +543,30 @@ def secondary(dev):
     lc = path_entry(fb * r["tokens"], by * r["tokens"], r["step"][1])
     lc["tokens_per_s"] = round(r["tokens"] * 3 / r["wall_s"], 1)
     lc["workload"] = wl.name
-    out["long_context_fwd_bwd"] = lc
+    return lc
+
+
+SECTIONS = {
+    "decode": decode_rates,
+    "dt_prep": dt_prep_rates,
+    "draft_rollback": draft_rollback_rates,
+    "around_scan": around_scan_rates,
+    "replay_sr16_b16": replay_sweep,
+    "long_context_fwd_bwd": long_context_rates,
+}
+
+
+def secondary(dev):
+    """Every path besides the fwd+bwd step: decode, SR16, time-step preparation, drafts and
+    rollback, the stages around the scan, the replay sweep and the long-context step."""
+    out = {}
+    for name, fn in SECTIONS.items():
+        log(f"{name} ...")
+        r = fn(dev)
+        if name == "decode":
+            out.update(r)
+        else:
+            out[name] = r
     return out
 
 
@@ -552,6 +578,8 @@ def main():
     ap.add_argument("--workload", default="prefill_b4_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--section", choices=sorted(SECTIONS),
+                    help="run only this secondary measurement and print its JSON (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (3 times), the known-size "
                          "reference for scaling HBM byte counters")
@@ -566,6 +594,10 @@ def main():
     from backward_mamba_ssd_amd import inputs
 
     dev = torch.device("cuda:0")
+    if args.section:
+        print(json.dumps({"section": args.section, **{"result": SECTIONS[args.section](dev)}}),
+              flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     log(f"workload {w.name}: batch {w.batch} T {w.seqlen} heads {w.nheads} P {w.headdim} "
         f"N {w.dstate} groups {w.ngroups} chunk {w.chunk}")
