@@ -24,9 +24,11 @@
 // the state once per saved chunk.  chunk_states[c] (state entering chunk c)
 // is stored whenever a block starts a chunk of L tokens (L % 64 == 0).
 //
-// One 512-thread workgroup (8 waves) per (batch, head), two per CU (LDS 71 KB,
-// at most 128 VGPRs: 16 waves per CU to hide the latency of the serial block
-// loop).  Wave w holds n-tile w of the state for all four p-tiles; the 10 causal
+// One 512-thread workgroup (8 waves) per (batch, head), two per CU (LDS exactly
+// 80 KB, at most 128 VGPRs: 16 waves per CU to hide the latency of the serial
+// block loop).  Every tile is staged in its natural [token][channel] row layout
+// with whole 16-byte row pieces per lane (no bank conflicts); the operands that
+// contract over tokens (X^T, Bs^T) are read with gfx950's transposing LDS load.  Wave w holds n-tile w of the state for all four p-tiles; the 10 causal
 // Gram tiles are spread so no wave computes more than two; each wave computes
 // two output tiles.  Workgroup ids are remapped so the heads of one group run on
 // the same XCD and share B/C in that XCD's L2.
@@ -39,15 +41,20 @@
 namespace ssm {
 namespace {
 
+// Row stride of the x tile: 40 dwords, so the four rows one transposing read spans
+// fall on distinct banks.
+constexpr int kSX = kLs + 16;
+
 struct __align__(16) FwdSmem {
     bf16_t C[kLs * kS128];    // [tok][n]
     bf16_t B[kLs * kS128];    // [tok][n]; after the Gram product: H in bf16, [p][n]
-    bf16_t BsT[kN * kS64];    // [n][tok] = B[tok][n] * exp(Lam_63 - Lam_tok) * dt_tok
-    bf16_t XT[kP * kS64];     // [p][tok]
+    bf16_t Bs[kLs * kS128];   // [tok][n] = B[tok][n] * exp(Lam_63 - Lam_tok) * dt_tok
+    bf16_t X[kLs * kSX];      // [tok][p]
     bf16_t Gm[kLs * kS64];    // [i][j] = (C_i.B_j) exp(Lam_i - Lam_j) dt_j for j <= i, else 0
     float2 ld[2][kLs];        // (Lam, dt) per token, double-buffered by block parity
     bf16_t Y[kLs * kS64];     // [tok][p]: the block's outputs, stored to HBM as whole rows
 };
+static_assert(sizeof(FwdSmem) <= 81920, "two workgroups per CU");
 
 __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -64,8 +71,6 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     const bf16_t *Bm = static_cast<const bf16_t *>(a.B);
     const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
     bf16_t *y = static_cast<bf16_t *>(a.y);
-    const bool lowhalf = wave < 4;          // waves 0-3 stage B; waves 4-7 stage C and x
-    const int sid = tid & 255;
 
     // state H^T: wave w owns n-tile w, all 4 p-tiles: n = 16w + lq + v, p = 16pt + lr
     f32x4 H[4];
@@ -79,9 +84,11 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
             H[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    const int xt0 = map64_tok(sid), xp0 = map64_col(sid);
-    const int bt0 = map128_tok(sid), bn0 = map128_col(sid);
-    u16x8 pre[6];   // low half: B rows (4); high half: C rows (4), x rows (2)
+    // staging map: B, C, Bs rows rt and rt + 32 from coordinate rc; x (and y) row xt from
+    // channel xc.  A wave covers whole rows, 16 contiguous bytes per lane.
+    const int rt = tid >> 4, rc = (tid & 15) * 8;
+    const int xt = tid >> 3, xc = (tid & 7) * 8;
+    u16x8 pre[5];   // B rows rt, rt + 32; C rows rt, rt + 32; x row xt
     float dtr = 0.f;
     const uint32_t tokx = static_cast<uint32_t>(a.H) * kP * 2;
     const uint32_t tokbc = static_cast<uint32_t>(a.G) * kN * 2;
@@ -98,17 +105,14 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     auto nvalid_of = [&](int64_t rem) { return static_cast<uint32_t>(rem < kLs ? rem : kLs); };
     auto prefetch = [&](int64_t rem) {  // rem: tokens from the prefetched block to the end
         const uint32_t nv = nvalid_of(rem);
-        if (lowhalf) {
-            const rsrc_t rb = make_rsrc(pB, nv * tokbc);
+        const rsrc_t rb = make_rsrc(pB, nv * tokbc), rcc = make_rsrc(pC, nv * tokbc);
+        const rsrc_t rx = make_rsrc(px, nv * tokx);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pre[i] = buf_ld_16b(rb, (bt0 + i) * tokbc + bn0 * 2);
-        } else {
-            const rsrc_t rc = make_rsrc(pC, nv * tokbc), rx = make_rsrc(px, nv * tokx);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pre[i] = buf_ld_16b(rc, (bt0 + i) * tokbc + bn0 * 2);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) pre[4 + i] = buf_ld_16b(rx, (xt0 + i) * tokx + xp0 * 2);
+        for (int i = 0; i < 2; ++i) {
+            pre[i] = buf_ld_16b(rb, (rt + 32 * i) * tokbc + rc * 2);
+            pre[2 + i] = buf_ld_16b(rcc, (rt + 32 * i) * tokbc + rc * 2);
         }
+        pre[4] = buf_ld_16b(rx, xt * tokx + xc * 2);
         if (tid < kLs) {
             const rsrc_t rd = make_rsrc(pdt, nv * a.H * 4u);
             dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
@@ -121,11 +125,10 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     // Outputs leave through LDS: each thread stores 16 bytes of one token row, so a
     // wave writes 8 tokens x 128 B (whole rows of this head) per instruction instead
     // of 16 tokens x 32 B from the MFMA accumulator layout.
-    const int yt = tid >> 3, yc = (tid & 7) * 8;  // token, first channel
     auto store_y = [&](int64_t tb) {
         const rsrc_t ry = make_rsrc(py, nvalid_of(T - tb) * tokx);
-        const u16x8 v = *reinterpret_cast<const u16x8 *>(&sm.Y[yt * kS64 + yc]);
-        buf_st_16b(ry, static_cast<uint32_t>(yt) * tokx + yc * 2, v);
+        const u16x8 v = *reinterpret_cast<const u16x8 *>(&sm.Y[xt * kS64 + xc]);
+        buf_st_16b(ry, static_cast<uint32_t>(xt) * tokx + xc * 2, v);
         py += sx;
     };
     // Gram tile assignment (i-tile, j-tiles): every tile with j <= i once, plus the two
@@ -148,31 +151,23 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
         if (s > 0) store_y(t0 - kLs);  // the previous block's outputs, complete since the barrier
         const float2 *ld = sm.ld[buf];
         const float lam_end = ld[kLs - 1].x;
-        // (2) stage the block in LDS: waves 0-3 B and Bs^T, waves 4-7 C and X^T
-        if (lowhalf) {
+        // (2) stage the block in LDS: B, C, Bs = B scaled per token, x
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<u16x8 *>(&sm.B[(bt0 + i) * kS128 + bn0]) = pre[i];
-            float coef[4];
-            const float4 l01 = *reinterpret_cast<const float4 *>(&ld[bt0]);
-            const float4 l23 = *reinterpret_cast<const float4 *>(&ld[bt0 + 2]);
-            coef[0] = __expf(lam_end - l01.x) * l01.y;
-            coef[1] = __expf(lam_end - l01.z) * l01.w;
-            coef[2] = __expf(lam_end - l23.x) * l23.y;
-            coef[3] = __expf(lam_end - l23.z) * l23.w;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<u16x4 *>(&sm.BsT[(bn0 + e) * kS64 + bt0]) =
-                    pack4(bf16_to_f32(pre[0][e]) * coef[0], bf16_to_f32(pre[1][e]) * coef[1],
-                          bf16_to_f32(pre[2][e]) * coef[2], bf16_to_f32(pre[3][e]) * coef[3]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<u16x8 *>(&sm.C[(bt0 + i) * kS128 + bn0]) = pre[i];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t pr = static_cast<uint32_t>(pre[4][e]) | (static_cast<uint32_t>(pre[5][e]) << 16);
-                *reinterpret_cast<uint32_t *>(&sm.XT[(xp0 + e) * kS64 + xt0]) = pr;
-            }
+        for (int i = 0; i < 2; ++i) {
+            const int r = rt + 32 * i;
+            *reinterpret_cast<u16x8 *>(&sm.B[r * kS128 + rc]) = pre[i];
+            *reinterpret_cast<u16x8 *>(&sm.C[r * kS128 + rc]) = pre[2 + i];
+            const float2 lt = ld[r];
+            const float cf = __expf(lam_end - lt.x) * lt.y;
+            const u16x8 v = pre[i];
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * cf, bf16_to_f32(v[1]) * cf),
+                             pack2_bf16(bf16_to_f32(v[2]) * cf, bf16_to_f32(v[3]) * cf),
+                             pack2_bf16(bf16_to_f32(v[4]) * cf, bf16_to_f32(v[5]) * cf),
+                             pack2_bf16(bf16_to_f32(v[6]) * cf, bf16_to_f32(v[7]) * cf)};
+            *reinterpret_cast<u32x4 *>(&sm.Bs[r * kS128 + rc]) = w;
         }
+        *reinterpret_cast<u16x8 *>(&sm.X[xt * kSX + xc]) = pre[4];
         // state entering a chunk of L tokens
         if (cs != nullptr && kc == 0) {
 #pragma unroll
@@ -236,7 +231,7 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) fh[kk] = frag_row(&Hb[prow * kS128 + 32 * kk + lk]);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) fx[kk] = frag_row(&sm.XT[prow * kS64 + 32 * kk + lk]);
+            for (int kk = 0; kk < 2; ++kk) fx[kk] = frag_tr(sm.X, kSX, 16 * pw, 32 * kk, lane);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int tt = 2 * ih + q;
@@ -265,10 +260,10 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
                 for (int v = 0; v < 4; ++v) H[pt][v] *= el;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 fb = frag_row(&sm.BsT[(16 * wave + lr) * kS64 + 32 * kk + lk]);
+                const bf16x8 fb = frag_tr(sm.Bs, kS128, 16 * wave, 32 * kk, lane);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
-                    H[pt] = mfma(fb, frag_row(&sm.XT[(16 * pt + lr) * kS64 + 32 * kk + lk]), H[pt]);
+                    H[pt] = mfma(fb, frag_tr(sm.X, kSX, 16 * pt, 32 * kk, lane), H[pt]);
             }
         }
     }
