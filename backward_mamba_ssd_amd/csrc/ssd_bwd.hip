@@ -46,9 +46,14 @@ namespace {
 // ===========================================================================
 // 1. reverse pass of the state gradient
 // ===========================================================================
+// Both tiles keep the natural [tok][channel] layout and are read with the transposing
+// LDS load; their row strides (72 and 40 dwords) put the four rows one such read spans
+// on distinct banks, and a wave's 16-byte row writes are conflict-free.
+constexpr int kSC = kN + 16;
+constexpr int kSY = kP + 16;
 struct DstSmem {
-    bf16_t CT[kN * kS64];    // [n][tok]
-    bf16_t EdYT[kP * kS64];  // [p][tok] = dy[tok][p] * exp(Lam_tok)
+    bf16_t C[kLs * kSC];     // [tok][n]
+    bf16_t EdY[kLs * kSY];   // [tok][p] = dy[tok][p] * exp(Lam_tok)
     float lam[2][kLs];
 };
 
@@ -76,8 +81,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
             G[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    const int yt0 = map64_tok(tid), yp0 = map64_col(tid);    // dy: 2 tokens x 8 channels
-    const int ct0 = map128_tok(tid), cn0 = map128_col(tid);  // C: 4 tokens x 8 coords
+    // staging map: dy rows yt0 + 32i from channel yp0; C rows ct0 + 16i from coordinate cn0
+    const int yt0 = tid >> 3, yp0 = (tid & 7) * 8;
+    const int ct0 = tid >> 4, cn0 = (tid & 15) * 8;
     // A block's rows in registers, loaded two blocks ahead: the loop is unrolled by two
     // so the two register sets alternate without copies (a copy of a loaded register
     // would wait for the load).
@@ -100,9 +106,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
         const rsrc_t ry = make_rsrc(dy0 + s * sy, nv * toky);
         const rsrc_t rc = make_rsrc(C0 + s * sc, nv * tokc);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) R.yr[i] = buf_ld_16b(ry, (yt0 + i) * toky + yp0 * 2);
+        for (int i = 0; i < 2; ++i) R.yr[i] = buf_ld_16b(ry, (yt0 + 32 * i) * toky + yp0 * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R.cr[i] = buf_ld_16b(rc, (ct0 + i) * tokc + cn0 * 2);
+        for (int i = 0; i < 4; ++i) R.cr[i] = buf_ld_16b(rc, (ct0 + 16 * i) * tokc + cn0 * 2);
         R.dtr = 0.f;
         if (tid < kLs) {
             const rsrc_t rd = make_rsrc(dt0 + s * sd, nv * a.H * 4u);
@@ -129,17 +135,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
         const float *lam = sm.lam[buf];
         const float lam_end = lam[kLs - 1];
         {
-            const float e0 = __expf(lam[yt0]), e1 = __expf(lam[yt0 + 1]);
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                *reinterpret_cast<uint32_t *>(&sm.EdYT[(yp0 + e) * kS64 + yt0]) =
-                    pack2_bf16(bf16_to_f32(R.yr[0][e]) * e0, bf16_to_f32(R.yr[1][e]) * e1);
+            for (int i = 0; i < 2; ++i) {
+                const float e = __expf(lam[yt0 + 32 * i]);
+                const u16x8 v = R.yr[i];
+                const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * e, bf16_to_f32(v[1]) * e),
+                                 pack2_bf16(bf16_to_f32(v[2]) * e, bf16_to_f32(v[3]) * e),
+                                 pack2_bf16(bf16_to_f32(v[4]) * e, bf16_to_f32(v[5]) * e),
+                                 pack2_bf16(bf16_to_f32(v[6]) * e, bf16_to_f32(v[7]) * e)};
+                *reinterpret_cast<u32x4 *>(&sm.EdY[(yt0 + 32 * i) * kSY + yp0]) = w;
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const u16x4 v = {R.cr[0][e], R.cr[1][e], R.cr[2][e], R.cr[3][e]};
-                *reinterpret_cast<u16x4 *>(&sm.CT[(cn0 + e) * kS64 + ct0]) = v;
-            }
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u16x8 *>(&sm.C[(ct0 + 16 * i) * kSC + cn0]) = R.cr[i];
         }
         if (s >= 2) prefetch(R, s - 2);
         __syncthreads();
@@ -152,8 +161,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
             for (int v = 0; v < 4; ++v) acc[v] *= el;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                acc = mma16(&sm.CT[(16 * nt + lr) * kS64 + 32 * kk + lk],
-                            &sm.EdYT[(16 * pt + lr) * kS64 + 32 * kk + lk], acc);
+                acc = mfma(frag_tr(sm.C, kSC, 16 * nt, 32 * kk, lane),
+                           frag_tr(sm.EdY, kSY, 16 * pt, 32 * kk, lane), acc);
             G[q] = acc;
         }
     };

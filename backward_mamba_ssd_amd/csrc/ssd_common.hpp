@@ -119,15 +119,4 @@ __device__ __forceinline__ u16x4 pack4(float a, float b, float c, float d) {
     return __builtin_bit_cast(u16x4, w);
 }
 
-// Staging thread maps (256 threads).  Transposed LDS writes are the bank-hot
-// accesses; these maps spread one wave's lanes over all 64 banks.
-//  [tok][p] source rows -> [p][tok] tile: thread covers 2 tokens x 8 channels,
-//  lanes of a wave vary the token pair (32 pairs) and 2 channel blocks.
-__device__ __forceinline__ int map64_tok(int tid) { return 2 * (tid & 31); }
-__device__ __forceinline__ int map64_col(int tid) { return 8 * ((tid >> 5) & 1) + 16 * (tid >> 6); }
-//  [tok][n] source rows -> [n][tok] tile: thread covers 4 tokens x 8 coords,
-//  lanes vary the token quad (16 quads) and 4 coordinate blocks.
-__device__ __forceinline__ int map128_tok(int tid) { return 4 * (tid & 15); }
-__device__ __forceinline__ int map128_col(int tid) { return 8 * ((tid >> 4) & 3) + 32 * (tid >> 6); }
-
 }  // namespace ssm
