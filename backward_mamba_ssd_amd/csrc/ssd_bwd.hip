@@ -448,7 +448,11 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const float2 *ld = sm.ld[par];  // (Lam, dt) of this head's chunk
         const float lam_blk0 = kS >= 0 ? ld[kS].x : 0.f;  // block-local Lam_i = Lam[base+i] - lam_blk0
         const float lam_e = ld[kE].x;
-        if (hh + 1 < hpg) prefetch_dt(h + 1);  // used by the next head's scan in S3
+        // The next head's loads are issued on every iteration (the last one re-reads its own
+        // head), so each iteration issues the same memory operations and the waits on them
+        // count exactly instead of draining everything in flight.
+        const int hn = (hh + 1 < hpg) ? h + 1 : h;
+        prefetch_dt(hn);  // used by the next head's scan in S3
         // ---- S1: stage this head's rows (scaled for the state products) ----
 #pragma unroll
         for (int kb = 0; kb < kMaxBlk; ++kb) {
@@ -471,7 +475,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             *reinterpret_cast<u32x4 *>(&sm.R[slot * kT64 + pr_tok * kS64 + pr_col]) = w;
         }
         __syncthreads();
-        if (hh + 1 < hpg) prefetch(h + 1);  // registers are free once staged
+        prefetch(hn);  // registers are free once staged
         // ---- S2: state products over the other blocks; Phase I of block k ----
         if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
         // Each A fragment (16 state rows n of one block's B or C) is read once and used
@@ -579,12 +583,10 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             dotp = wave_total(dotp);
             if (lane == 0) sm.dot[wave] = dotp;
         }
-        if (hh + 1 < hpg) {
-            load_states(h + 1);
-            // the other parity slot is free: this head reads only lam[par], dt[par], and
-            // the barrier below publishes the next head's values before its first use
-            if (wave == 0) scan(h + 1, par ^ 1);
-        }
+        load_states(hn);
+        // the other parity slot is free: this head reads only lam[par], dt[par], and
+        // the barrier below publishes the next head's values before its first use
+        if (wave == 0) scan(hn, par ^ 1);
         __syncthreads();
         // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tiles 2wh, 2wh+1) ----
         {
