@@ -51,6 +51,14 @@ namespace {
 // on distinct banks, and a wave's 16-byte row writes are conflict-free.
 constexpr int kSC = kN + 16;
 constexpr int kSY = kP + 16;
+// Offset (floats) of lane `lane`'s four accumulator values of state tile (n-tile nt,
+// p-tile pt) in one chunk's gradient of the workspace: 32 tiles of 16 x 16 floats in
+// n-tile-major order, each as 64 lanes x 4 floats (lane l holds p = 16 pt + l % 16,
+// n = 16 nt + 4 (l / 16) + 0..3).
+__device__ __forceinline__ int dstate_tile(int nt, int pt, int lane) {
+    return (nt * (kP / 16) + pt) * 256 + lane * 4;
+}
+
 struct DstSmem {
     bf16_t C[kLs * kSC];     // [tok][n]
     bf16_t EdY[kLs * kSY];   // [tok][p] = dy[tok][p] * exp(Lam_tok)
@@ -122,12 +130,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     auto step = [&](int s, Rows &R) {
         const int buf = s & 1;
         if (s == nblk - 1 || (s + 1) % bpc == 0) {
-            // gradient on the state leaving chunk c (everything after it)
+            // gradient on the state leaving chunk c (everything after it), stored tile by
+            // tile in accumulator lane order: a wave writes whole 1 KB tiles and the
+            // per-block kernel reads them back with the same lane map
             float *dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
-                *reinterpret_cast<float4 *>(dst + p * kN + n) = make_float4(G[q][0], G[q][1], G[q][2], G[q][3]);
+                const int nt = 2 * wave + q / 4, pt = q % 4;
+                *reinterpret_cast<float4 *>(dst + dstate_tile(nt, pt, lane)) = make_float4(G[q][0], G[q][1], G[q][2], G[q][3]);
             }
         }
         if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(R.dtr * Ah);
@@ -345,9 +355,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         for (int q = 0; q < 4; ++q) {
             const int n = 16 * (2 * wq + (q >> 1)) + lq, p = 16 * (2 * wh + (q & 1)) + lr;
             const float4 u = *reinterpret_cast<const float4 *>(hc + p * kN + n);
-            const float4 v = *reinterpret_cast<const float4 *>(dc + p * kN + n);
+            const float4 v = *reinterpret_cast<const float4 *>(dc + dstate_tile(2 * wq + (q >> 1), 2 * wh + (q & 1), lane));
             Hs[q] = f32x4{u.x, u.y, u.z, u.w};
-            dHs[q] = f32x4{v.x, v.y, v.z, v.w};
+            dHs[q] = f32x4{v.x, v.y, v.z, v.w};  // (from the tile-ordered workspace)
         }
     };
 
