@@ -28,9 +28,10 @@
 // 80 KB, at most 128 VGPRs: 16 waves per CU to hide the latency of the serial
 // block loop).  Every tile is staged in its natural [token][channel] row layout
 // with whole 16-byte row pieces per lane (no bank conflicts); the operands that
-// contract over tokens (X^T, Bs^T) are read with gfx950's transposing LDS load.  Wave w holds n-tile w of the state for all four p-tiles; the 10 causal
-// Gram tiles are spread so no wave computes more than two; each wave computes
-// two output tiles.  Workgroup ids are remapped so the heads of one group run on
+// contract over tokens (X^T, Bs^T) are read with gfx950's transposing LDS load.
+// Each wave holds 2 x 2 tiles of the state and computes two output tiles of one
+// p-tile (one of its state p-tiles, so the X^T fragments serve both products); the
+// 10 causal Gram tiles are spread so no wave computes more than two.  Workgroup ids are remapped so the heads of one group run on
 // the same XCD and share B/C in that XCD's L2.
 //
 // MFMA tiles follow the "NT" convention of ssd_common.hpp.
@@ -72,16 +73,22 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
     bf16_t *y = static_cast<bf16_t *>(a.y);
 
-    // state H^T: wave w owns n-tile w, all 4 p-tiles: n = 16w + lq + v, p = 16pt + lr
+    // Output tiles Y^T of wave w: p-tile pw, token tiles 2 ih + {0, 1}.  State H^T of wave w:
+    // tile q = n-tile 2 (w % 4) + q / 2, p-tile pw ^ (q % 2) (the output's p-tile and its
+    // neighbour), so the state update reuses the X^T fragments the output product read.
+    // Lane layout of a state tile: n = 16 nt + lq + v, p = 16 pt + lr.
+    const int pw = 2 * (wave >> 2) + (wave & 1), ih = (wave >> 1) & 1;
+    auto st_n = [&](int q) { return 16 * (2 * (wave & 3) + (q >> 1)) + lq; };
+    auto st_p = [&](int q) { return 16 * (pw ^ (q & 1)) + lr; };
     f32x4 H[4];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-        const int n = 16 * wave + lq, p = 16 * pt + lr;
+    for (int q = 0; q < 4; ++q) {
+        const int n = st_n(q), p = st_p(q);
         if (a.h0 != nullptr) {
             const float4 v = *reinterpret_cast<const float4 *>(a.h0 + (static_cast<int64_t>(bh) * kP + p) * kN + n);
-            H[pt] = f32x4{v.x, v.y, v.z, v.w};
+            H[q] = f32x4{v.x, v.y, v.z, v.w};
         } else {
-            H[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            H[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     // staging map: B, C, Bs rows rt and rt + 32 from coordinate rc; x (and y) row xt from
@@ -171,9 +178,9 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
         // state entering a chunk of L tokens
         if (cs != nullptr && kc == 0) {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int n = 16 * wave + lq, p = 16 * pt + lr;
-                *reinterpret_cast<float4 *>(cs + p * kN + n) = make_float4(H[pt][0], H[pt][1], H[pt][2], H[pt][3]);
+            for (int q = 0; q < 4; ++q) {
+                const int n = st_n(q), p = st_p(q);
+                *reinterpret_cast<float4 *>(cs + p * kN + n) = make_float4(H[q][0], H[q][1], H[q][2], H[q][3]);
             }
             cs += kP * kN;
         }
@@ -217,15 +224,14 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
         // (4) H in bf16 over the consumed B rows: [p][n]
         bf16_t *Hb = sm.B;
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const int n = 16 * wave + lq, p = 16 * pt + lr;
-            *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(H[pt][0], H[pt][1], H[pt][2], H[pt][3]);
+        for (int q = 0; q < 4; ++q) {
+            const int n = st_n(q), p = st_p(q);
+            *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(H[q][0], H[q][1], H[q][2], H[q][3]);
         }
         __syncthreads();
-        // (5) outputs Y^T: p-tile (w & 3), token tiles 2*(w >> 2) + {0, 1}; the wave's H and
-        //     X^T fragments are read once for both
+        // (5) outputs Y^T: p-tile pw, token tiles 2 ih + {0, 1}; the wave's H and X^T
+        //     fragments are read once for both, and X^T again serves the state update
         {
-            const int pw = wave & 3, ih = wave >> 2;
             const int prow = 16 * pw + lr;
             bf16x8 fh[4], fx[2];
 #pragma unroll
@@ -250,20 +256,21 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
                 }
                 *reinterpret_cast<u16x4 *>(&sm.Y[tok * kS64 + 16 * pw + lq]) = pack4(acc[0], acc[1], acc[2], acc[3]);
             }
-        }
-        // (6) state update H^T = exp(Lam_63) H^T + Bs^T X on the wave's n-tile
-        {
+            // (6) state update H^T = exp(Lam_63) H^T + Bs^T X on the wave's 2 x 2 state tiles
             const float el = __expf(lam_end);
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) H[pt][v] *= el;
+                for (int v = 0; v < 4; ++v) H[q][v] *= el;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 fb = frag_tr(sm.Bs, kS128, 16 * wave, 32 * kk, lane);
+                const bf16x8 fo = frag_tr(sm.X, kSX, 16 * (pw ^ 1), 32 * kk, lane);  // the other p-tile
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    H[pt] = mfma(fb, frag_tr(sm.X, kSX, 16 * pt, 32 * kk, lane), H[pt]);
+                for (int t = 0; t < 2; ++t) {
+                    const bf16x8 fb = frag_tr(sm.Bs, kS128, 16 * (2 * (wave & 3) + t), 32 * kk, lane);
+                    H[2 * t] = mfma(fb, fx[kk], H[2 * t]);
+                    H[2 * t + 1] = mfma(fb, fo, H[2 * t + 1]);
+                }
             }
         }
     }
@@ -271,10 +278,10 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     if (nblk > 0) store_y((nblk - 1) * kLs);
     if (a.h_final != nullptr) {
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const int n = 16 * wave + lq, p = 16 * pt + lr;
+        for (int q = 0; q < 4; ++q) {
+            const int n = st_n(q), p = st_p(q);
             *reinterpret_cast<float4 *>(a.h_final + (static_cast<int64_t>(bh) * kP + p) * kN + n) =
-                make_float4(H[pt][0], H[pt][1], H[pt][2], H[pt][3]);
+                make_float4(H[q][0], H[q][1], H[q][2], H[q][3]);
         }
     }
 }
