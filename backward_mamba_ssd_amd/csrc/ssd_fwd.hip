@@ -35,6 +35,8 @@
 // the same XCD and share B/C in that XCD's L2.
 //
 // MFMA tiles follow the "NT" convention of ssd_common.hpp.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "ssd_common.hpp"
@@ -290,13 +292,18 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
 
 hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s) {
     const size_t smem = sizeof(FwdSmem);
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ssd_fwd_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(smem));
+    // The dynamic-LDS limit is a per-device attribute of the kernel: set it once on
+    // every device this process launches on.
+    static std::atomic<uint64_t> configured{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (bit == 0 || (configured.load() & bit) == 0) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ssd_fwd_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
         if (e != hipSuccess) return e;
-        configured = true;
+        configured.fetch_or(bit);
     }
     const unsigned grid = static_cast<unsigned>(a.Bsz * a.H);
     ssd_fwd_kernel<<<grid, 512, smem, s>>>(a);
