@@ -145,7 +145,7 @@ __device__ __forceinline__ float wave_suffix_sum(float v) {
     return lane_reverse(wave_prefix_sum(lane_reverse(v)));
 }
 
-// Sum / max over aligned groups of W lanes (W = 4, 8, 16, 32, 64); every lane of a
+// Sum / max over aligned groups of W lanes (W = 2, 4, 8, 16, 32, 64); every lane of a
 // group gets the group's result, in a fixed order.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -154,9 +154,9 @@ __device__ __forceinline__ float dpp_mov(float x) {
 template <int W, bool MAX>
 __device__ __forceinline__ float lane_group_reduce(float v) {
     auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
-    static_assert(W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
+    static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
     v = op(v, dpp_mov<0xB1>(v));                              // quad_perm [1,0,3,2]
-    v = op(v, dpp_mov<0x4E>(v));                              // quad_perm [2,3,0,1]
+    if constexpr (W >= 4) v = op(v, dpp_mov<0x4E>(v));        // quad_perm [2,3,0,1]
     if constexpr (W >= 8) v = op(v, dpp_mov<0x141>(v));       // row_half_mirror
     if constexpr (W >= 16) v = op(v, dpp_mov<0x140>(v));      // row_mirror
     if constexpr (W >= 32) {

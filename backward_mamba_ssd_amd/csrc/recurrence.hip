@@ -60,21 +60,30 @@ __device__ __forceinline__ float4 scale4(const float4 &v, float s) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one (batch, head) per workgroup, MAXR row passes unrolled so all
-// state loads are in flight before the arithmetic.  With SR16 the state lives in
+// Decode: one (batch, head) per workgroup, all row passes unrolled so all state
+// loads are in flight before the arithmetic.  With SR16 the state lives in
 // binary16: it is widened exactly, updated in float32 with the same arithmetic,
 // and stored back stochastically rounded ("Nemotron 3 Ultra: replaying a rounded
 // state": the quantized model keeps its recurrent state cache in FP16 with
 // stochastic rounding), element e of the state using entropy (seed, key, e).
+// A lane holds CPL consecutive coordinates of a row: 4 for the float32 state
+// (16-byte accesses), 8 for the binary16 one (16-byte accesses too, so the binary16
+// cache needs half the memory instructions).  With 8 the lane first adds its two
+// 4-coordinate partial sums and the row reduction runs over half as many lanes: the
+// same pairs are added in the same tree as with 4, so y is bit-identical to the
+// float32 decode of the same (widened) state.
 // ---------------------------------------------------------------------------
 template <int N, int MAXR, typename T, bool SR16>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
-    constexpr int LPR = N / 4;
-    constexpr int RPW = 256 / LPR;
+    constexpr int CPL = SR16 ? 8 : 4;          // coordinates per lane
+    constexpr int NV = CPL / 4;                // float4 sub-vectors per lane
+    constexpr int LPR = N / CPL;               // lanes per state row
+    constexpr int RPW = 256 / LPR;             // rows per pass
+    constexpr int NPASS = MAXR * 4 / CPL;      // passes (same row capacity for both CPL)
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x;
-    const int n0 = (tid % LPR) * 4;
+    const int n0 = (tid % LPR) * CPL;
     const int r0 = tid / LPR;
     const T *x = static_cast<const T *>(a.x);
     const T *Bm = static_cast<const T *>(a.B);
@@ -83,20 +92,24 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     float *st = SR16 ? nullptr : a.state + row_base * N;
     uint16_t *st16 = SR16 ? a.state16 + row_base * N : nullptr;
 
-    float4 s[MAXR];
+    float4 s[NPASS][NV];
 #pragma unroll
-    for (int i = 0; i < MAXR; ++i) {
+    for (int i = 0; i < NPASS; ++i) {
         const int p = r0 + i * RPW;
-        s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < NV; ++q) s[i][q] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (p < a.P) {
             if constexpr (SR16) {
                 // binary16 -> float32 is exact; convert the whole vector (an element-wise
                 // bit_cast of a vector subscript is not reliable here)
-                const h16x4 hv = __builtin_nontemporal_load(reinterpret_cast<const h16x4 *>(st16 + static_cast<int64_t>(p) * N + n0));
-                const f32x4 fv = __builtin_convertvector(hv, f32x4);
-                s[i] = make_float4(fv[0], fv[1], fv[2], fv[3]);
+                typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+                typedef float f32x8 __attribute__((ext_vector_type(8)));
+                const h16x8 hv = __builtin_nontemporal_load(reinterpret_cast<const h16x8 *>(st16 + static_cast<int64_t>(p) * N + n0));
+                const f32x8 fv = __builtin_convertvector(hv, f32x8);
+                s[i][0] = make_float4(fv[0], fv[1], fv[2], fv[3]);
+                s[i][1] = make_float4(fv[4], fv[5], fv[6], fv[7]);
             } else {
-                s[i] = nt_ld4(st + static_cast<int64_t>(p) * N + n0);
+                s[i][0] = nt_ld4(st + static_cast<int64_t>(p) * N + n0);
             }
         }
     }
@@ -104,27 +117,34 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const float av = retention(dtv, a.A[h]);
     const float Dh = a.D[h];
     const int64_t bgN = (static_cast<int64_t>(b) * a.G + g) * N + n0;
-    const float4 bdt = scale4(IO<T>::ld4(Bm, bgN), dtv);
-    const float4 c = IO<T>::ld4(Cm, bgN);
+    float4 bdt[NV], c[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        bdt[q] = scale4(IO<T>::ld4(Bm, bgN + 4 * q), dtv);
+        c[q] = IO<T>::ld4(Cm, bgN + 4 * q);
+    }
     const uint64_t sub = SR16 ? sr16_stream(a.seed, a.key) : 0ull;
 #pragma unroll
-    for (int i = 0; i < MAXR; ++i) {
+    for (int i = 0; i < NPASS; ++i) {
         if (i * RPW >= a.P) break;  // uniform: no row of this pass exists
         const int p = r0 + i * RPW;
         const float xp = (p < a.P) ? IO<T>::ld(x, static_cast<int64_t>(bh) * a.P + p) : 0.f;
-        float acc = row_step(s[i], av, xp, bdt, c);
+        float acc = row_step(s[i][0], av, xp, bdt[0], c[0]);
+        if constexpr (NV == 2) acc = acc + row_step(s[i][1], av, xp, bdt[1], c[1]);
         acc = row_reduce<LPR>(acc);  // whole rows are active or inactive together
         if (p < a.P) {
             if constexpr (SR16) {
                 const uint64_t e0 = static_cast<uint64_t>(row_base + p) * N + n0;  // element index
-                u16x4 o;
-                o[0] = sr16_bits(s[i].x, sr16_entropy(sub, e0 + 0));
-                o[1] = sr16_bits(s[i].y, sr16_entropy(sub, e0 + 1));
-                o[2] = sr16_bits(s[i].z, sr16_entropy(sub, e0 + 2));
-                o[3] = sr16_bits(s[i].w, sr16_entropy(sub, e0 + 3));
-                __builtin_nontemporal_store(o, reinterpret_cast<u16x4 *>(st16 + static_cast<int64_t>(p) * N + n0));
+                uint32_t u[8];
+                sr16_entropy_run<8>(sub, e0, u);
+                const float v[8] = {s[i][0].x, s[i][0].y, s[i][0].z, s[i][0].w,
+                                    s[i][1].x, s[i][1].y, s[i][1].z, s[i][1].w};
+                u16x8 o;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = sr16_bits(v[j], u[j]);
+                __builtin_nontemporal_store(o, reinterpret_cast<u16x8 *>(st16 + static_cast<int64_t>(p) * N + n0));
             } else {
-                nt_st4(st + static_cast<int64_t>(p) * N + n0, s[i]);
+                nt_st4(st + static_cast<int64_t>(p) * N + n0, s[i][0]);
             }
             if ((tid % LPR) == 0)
                 IO<T>::st(static_cast<T *>(a.y), static_cast<int64_t>(bh) * a.P + p,

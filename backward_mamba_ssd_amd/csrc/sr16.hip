@@ -10,7 +10,7 @@
 namespace ssm {
 
 __global__ void __launch_bounds__(256) sr16_kernel(Sr16Args a) {
-    const uint64_t sub = sm64_mix(a.seed + (a.ckpt + 1ull) * kGamma);
+    const uint64_t sub = sr16_stream(a.seed, a.ckpt);
     const uint64_t i0 = (static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8ull;
     if (i0 >= a.n) return;
     if (i0 + 8 <= a.n && (reinterpret_cast<uintptr_t>(a.in + i0) & 15u) == 0 &&
@@ -19,18 +19,15 @@ __global__ void __launch_bounds__(256) sr16_kernel(Sr16Args a) {
         const float4 v1 = nt_ld4(a.in + i0 + 4);
         const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
         u16x8 o;
+        uint32_t u[8];
+        sr16_entropy_run<8>(sub, a.offset + i0, u);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint64_t e = a.offset + i0 + j;
-            const uint32_t u = static_cast<uint32_t>(sm64_mix(sub + (e + 1ull) * kGamma) >> 32);
-            o[j] = sr16_bits(vv[j], u);
-        }
+        for (int j = 0; j < 8; ++j) o[j] = sr16_bits(vv[j], u[j]);
         __builtin_nontemporal_store(o, reinterpret_cast<u16x8 *>(a.out + i0));
     } else {
         for (uint64_t i = i0; i < a.n && i < i0 + 8; ++i) {
             const uint64_t e = a.offset + i;
-            const uint32_t u = static_cast<uint32_t>(sm64_mix(sub + (e + 1ull) * kGamma) >> 32);
-            a.out[i] = sr16_bits(a.in[i], u);
+            a.out[i] = sr16_bits(a.in[i], sr16_entropy(sub, e));
         }
     }
 }

@@ -34,27 +34,40 @@ __device__ __forceinline__ uint16_t sr16_bits(float v, uint32_t u) {
     const uint32_t mag = b & 0x7FFFFFFFu;
     if (mag > 0x7F800000u) return static_cast<uint16_t>(sign | 0x7E00u);  // NaN
     if (mag >= 0x47800000u) return static_cast<uint16_t>(sign | 0x7C00u); // >= 65536, Inf
-    const uint32_t e = mag >> 23;             // biased float32 exponent
-    if (e == 0) return static_cast<uint16_t>(sign);  // zero / float32 subnormal: R = 0
-    const uint32_t sig = (mag & 0x7FFFFFu) | 0x800000u;  // 24-bit significand
-    uint32_t k, R;
-    if (e >= 113) {
-        // binary16 normal binade: spacing 2^(e-127-10); 13 discarded bits
-        k = sig >> 13;
-        R = (sig & 0x1FFFu) << 19;
-        k += (u < R) ? 1u : 0u;
-        // exponent field (e-112) and mantissa (k-1024); k == 2048 carries into
-        // the next binade and into infinity (0x7C00) at the top.
-        return static_cast<uint16_t>(sign | (((e - 112u) << 10) + (k - 1024u)));
-    }
-    // binary16 subnormal range: spacing 2^-24; shift = 126 - e >= 14
-    const uint32_t sh = 126u - e;
-    if (sh >= 56u) return static_cast<uint16_t>(sign);  // remainder < 2^-32: never up
-    k = (sh >= 32u) ? 0u : (sig >> sh);
-    uint64_t rem = static_cast<uint64_t>(sig) & ((1ull << sh) - 1ull);
-    R = static_cast<uint32_t>(sh <= 32u ? (rem << (32u - sh)) : (rem >> (sh - 32u)));
-    k += (u < R) ? 1u : 0u;  // k <= 1024: 1024 is the smallest normal's bit pattern
-    return static_cast<uint16_t>(sign | k);
+    // One form for both binary16 ranges.  The float32 significand (24 bits) is shifted
+    // onto the binary16 grid of its binade: by 13 bits in the normal range (biased
+    // float32 exponent e >= 113) and by 126 - e bits below it (spacing 2^-24).  k is
+    // the kept integer, R the discarded bits scaled to 32 bits (floor; 0 once the shift
+    // reaches 56, i.e. remainder < 2^-32, and for zeros and float32 subnormals, e = 0);
+    // k + 1 is taken iff u < R.  The result is the exponent field (e - 113 in the
+    // normal range, 0 below) shifted by 10 plus k, so that k = 2048 carries into the
+    // next binade and into infinity at the top, and k = 1024 below the normal range is
+    // the smallest normal's bit pattern.  (The rare cases stay branches: a wave skips
+    // them when none of its lanes needs them.)
+    const uint32_t e = mag >> 23;
+    const uint32_t sig = (mag & 0x7FFFFFu) | 0x800000u;
+    const bool normal = e >= 113u;
+    const uint32_t es = normal ? e - 113u : 0u;
+    const uint32_t sh = normal ? 13u : 126u - e;
+    const uint32_t k = sh >= 32u ? 0u : (sig >> sh);
+    const uint32_t R = sh >= 56u ? 0u : (sh <= 32u ? (sig << (32u - sh)) : (sig >> (sh - 32u)));
+    return static_cast<uint16_t>(sign | ((es << 10) + k + (u < R ? 1u : 0u)));
+}
+
+// The high 32 bits of sm64_mix(z), computed on 32-bit halves (the same value bit for
+// bit): only the high word of the second product is needed, and the high word of
+// z ^ (z >> 31) is hi ^ (hi >> 31).
+__device__ __forceinline__ uint32_t sm64_mix_hi(uint64_t z) {
+    const uint32_t zl = static_cast<uint32_t>(z), zh = static_cast<uint32_t>(z >> 32);
+    const uint32_t yl = zl ^ ((zl >> 30) | (zh << 2)), yh = zh ^ (zh >> 30);
+    constexpr uint32_t c1l = 0x1CE4E5B9u, c1h = 0xBF58476Du;  // 0xBF58476D1CE4E5B9
+    const uint64_t p = static_cast<uint64_t>(yl) * c1l;
+    const uint32_t ml = static_cast<uint32_t>(p);
+    const uint32_t mh = static_cast<uint32_t>(p >> 32) + yl * c1h + yh * c1l;
+    const uint32_t wl = ml ^ ((ml >> 27) | (mh << 5)), wh = mh ^ (mh >> 27);
+    constexpr uint32_t c2l = 0x133111EBu, c2h = 0x94D049BBu;  // 0x94D049BB133111EB
+    const uint32_t hi = __umulhi(wl, c2l) + wl * c2h + wh * c2l;
+    return hi ^ (hi >> 31);
 }
 
 // u for element e under (seed, key): sub = sr16_stream(seed, key) once per call
@@ -62,7 +75,18 @@ __device__ __forceinline__ uint64_t sr16_stream(uint64_t seed, uint64_t key) {
     return sm64_mix(seed + (key + 1ull) * kGamma);
 }
 __device__ __forceinline__ uint32_t sr16_entropy(uint64_t sub, uint64_t e) {
-    return static_cast<uint32_t>(sm64_mix(sub + (e + 1ull) * kGamma) >> 32);
+    return sm64_mix_hi(sub + (e + 1ull) * kGamma);
+}
+// u for the K consecutive elements e .. e+K-1: the stream counter advances by one
+// gamma per element, so only the first needs a 64-bit multiply.
+template <int K>
+__device__ __forceinline__ void sr16_entropy_run(uint64_t sub, uint64_t e, uint32_t (&u)[K]) {
+    uint64_t z = sub + (e + 1ull) * kGamma;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        u[j] = sm64_mix_hi(z);
+        z += kGamma;
+    }
 }
 
 }  // namespace ssm
