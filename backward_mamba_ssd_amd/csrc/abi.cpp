@@ -106,7 +106,7 @@ size_t bwd_ws_bytes(const ssm_dims *d, ssm_dtype t) {
     const size_t nc = nchunks_of(d);
     if (mfma_bwd_path(d, t)) {
         const size_t nb = d->chunk / 64;
-        return round_up(B * H * nc * P * N * sizeof(float)) +
+        return round_up(B * H * nc * P * N * sizeof(uint16_t)) +
                2 * round_up(B * H * nc * nb * sizeof(double));
     }
     const size_t L = d->chunk < d->seqlen ? d->chunk : (d->seqlen > 0 ? d->seqlen : 1);
@@ -311,7 +311,7 @@ ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void
         a.ddt = ddt; a.dA = dA; a.dD = dD; a.dh0 = dh0;
         a.ev_begin = static_cast<hipEvent_t>(g_prof_begin.exchange(nullptr));
         a.ev_end = static_cast<hipEvent_t>(g_prof_end.exchange(nullptr));
-        a.dstates = cv.take<float>(d->batch * d->nheads * nc * PN);
+        a.dstates = cv.take<bf16_t>(d->batch * d->nheads * nc * PN);
         a.pA = cv.take<double>(d->batch * d->nheads * nc * (d->chunk / 64));
         a.pD = cv.take<double>(d->batch * d->nheads * nc * (d->chunk / 64));
 #ifdef SSM_WITH_MFMA_BWD

@@ -51,12 +51,15 @@ namespace {
 // on distinct banks, and a wave's 16-byte row writes are conflict-free.
 constexpr int kSC = kN + 16;
 constexpr int kSY = kP + 16;
-// Offset (floats) of lane `lane`'s four accumulator values of state tile (n-tile nt,
-// p-tile pt) in one chunk's gradient of the workspace: 32 tiles of 16 x 16 floats in
-// n-tile-major order, each as 64 lanes x 4 floats (lane l holds p = 16 pt + l % 16,
-// n = 16 nt + 4 (l / 16) + 0..3).
-__device__ __forceinline__ int dstate_tile(int nt, int pt, int lane) {
-    return (nt * (kP / 16) + pt) * 256 + lane * 4;
+// Offset (bf16 elements) of lane `lane`'s eight values of the tile pair (n-tile nt,
+// p-tiles 2m and 2m + 1) in one chunk's gradient of the workspace: the four
+// accumulator values of tile (nt, 2m) followed by those of tile (nt, 2m + 1), lane l
+// holding p = 16 pt + l % 16, n = 16 nt + 4 (l / 16) + 0..3.  Each lane moves 16
+// bytes, and a wave a whole 1 KB, in both kernels.  The gradient is rounded to bf16
+// here: every use in the per-block kernel rounds the block-exit gradient it builds
+// from it to bf16 for the MFMA operands anyway.
+__device__ __forceinline__ int dstate_pair(int nt, int m, int lane) {
+    return ((nt * (kP / 32) + m) * 64 + lane) * 8;
 }
 
 struct DstSmem {
@@ -125,19 +128,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     };
     const int nblk = static_cast<int>((T + kLs - 1) / kLs);
     const int bpc = static_cast<int>(a.L / kLs);  // blocks per chunk
-    float *const dst0 = a.dstates + static_cast<int64_t>(bh) * a.nchunks * PN;
+    bf16_t *const dst0 = a.dstates + static_cast<int64_t>(bh) * a.nchunks * PN;
     // one block of the reverse walk; R is refilled with block s - 2 once staged
     auto step = [&](int s, Rows &R) {
         const int buf = s & 1;
         if (s == nblk - 1 || (s + 1) % bpc == 0) {
-            // gradient on the state leaving chunk c (everything after it), stored tile by
-            // tile in accumulator lane order: a wave writes whole 1 KB tiles and the
-            // per-block kernel reads them back with the same lane map
-            float *dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
+            // gradient on the state leaving chunk c (everything after it), stored by tile
+            // pairs in accumulator lane order (tiles q and q + 1 share an n-tile)
+            bf16_t *dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int nt = 2 * wave + q / 4, pt = q % 4;
-                *reinterpret_cast<float4 *>(dst + dstate_tile(nt, pt, lane)) = make_float4(G[q][0], G[q][1], G[q][2], G[q][3]);
+            for (int q = 0; q < 8; q += 2) {
+                const int nt = 2 * wave + q / 4, m = (q % 4) / 2;
+                const u16x4 lo = pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
+                const u16x4 hi = pack4(G[q + 1][0], G[q + 1][1], G[q + 1][2], G[q + 1][3]);
+                const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                *reinterpret_cast<u16x8 *>(dst + dstate_pair(nt, m, lane)) = v;
             }
         }
         if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(R.dtr * Ah);
@@ -346,19 +351,20 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     // p-tile 2wh + q%2
     // raw chunk-boundary state and chunk-exit gradient of the next head, loaded a full
     // head ahead of their use in S3
-    f32x4 Hs[4], dHs[4];
+    f32x4 Hs[4];
+    u16x8 dHr[2];  // chunk-exit gradient tile pairs (n-tile 2wq + j, p-tiles 2wh, 2wh + 1), bf16
     auto load_states = [&](int h) {
         const int64_t bh = static_cast<int64_t>(b) * a.H + h;
         const float *hc = a.chunk_states + (bh * a.nchunks + c) * PN;
-        const float *dc = a.dstates + (bh * a.nchunks + c) * PN;
+        const bf16_t *dc = a.dstates + (bh * a.nchunks + c) * PN;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int n = 16 * (2 * wq + (q >> 1)) + lq, p = 16 * (2 * wh + (q & 1)) + lr;
             const float4 u = *reinterpret_cast<const float4 *>(hc + p * kN + n);
-            const float4 v = *reinterpret_cast<const float4 *>(dc + dstate_tile(2 * wq + (q >> 1), 2 * wh + (q & 1), lane));
             Hs[q] = f32x4{u.x, u.y, u.z, u.w};
-            dHs[q] = f32x4{v.x, v.y, v.z, v.w};  // (from the tile-ordered workspace)
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dHr[j] = *reinterpret_cast<const u16x8 *>(dc + dstate_pair(2 * wq + j, wh, lane));
     };
 
     prefetch(h0);
@@ -584,7 +590,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     hv[v] = fmaf(es, Hs[q][v], aH[q][v]);
-                    gv[v] = fmaf(ee, dHs[q][v], adH[q][v]);
+                    gv[v] = fmaf(ee, bf16_to_f32(dHr[q >> 1][4 * (q & 1) + v]), adH[q][v]);
                     dotp = fmaf(hv[v], gv[v], dotp);
                 }
                 *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(hv[0], hv[1], hv[2], hv[3]);

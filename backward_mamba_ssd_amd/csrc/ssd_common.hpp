@@ -33,8 +33,8 @@ struct SsdBwdArgs {
     float *dB, *dC, *ddt, *dA, *dD, *dh0;
     hipEvent_t ev_begin, ev_end;  // optional: recorded around the per-block kernel
     // workspace
-    float *dstates;   // [Bsz, H, nchunks, 32 tiles x 256]: gradient on the state leaving chunk c
-                      // (16 x 16 tiles in accumulator lane order)
+    bf16_t *dstates;  // [Bsz, H, nchunks, 64 x 128]: gradient on the state leaving chunk c, in bf16,
+                      // in pairs of 16 x 16 tiles in accumulator lane order (dstate_pair)
     double *pA, *pD;  // [Bsz, H, nchunks, chunk/64] per-block partials of dA, dD
 };
 

@@ -47,11 +47,12 @@ def fwd_bytes_per_token(w):
 
 def bwd_block_bytes_per_token(w):
     """Algorithmic HBM bytes per token of the per-block backward kernel:
-    x, dy read and dx written (2 B each), the chunk-boundary state and the
-    chunk-exit state gradient read once per chunk (4 B per element), B and C
-    read (2 B), dB and dC written (4 B), dt read and ddt written (4 B)."""
+    x, dy read and dx written (2 B each), the chunk-boundary state (4 B per
+    element) and the chunk-exit state gradient (2 B per element) read once per
+    chunk, B and C read (2 B), dB and dC written (4 B), dt read and ddt written
+    (4 B)."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
-    return (3 * 2 * H * P + 2 * 4 * H * P * N / L + 2 * 2 * G * N + 2 * 4 * G * N + 2 * 4 * H)
+    return (3 * 2 * H * P + (4 + 2) * H * P * N / L + 2 * 2 * G * N + 2 * 4 * G * N + 2 * 4 * H)
 
 
 def fwd_flops_per_token(w):
@@ -72,9 +73,9 @@ def bwd_flops_per_token(w):
 def bwd_call_bytes_per_token(w):
     """Algorithmic HBM bytes per token of the whole backward call of this design: the
     reverse state pass (dy and C read, chunk-exit state gradients written once per
-    chunk) plus the per-block kernel (bwd_block_bytes_per_token)."""
+    chunk in bf16) plus the per-block kernel (bwd_block_bytes_per_token)."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
-    return 2 * H * P + 2 * G * N + 4 * H * P * N / L + bwd_block_bytes_per_token(w)
+    return 2 * H * P + 2 * G * N + 2 * H * P * N / L + bwd_block_bytes_per_token(w)
 
 
 def path_entry(flops, nbytes, ms, flop_peak_tflops=None):
