@@ -68,7 +68,7 @@ struct DstSmem {
     float lam[2][kLs];
 };
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
     __shared__ DstSmem sm;
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
@@ -95,9 +95,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     // staging map: dy rows yt0 + 32i from channel yp0; C rows ct0 + 16i from coordinate cn0
     const int yt0 = tid >> 3, yp0 = (tid & 7) * 8;
     const int ct0 = tid >> 4, cn0 = (tid & 15) * 8;
-    // A block's rows in registers, loaded two blocks ahead: the loop is unrolled by two
-    // so the two register sets alternate without copies (a copy of a loaded register
-    // would wait for the load).
+    // A block's rows in registers, loaded one block ahead (right after the previous
+    // block's rows were staged); four workgroups per CU cover each other's latency.
     struct Rows {
         u16x8 yr[2], cr[4];
         float dtr;
@@ -129,7 +128,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
     const int nblk = static_cast<int>((T + kLs - 1) / kLs);
     const int bpc = static_cast<int>(a.L / kLs);  // blocks per chunk
     bf16_t *const dst0 = a.dstates + static_cast<int64_t>(bh) * a.nchunks * PN;
-    // one block of the reverse walk; R is refilled with block s - 2 once staged
+    // one block of the reverse walk; R is refilled with block s - 1 once staged
     auto step = [&](int s, Rows &R) {
         const int buf = s & 1;
         if (s == nblk - 1 || (s + 1) % bpc == 0) {
@@ -165,7 +164,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<u16x8 *>(&sm.C[(ct0 + 16 * i) * kSC + cn0]) = R.cr[i];
         }
-        if (s >= 2) prefetch(R, s - 2);
+        if (s >= 1) prefetch(R, s - 1);
         __syncthreads();
         const float el = __expf(lam_end);
 #pragma unroll
@@ -181,13 +180,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
             G[q] = acc;
         }
     };
-    Rows RA, RB;
-    prefetch(RA, nblk - 1);
-    if (nblk >= 2) prefetch(RB, nblk - 2);
-    for (int s = nblk - 1; s >= 0; s -= 2) {
-        step(s, RA);
-        if (s >= 1) step(s - 1, RB);
-    }
+    Rows R;
+    prefetch(R, nblk - 1);
+    for (int s = nblk - 1; s >= 0; --s) step(s, R);
     if (a.dh0 != nullptr) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
