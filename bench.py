@@ -586,7 +586,7 @@ def main():
                          "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(sharding is design-only); rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
