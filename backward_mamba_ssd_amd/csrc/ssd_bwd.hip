@@ -594,11 +594,13 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             dotp = wave_total(dotp);
             if (lane == 0) sm.dot[wave] = dotp;
         }
-        load_states(hn);
         // the other parity slot is free: this head reads only lam[par], dt[par], and
         // the barrier below publishes the next head's values before its first use
         if (wave == 0) scan(hn, par ^ 1);
         __syncthreads();
+        // the next head's chunk-boundary state and exit gradient (this head's were consumed
+        // in S3); issued here rather than inside S3, where they queued behind the row prefetch
+        load_states(hn);
         // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tiles 2wh, 2wh+1) ----
         {
             f32x4 acc[2], acc4[2];
