@@ -487,41 +487,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         }
         __syncthreads();
         prefetch(hn);  // registers are free once staged
-        // ---- S2: state products over the other blocks; Phase I of block k ----
+        // ---- S2: Phase I of block k, then the state products over the other blocks
+        //      (in this order 1.628 -> 1.616 ms; the two are independent) ----
         if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
-        // Each A fragment (16 state rows n of one block's B or C) is read once and used
-        // for all four p-tiles.
-        // The sums start from zero; the decayed chunk-boundary terms are added in S3.
-        f32x4 aH[4], adH[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) aH[q] = adH[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // 2 x 2 register blocking: per 32-token step the wave reads two n fragments and
-        // two p fragments for four products.
-        {
-            auto chain = [&](const bf16_t *bc, const bf16_t *xs, f32x4 *acc) {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8 fa[2], fb[2];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        fa[t] = frag_tr(bc, kS128, 16 * (2 * wq + t), 32 * kk, lane);
-                        fb[t] = frag_tr(xs, kS64, 16 * (2 * wh + t), 32 * kk, lane);
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = mfma(fa[q >> 1], fb[q & 1], acc[q]);
-                }
-            };
-#pragma unroll
-            for (int kb = 0; kb < kMaxBlk - 1; ++kb) {  // H_k = e H_c + sum over earlier blocks
-                if (kb >= k) break;
-                chain(sm.chainBC + kb * kT128, sm.R + kb * kT64, aH);
-            }
-#pragma unroll
-            for (int sl = 0; sl < kMaxBlk - 1; ++sl) {  // dH_{k+1} = e dH_c + sum over later blocks (slot sl = block sl+1)
-                if (sl < k || sl + 1 >= nbc) continue;
-                chain(sm.chainBC + sl * kT128, sm.R + sl * kT64, adH);
-            }
-        }
         // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile wq, j-tiles 2wh, 2wh+1)
         {
             float lam_i[4], rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
@@ -570,6 +538,39 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             }
             diag = wave_total(diag);
             if (lane == 0) sm.dd_sum[par][wave] = diag;
+        }
+        // Each A fragment (16 state rows n of one block's B or C) is read once and used
+        // for all four p-tiles.
+        // The sums start from zero; the decayed chunk-boundary terms are added in S3.
+        f32x4 aH[4], adH[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) aH[q] = adH[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // 2 x 2 register blocking: per 32-token step the wave reads two n fragments and
+        // two p fragments for four products.
+        {
+            auto chain = [&](const bf16_t *bc, const bf16_t *xs, f32x4 *acc) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 fa[2], fb[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        fa[t] = frag_tr(bc, kS128, 16 * (2 * wq + t), 32 * kk, lane);
+                        fb[t] = frag_tr(xs, kS64, 16 * (2 * wh + t), 32 * kk, lane);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q] = mfma(fa[q >> 1], fb[q & 1], acc[q]);
+                }
+            };
+#pragma unroll
+            for (int kb = 0; kb < kMaxBlk - 1; ++kb) {  // H_k = e H_c + sum over earlier blocks
+                if (kb >= k) break;
+                chain(sm.chainBC + kb * kT128, sm.R + kb * kT64, aH);
+            }
+#pragma unroll
+            for (int sl = 0; sl < kMaxBlk - 1; ++sl) {  // dH_{k+1} = e dH_c + sum over later blocks (slot sl = block sl+1)
+                if (sl < k || sl + 1 >= nbc) continue;
+                chain(sm.chainBC + sl * kT128, sm.R + sl * kT64, adH);
+            }
         }
         __syncthreads();
         // ---- S3: block-entry state and exit gradient in bf16, [p][n] ----
