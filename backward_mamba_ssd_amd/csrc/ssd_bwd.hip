@@ -36,6 +36,8 @@
 //     the heads in registers (fixed order, no atomics), and sum_h K is applied
 //     to B and C once after the loop.  ddt is complete per block.
 //  3. ssd_bwd_params: dA, dD as fixed-order fp64 sums of per-block partials.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "ssd_common.hpp"
@@ -68,7 +70,14 @@ struct DstSmem {
     float lam[2][kLs];
 };
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
+// NW waves per workgroup: 4 when the (batch, head) workgroups fill every CU four deep,
+// 8 for smaller grids (batch 1 at long context), so each CU still runs 16 waves.  Wave w
+// owns n-tiles (8 / NW) w .. (8 / NW) w + 8 / NW - 1 of dH^T and all four p-tiles; every
+// tile sees the same MFMA sequence either way, so the results do not depend on NW.
+template <int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
+    constexpr int kTiles = 32 / NW;  // dH^T tiles per wave
+    constexpr int kNT = 8 / NW;      // n-tiles per wave
     __shared__ DstSmem sm;
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
@@ -80,11 +89,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
     const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
     constexpr int PN = kP * kN;
 
-    // dH^T accumulators: tile q: nt = 2w + q/4, pt = q%4; n = 16nt + lq + v, p = 16pt + lr
-    f32x4 G[8];
+    // dH^T accumulators: tile q: nt = kNT w + q/4, pt = q%4; n = 16nt + lq + v, p = 16pt + lr
+    f32x4 G[kTiles];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+    for (int q = 0; q < kTiles; ++q) {
+        const int n = 16 * (kNT * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
         if (a.dh_final != nullptr) {
             const float4 v = *reinterpret_cast<const float4 *>(a.dh_final + static_cast<int64_t>(bh) * PN + p * kN + n);
             G[q] = f32x4{v.x, v.y, v.z, v.w};
@@ -92,13 +101,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
             G[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // staging map: dy rows yt0 + 32i from channel yp0; C rows ct0 + 16i from coordinate cn0
+    // staging map: dy rows yt0 + 8 NW i from channel yp0; C rows ct0 + 4 NW i from coordinate cn0
     const int yt0 = tid >> 3, yp0 = (tid & 7) * 8;
     const int ct0 = tid >> 4, cn0 = (tid & 15) * 8;
     // A block's rows in registers, loaded one block ahead (right after the previous
     // block's rows were staged); four workgroups per CU cover each other's latency.
+    constexpr int kYR = 8 / NW, kCR = 16 / NW;  // 16-byte row pieces per thread
     struct Rows {
-        u16x8 yr[2], cr[4];
+        u16x8 yr[kYR], cr[kCR];
         float dtr;
     };
     // per-block buffer descriptors: rows at or past the end of the sequence read zero.
@@ -116,9 +126,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
         const rsrc_t ry = make_rsrc(dy0 + s * sy, nv * toky);
         const rsrc_t rc = make_rsrc(C0 + s * sc, nv * tokc);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) R.yr[i] = buf_ld_16b(ry, (yt0 + 32 * i) * toky + yp0 * 2);
+        for (int i = 0; i < kYR; ++i) R.yr[i] = buf_ld_16b(ry, (yt0 + 8 * NW * i) * toky + yp0 * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R.cr[i] = buf_ld_16b(rc, (ct0 + 16 * i) * tokc + cn0 * 2);
+        for (int i = 0; i < kCR; ++i) R.cr[i] = buf_ld_16b(rc, (ct0 + 4 * NW * i) * tokc + cn0 * 2);
         R.dtr = 0.f;
         if (tid < kLs) {
             const rsrc_t rd = make_rsrc(dt0 + s * sd, nv * a.H * 4u);
@@ -136,8 +146,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
             // pairs in accumulator lane order (tiles q and q + 1 share an n-tile)
             bf16_t *dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
 #pragma unroll
-            for (int q = 0; q < 8; q += 2) {
-                const int nt = 2 * wave + q / 4, m = (q % 4) / 2;
+            for (int q = 0; q < kTiles; q += 2) {
+                const int nt = kNT * wave + q / 4, m = (q % 4) / 2;
                 const u16x4 lo = pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
                 const u16x4 hi = pack4(G[q + 1][0], G[q + 1][1], G[q + 1][2], G[q + 1][3]);
                 const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -151,25 +161,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
         {
             typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float e = __expf(lam[yt0 + 32 * i]);
+            for (int i = 0; i < kYR; ++i) {
+                const float e = __expf(lam[yt0 + 8 * NW * i]);
                 const u16x8 v = R.yr[i];
                 const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * e, bf16_to_f32(v[1]) * e),
                                  pack2_bf16(bf16_to_f32(v[2]) * e, bf16_to_f32(v[3]) * e),
                                  pack2_bf16(bf16_to_f32(v[4]) * e, bf16_to_f32(v[5]) * e),
                                  pack2_bf16(bf16_to_f32(v[6]) * e, bf16_to_f32(v[7]) * e)};
-                *reinterpret_cast<u32x4 *>(&sm.EdY[(yt0 + 32 * i) * kSY + yp0]) = w;
+                *reinterpret_cast<u32x4 *>(&sm.EdY[(yt0 + 8 * NW * i) * kSY + yp0]) = w;
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<u16x8 *>(&sm.C[(ct0 + 16 * i) * kSC + cn0]) = R.cr[i];
+            for (int i = 0; i < kCR; ++i)
+                *reinterpret_cast<u16x8 *>(&sm.C[(ct0 + 4 * NW * i) * kSC + cn0]) = R.cr[i];
         }
         if (s >= 1) prefetch(R, s - 1);
         __syncthreads();
         const float el = __expf(lam_end);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int nt = 2 * wave + q / 4, pt = q % 4;
+        for (int q = 0; q < kTiles; ++q) {
+            const int nt = kNT * wave + q / 4, pt = q % 4;
             f32x4 acc = G[q];
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] *= el;
@@ -185,8 +195,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
     for (int s = nblk - 1; s >= 0; --s) step(s, R);
     if (a.dh0 != nullptr) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int n = 16 * (2 * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+        for (int q = 0; q < kTiles; ++q) {
+            const int n = 16 * (kNT * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
             *reinterpret_cast<float4 *>(a.dh0 + static_cast<int64_t>(bh) * PN + p * kN + n) =
                 make_float4(G[q][0], G[q][1], G[q][2], G[q][3]);
         }
@@ -756,6 +766,21 @@ __global__ void __launch_bounds__(64) ssd_bwd_params_kernel(SsdBwdArgs a) {
 
 }  // namespace
 
+// Compute units of the current device, queried once per device.
+static hipError_t cu_count(int *out) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int v = (dev >= 0 && dev < 64) ? cache[dev].load() : 0;
+    if (v == 0) {
+        if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) cache[dev].store(v);
+    }
+    *out = v;
+    return hipSuccess;
+}
+
 hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s) {
     // partials of blocks past the end of the sequence stay untouched: clear them
     const int64_t nparts = a.Bsz * a.H * a.nchunks * (a.L / kLs);
@@ -763,7 +788,14 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     e = launch_fill(reinterpret_cast<float *>(a.pD), 2 * nparts, 0.f, s);
     if (e != hipSuccess) return e;
-    ssd_bwd_dstate_kernel<<<static_cast<unsigned>(a.Bsz * a.H), 256, 0, s>>>(a);
+    // four 4-wave workgroups per CU when the grid fills the chip that deep, else 8 waves
+    int cus = 0;
+    if ((e = cu_count(&cus)) != hipSuccess) return e;
+    const int64_t nbh = a.Bsz * a.H;
+    if (nbh >= 4 * static_cast<int64_t>(cus))
+        ssd_bwd_dstate_kernel<4><<<static_cast<unsigned>(nbh), 256, 0, s>>>(a);
+    else
+        ssd_bwd_dstate_kernel<8><<<static_cast<unsigned>(nbh), 512, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nwg = a.Bsz * a.G * a.nchunks * (a.L / kLs);
