@@ -4,7 +4,9 @@ Tolerance 2e-2 scaled error on dx, dB, dC, ddt, dA, dD, dh0 (bf16 MFMA
 operands, fp32 accumulation, fp64 final dA/dD sums).  Small problems span
 several 64-token blocks, partial chunks and ragged tails; the full prefill
 workload (batch 4, 256 heads, T = 4096) is checked on one whole group over all
-batches (so dA/dD of its heads are complete); the long-context workload
+batches (so dA/dD of its heads are complete); each batch of a 256-head problem run
+alone matches the batched run bit for bit (the two runs take the 4-wave and the
+8-wave form of the reverse pass); the long-context workload
 (T = 131,072, 512 saved chunk states per head) is checked per head over the
 full length and on all heads of a group over the final 1024 tokens.
 """
@@ -73,6 +75,31 @@ def test_backward_deterministic(ssm):
     torch.cuda.synchronize()
     for k in GRADS:
         assert torch.equal(g1[k], g2[k]), k
+
+
+def test_batch_slices_are_independent(ssm):
+    # Every (batch, head) is computed by its own workgroups, so each batch run alone gives
+    # the same bits as the batched run.  With 256 heads the batch-4 reverse pass fills an
+    # MI355X four deep and takes its 4-wave form, while a batch of 1 takes the 8-wave
+    # form: this also checks that the two forms agree bit for bit.  (dA and dD sum over
+    # the batch, so only their batch-summed values are compared, at tolerance.)
+    b, t, h, p, n, g, L = 4, 320, 256, 64, 128, 8, 128
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 41, dev, h0="randn", dh_final=True)
+    y, hf, cs, gr = _run(ssm, pr, L)
+    dA = torch.zeros_like(gr["dA"], dtype=torch.float64)
+    dD = torch.zeros_like(dA)
+    for i in range(b):
+        one = {k: (v[i:i + 1].contiguous() if (v is not None and v.dim() > 1) else v)
+               for k, v in pr.items()}
+        y1, hf1, cs1, g1 = _run(ssm, one, L)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y[i:i + 1]) and torch.equal(cs1, cs[i:i + 1]), i
+        for k in ("dx", "dB", "dC", "ddt", "dh0"):
+            assert torch.equal(g1[k], gr[k][i:i + 1]), (k, i)
+        dA += g1["dA"].double()
+        dD += g1["dD"].double()
+    assert_close("dA over batch", gr["dA"], dA, 1e-5)
+    assert_close("dD over batch", gr["dD"], dD, 1e-5)
 
 
 def test_full_prefill_workload_one_group(ssm):
