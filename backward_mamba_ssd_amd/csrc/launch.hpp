@@ -5,9 +5,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "ssd_common.hpp"
 
 namespace ssm {
+
+// Compute units of the current device, queried once per device (the chunked launchers
+// size their workgroups by how deep the grid fills the chip).
+inline hipError_t device_cu_count(int *out) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int v = (dev >= 0 && dev < 64) ? cache[dev].load() : 0;
+    if (v == 0) {
+        if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) cache[dev].store(v);
+    }
+    *out = v;
+    return hipSuccess;
+}
 
 struct DecodeArgs {
     int64_t Bsz;

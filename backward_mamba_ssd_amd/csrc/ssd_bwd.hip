@@ -766,21 +766,6 @@ __global__ void __launch_bounds__(64) ssd_bwd_params_kernel(SsdBwdArgs a) {
 
 }  // namespace
 
-// Compute units of the current device, queried once per device.
-static hipError_t cu_count(int *out) {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    int v = (dev >= 0 && dev < 64) ? cache[dev].load() : 0;
-    if (v == 0) {
-        if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) cache[dev].store(v);
-    }
-    *out = v;
-    return hipSuccess;
-}
-
 hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s) {
     // partials of blocks past the end of the sequence stay untouched: clear them
     const int64_t nparts = a.Bsz * a.H * a.nchunks * (a.L / kLs);
@@ -790,7 +775,7 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     // four 4-wave workgroups per CU when the grid fills the chip that deep, else 8 waves
     int cus = 0;
-    if ((e = cu_count(&cus)) != hipSuccess) return e;
+    if ((e = device_cu_count(&cus)) != hipSuccess) return e;
     const int64_t nbh = a.Bsz * a.H;
     if (nbh >= 4 * static_cast<int64_t>(cus))
         ssd_bwd_dstate_kernel<4><<<static_cast<unsigned>(nbh), 256, 0, s>>>(a);

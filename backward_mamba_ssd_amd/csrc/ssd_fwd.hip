@@ -59,6 +59,11 @@ struct __align__(16) FwdSmem {
 };
 static_assert(sizeof(FwdSmem) <= 81920, "two workgroups per CU");
 
+// DEPTH: blocks of rows held in registers ahead of the one being computed.  1 when two
+// workgroups share a CU (at most 128 registers); 2 when the grid has fewer (batch, head)
+// pairs than two per CU, so each workgroup has a CU to itself and nothing else covers its
+// load latency (batch 1 at long context).  The arithmetic is the same either way.
+template <int DEPTH>
 __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     FwdSmem &sm = *reinterpret_cast<FwdSmem *>(smem_raw);
@@ -97,8 +102,10 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     // channel xc.  A wave covers whole rows, 16 contiguous bytes per lane.
     const int rt = tid >> 4, rc = (tid & 15) * 8;
     const int xt = tid >> 3, xc = (tid & 7) * 8;
-    u16x8 pre[5];   // B rows rt, rt + 32; C rows rt, rt + 32; x row xt
-    float dtr = 0.f;
+    struct Rows {
+        u16x8 v[5];  // B rows rt, rt + 32; C rows rt, rt + 32; x row xt
+        float dt;    // dt of token `tid` (wave 0)
+    };
     const uint32_t tokx = static_cast<uint32_t>(a.H) * kP * 2;
     const uint32_t tokbc = static_cast<uint32_t>(a.G) * kN * 2;
     // Per-block pointers advance by a fixed stride (no 64-bit multiply or divide in the
@@ -112,19 +119,20 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     const float *pdt = a.dt + b * T * a.H + h;
     bf16_t *py = y + (b * T * a.H + h) * kP;        // block being computed
     auto nvalid_of = [&](int64_t rem) { return static_cast<uint32_t>(rem < kLs ? rem : kLs); };
-    auto prefetch = [&](int64_t rem) {  // rem: tokens from the prefetched block to the end
+    auto prefetch = [&](Rows &R, int64_t rem) {  // rem: tokens from the prefetched block to the end
         const uint32_t nv = nvalid_of(rem);
         const rsrc_t rb = make_rsrc(pB, nv * tokbc), rcc = make_rsrc(pC, nv * tokbc);
         const rsrc_t rx = make_rsrc(px, nv * tokx);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            pre[i] = buf_ld_16b(rb, (rt + 32 * i) * tokbc + rc * 2);
-            pre[2 + i] = buf_ld_16b(rcc, (rt + 32 * i) * tokbc + rc * 2);
+            R.v[i] = buf_ld_16b(rb, (rt + 32 * i) * tokbc + rc * 2);
+            R.v[2 + i] = buf_ld_16b(rcc, (rt + 32 * i) * tokbc + rc * 2);
         }
-        pre[4] = buf_ld_16b(rx, xt * tokx + xc * 2);
+        R.v[4] = buf_ld_16b(rx, xt * tokx + xc * 2);
+        R.dt = 0.f;
         if (tid < kLs) {
             const rsrc_t rd = make_rsrc(pdt, nv * a.H * 4u);
-            dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
+            R.dt = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
         }
         px += sx;
         pB += sbc;
@@ -150,12 +158,12 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
     const int bpc = static_cast<int>(a.L / kLs);  // blocks per chunk
     int kc = 0;                                   // block index within its chunk
     float *cs = (a.chunk_states != nullptr) ? a.chunk_states + static_cast<int64_t>(bh) * a.nchunks * (kP * kN) : nullptr;
-    prefetch(T);
-    for (int64_t s = 0; s < nblk; ++s) {
+    // one block; R holds its rows and is refilled with block s + DEPTH
+    auto step = [&](int64_t s, Rows &R) {
         const int64_t t0 = s * kLs;
         const int buf = static_cast<int>(s & 1);
         // (1) cumulative log-retention of the block (one wave, one token per lane)
-        if (wave == 0) sm.ld[buf][lane] = make_float2(wave_prefix_sum(dtr * Ah), dtr);
+        if (wave == 0) sm.ld[buf][lane] = make_float2(wave_prefix_sum(R.dt * Ah), R.dt);
         __syncthreads();
         const float2 *ld = sm.ld[buf];
         const float lam_end = ld[kLs - 1].x;
@@ -163,11 +171,11 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int r = rt + 32 * i;
-            *reinterpret_cast<u16x8 *>(&sm.B[r * kS128 + rc]) = pre[i];
-            *reinterpret_cast<u16x8 *>(&sm.C[r * kS128 + rc]) = pre[2 + i];
+            *reinterpret_cast<u16x8 *>(&sm.B[r * kS128 + rc]) = R.v[i];
+            *reinterpret_cast<u16x8 *>(&sm.C[r * kS128 + rc]) = R.v[2 + i];
             const float2 lt = ld[r];
             const float cf = __expf(lam_end - lt.x) * lt.y;
-            const u16x8 v = pre[i];
+            const u16x8 v = R.v[i];
             typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
             const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * cf, bf16_to_f32(v[1]) * cf),
                              pack2_bf16(bf16_to_f32(v[2]) * cf, bf16_to_f32(v[3]) * cf),
@@ -175,7 +183,7 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
                              pack2_bf16(bf16_to_f32(v[6]) * cf, bf16_to_f32(v[7]) * cf)};
             *reinterpret_cast<u32x4 *>(&sm.Bs[r * kS128 + rc]) = w;
         }
-        *reinterpret_cast<u16x8 *>(&sm.X[xt * kSX + xc]) = pre[4];
+        *reinterpret_cast<u16x8 *>(&sm.X[xt * kSX + xc]) = R.v[4];
         __syncthreads();
         // This phase's stores go out after the staging barrier rather than before the
         // staging writes (0.559 -> 0.550 ms): the previous block's outputs (complete since
@@ -236,7 +244,7 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
         // The next block's rows are requested here, after the Gram and H phases: the
         // kernel took 0.61 ms with the request at the end of staging, 0.57 after the Gram
         // barrier, 0.56 here and 0.62 or more later in this phase.
-        if (s + 1 < nblk) prefetch(T - t0 - kLs);
+        if (s + DEPTH < nblk) prefetch(R, T - t0 - DEPTH * kLs);
         // (5) outputs Y^T: p-tile pw, token tiles 2 ih + {0, 1}; the wave's H and X^T
         //     fragments are read once for both, and X^T again serves the state update
         {
@@ -281,6 +289,17 @@ __global__ void __launch_bounds__(512) ssd_fwd_kernel(SsdFwdArgs a) {
                 }
             }
         }
+    };
+    Rows RA, RB;
+    prefetch(RA, T);
+    if (DEPTH == 1) {
+        for (int64_t s = 0; s < nblk; ++s) step(s, RA);
+    } else {
+        if (nblk > 1) prefetch(RB, T - kLs);
+        for (int64_t s = 0; s < nblk; s += 2) {
+            step(s, RA);
+            if (s + 1 < nblk) step(s + 1, RB);
+        }
     }
     __syncthreads();
     if (nblk > 0) store_y((nblk - 1) * kLs);
@@ -306,13 +325,22 @@ hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
     if (bit == 0 || (configured.load() & bit) == 0) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ssd_fwd_kernel),
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ssd_fwd_kernel<1>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ssd_fwd_kernel<2>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
         if (e != hipSuccess) return e;
         configured.fetch_or(bit);
     }
-    const unsigned grid = static_cast<unsigned>(a.Bsz * a.H);
-    ssd_fwd_kernel<<<grid, 512, smem, s>>>(a);
+    int cus = 0;
+    if ((e = device_cu_count(&cus)) != hipSuccess) return e;
+    const int64_t nbh = a.Bsz * a.H;
+    const unsigned grid = static_cast<unsigned>(nbh);
+    if (nbh >= 2 * static_cast<int64_t>(cus))
+        ssd_fwd_kernel<1><<<grid, 512, smem, s>>>(a);
+    else
+        ssd_fwd_kernel<2><<<grid, 512, smem, s>>>(a);
     return hipGetLastError();
 }
 
