@@ -32,19 +32,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "abi.cpp")]
 
 
-def _defines():
-    have = {os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "*.hip"))}
-    defs = []
-    if "ssd_fwd.hip" in have:
-        defs.append("-DSSM_WITH_MFMA_FWD")
-    if "ssd_bwd.hip" in have:
-        defs.append("-DSSM_WITH_MFMA_BWD")
-    return defs
-
-
-def _compile(src, defs, verbose):
+def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = ["hipcc", *FLAGS, *defs, "-c", src, "-o", obj]
+    cmd = ["hipcc", *FLAGS, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     p = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,11 +49,10 @@ def _compile(src, defs, verbose):
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    defs = _defines()
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, defs, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     p = subprocess.run(cmd, capture_output=True, text=True)

@@ -7,7 +7,6 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
-#include <atomic>
 #include <initializer_list>
 
 #include "../../include/ssm.h"
@@ -67,24 +66,10 @@ bool mfma_shape(const ssm_dims *d, ssm_dtype t) {
     return t == SSM_BF16 && d->headdim == 64 && d->dstate == 128 && d->chunk % 64 == 0;
 }
 
-bool mfma_fwd_path(const ssm_dims *d, ssm_dtype t) {
-#ifdef SSM_WITH_MFMA_FWD
-    return mfma_shape(d, t);
-#else
-    (void)d;
-    (void)t;
-    return false;
-#endif
-}
+bool mfma_fwd_path(const ssm_dims *d, ssm_dtype t) { return mfma_shape(d, t); }
 
 bool mfma_bwd_path(const ssm_dims *d, ssm_dtype t) {
-#ifdef SSM_WITH_MFMA_BWD
     return mfma_shape(d, t) && d->chunk <= 256 && d->nheads / d->ngroups <= 64;
-#else
-    (void)d;
-    (void)t;
-    return false;
-#endif
 }
 
 bool mfma_path(const ssm_dims *d, ssm_dtype t) { return mfma_fwd_path(d, t) && mfma_bwd_path(d, t); }
@@ -162,16 +147,9 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 hipError_t fill(float *p, int64_t n, hipStream_t s) { return launch_fill(p, n, 0.f, s); }
 
-std::atomic<void *> g_prof_begin{nullptr}, g_prof_end{nullptr};
-
 }  // namespace
 
 extern "C" {
-
-void ssm_profile_next_bwd_block(void *begin, void *end) {
-    g_prof_end.store(end);
-    g_prof_begin.store(begin);
-}
 
 const char *ssm_status_string(ssm_status s) {
     switch (s) {
@@ -250,11 +228,7 @@ ssm_status ssm_fwd_chunked(const ssm_dims *d, ssm_dtype dtype, const void *x, co
         a.G = static_cast<int>(d->ngroups); a.L = d->chunk; a.nchunks = nchunks_of(d);
         a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.D = D; a.h0 = h0; a.y = y;
         a.h_final = h_final; a.chunk_states = chunk_states;
-#ifdef SSM_WITH_MFMA_FWD
         e = launch_ssd_fwd(a, s);
-#else
-        e = hipErrorNotSupported;
-#endif
     } else {
         ScanArgs a{};
         a.Bsz = d->batch; a.T = d->seqlen; a.H = static_cast<int>(d->nheads);
@@ -268,11 +242,17 @@ ssm_status ssm_fwd_chunked(const ssm_dims *d, ssm_dtype dtype, const void *x, co
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
-ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
-                   const void *C, const float *dt, const float *A, const float *D,
-                   const float *chunk_states, const void *dy, const float *dh_final, void *dx,
-                   float *dB, float *dC, float *ddt, float *dA, float *dD, float *dh0,
-                   void *workspace, size_t ws_bytes, ssm_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// ssm_bwd and ssm_bwd_timed: `ev` is NULL or two caller events recorded around the
+// per-block kernel of the chunked path.
+ssm_status bwd_impl(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                    const void *C, const float *dt, const float *A, const float *D,
+                    const float *chunk_states, const void *dy, const float *dh_final, void *dx,
+                    float *dB, float *dC, float *ddt, float *dA, float *dD, float *dh0,
+                    void *workspace, size_t ws_bytes, void *const *ev, hipStream_t s) {
     ssm_status st = check_dims(d, true);
     if (st != SSM_OK) return st;
     if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
@@ -287,7 +267,15 @@ ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void
         return SSM_ERR_ALIGN;
     const size_t need = tokens ? bwd_ws_bytes(d, dtype) : 0;
     if (need > 0 && (workspace == nullptr || ws_bytes < need)) return SSM_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev_begin = nullptr, ev_end = nullptr;
+    if (ev != nullptr) {
+        ev_begin = static_cast<hipEvent_t>(ev[0]);
+        ev_end = static_cast<hipEvent_t>(ev[1]);
+        if (ev_begin == nullptr || ev_end == nullptr) return SSM_ERR_NULL;
+        // a first record of both events: an unusable event fails here, before any work
+        if (hipEventRecord(ev_begin, s) != hipSuccess || hipEventRecord(ev_end, s) != hipSuccess)
+            return SSM_ERR_HIP;
+    }
     const int64_t PN = d->headdim * d->dstate;
     if (!tokens) {  // no tokens: zero parameter gradients, dh0 = dh_final
         if (fill(dA, d->nheads, s) != hipSuccess || fill(dD, d->nheads, s) != hipSuccess)
@@ -309,16 +297,10 @@ ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void
         a.x = x; a.B = B; a.C = C; a.dy = dy; a.dt = dt; a.A = A; a.D = D;
         a.chunk_states = chunk_states; a.dh_final = dh_final; a.dx = dx; a.dB = dB; a.dC = dC;
         a.ddt = ddt; a.dA = dA; a.dD = dD; a.dh0 = dh0;
-        a.ev_begin = static_cast<hipEvent_t>(g_prof_begin.exchange(nullptr));
-        a.ev_end = static_cast<hipEvent_t>(g_prof_end.exchange(nullptr));
         a.dstates = cv.take<bf16_t>(d->batch * d->nheads * nc * PN);
         a.pA = cv.take<double>(d->batch * d->nheads * nc * (d->chunk / 64));
         a.pD = cv.take<double>(d->batch * d->nheads * nc * (d->chunk / 64));
-#ifdef SSM_WITH_MFMA_BWD
-        e = launch_ssd_bwd(a, s);
-#else
-        e = hipErrorNotSupported;
-#endif
+        e = launch_ssd_bwd(a, ev_begin, ev_end, s);
     } else {
         ScanBwdArgs a{};
         a.Bsz = d->batch; a.T = d->seqlen; a.H = static_cast<int>(d->nheads);
@@ -338,6 +320,30 @@ ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void
         e = launch_scan_bwd(a, dtype == SSM_BF16, s);
     }
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                   const void *C, const float *dt, const float *A, const float *D,
+                   const float *chunk_states, const void *dy, const float *dh_final, void *dx,
+                   float *dB, float *dC, float *ddt, float *dA, float *dD, float *dh0,
+                   void *workspace, size_t ws_bytes, ssm_stream stream) {
+    return bwd_impl(d, dtype, x, B, C, dt, A, D, chunk_states, dy, dh_final, dx, dB, dC, ddt, dA,
+                    dD, dh0, workspace, ws_bytes, nullptr, static_cast<hipStream_t>(stream));
+}
+
+ssm_status ssm_bwd_timed(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                         const void *C, const float *dt, const float *A, const float *D,
+                         const float *chunk_states, const void *dy, const float *dh_final,
+                         void *dx, float *dB, float *dC, float *ddt, float *dA, float *dD,
+                         float *dh0, void *workspace, size_t ws_bytes, void *const *block_events,
+                         ssm_stream stream) {
+    if (block_events == nullptr) return SSM_ERR_NULL;
+    return bwd_impl(d, dtype, x, B, C, dt, A, D, chunk_states, dy, dh_final, dx, dB, dC, ddt, dA,
+                    dD, dh0, workspace, ws_bytes, block_events, static_cast<hipStream_t>(stream));
 }
 
 ssm_status ssm_decode_step(const ssm_dims *d, ssm_dtype dtype, float *state, const void *x,

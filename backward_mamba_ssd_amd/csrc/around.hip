@@ -58,7 +58,6 @@ template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t *p, float4 v) {
 __device__ __forceinline__ float get(const float4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 constexpr int kConvFwdTile = 64;   // tokens per forward thread (window halo K-1)
-constexpr int kConvBwdTile = 256;  // tokens per backward thread (fp64 partials per tile)
 constexpr int kConvUnroll = 8;     // forward: tokens whose loads are in flight together
 
 // ---------------------------------------------------------------------------
@@ -284,7 +283,6 @@ __global__ void __launch_bounds__(256) conv_param_sum_kernel(ConvArgs a) {
 // gated group RMSNorm: a 256-thread workgroup per (row, group) (forward) or per
 // (row tile, group) (backward); thread j holds channels 8*(j + 256*q), q < NQ
 // ---------------------------------------------------------------------------
-constexpr int kNormRows = 32;  // rows per backward workgroup (dw partials per tile)
 
 template <typename T> __device__ __forceinline__ void ld8(const T *p, float *v);
 template <> __device__ __forceinline__ void ld8<float>(const float *p, float *v) {
@@ -546,8 +544,6 @@ hipError_t norm_dispatch(const NormArgs &a, bool bwd, hipStream_t s) {
 
 }  // namespace
 
-int64_t conv_bwd_tiles(int64_t T) { return (T + kConvBwdTile - 1) / kConvBwdTile; }
-int64_t norm_row_tiles(int64_t rows) { return (rows + kNormRows - 1) / kNormRows; }
 
 hipError_t launch_conv(const ConvArgs &a, bool bf16, bool bwd, hipStream_t s) {
     if (a.Bsz == 0 || a.C == 0) return hipSuccess;

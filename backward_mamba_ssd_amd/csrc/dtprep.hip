@@ -29,7 +29,7 @@
 namespace ssm {
 namespace {
 
-constexpr int kRowsPerTile = 16;   // rows of one workgroup (loads in flight together)
+constexpr int kRowsPerTile = kDtPrepRowsPerTile;  // rows of one workgroup (loads in flight together)
 constexpr int kHeadsPerTile = 256; // heads of one workgroup (one per thread)
 
 // softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|); no overflow for any v.
@@ -109,7 +109,6 @@ __global__ void __launch_bounds__(64) dt_prep_bwd_heads_kernel(DtPrepArgs a, int
 
 }  // namespace
 
-int64_t dt_prep_row_tiles(int64_t rows) { return (rows + kRowsPerTile - 1) / kRowsPerTile; }
 
 hipError_t launch_dt_prep(const DtPrepArgs &a, hipStream_t s) {
     int64_t nt = dt_prep_row_tiles(a.rows);

@@ -127,6 +127,15 @@ struct NormArgs {
     double *part;        // [row tiles][C] fp64 partials
 };
 
+// Tile sizes that fix the shapes of the fp64 partial-sum workspaces (host and kernels agree
+// on them through these definitions).
+constexpr int kDtPrepRowsPerTile = 16;  // time-step preparation: rows per workgroup
+constexpr int kConvBwdTile = 256;       // conv backward: tokens per partial-sum tile
+constexpr int kNormRows = 32;           // norm backward: rows per partial-sum tile
+inline int64_t dt_prep_row_tiles(int64_t rows) { return (rows + kDtPrepRowsPerTile - 1) / kDtPrepRowsPerTile; }
+inline int64_t conv_bwd_tiles(int64_t T) { return (T + kConvBwdTile - 1) / kConvBwdTile; }
+inline int64_t norm_row_tiles(int64_t rows) { return (rows + kNormRows - 1) / kNormRows; }
+
 hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);  // state or state16
@@ -137,10 +146,8 @@ hipError_t launch_rollback(const RollbackArgs &a, hipStream_t s);
 hipError_t launch_scan_bwd(const ScanBwdArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_sr16(const Sr16Args &a, hipStream_t s);
 hipError_t launch_ssd_fwd(const SsdFwdArgs &a, hipStream_t s);
-hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s);
-int64_t dt_prep_row_tiles(int64_t rows);
-int64_t conv_bwd_tiles(int64_t T);
-int64_t norm_row_tiles(int64_t rows);
+// ev_begin / ev_end: NULL, or events recorded on s around the per-block kernel
+hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s);
 hipError_t launch_conv(const ConvArgs &a, bool bf16, bool bwd, hipStream_t s);
 hipError_t launch_norm(const NormArgs &a, bool bf16, bool bwd, hipStream_t s);
 hipError_t launch_dt_prep(const DtPrepArgs &a, hipStream_t s);

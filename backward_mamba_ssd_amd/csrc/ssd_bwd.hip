@@ -766,7 +766,7 @@ __global__ void __launch_bounds__(64) ssd_bwd_params_kernel(SsdBwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s) {
+hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s) {
     // partials of blocks past the end of the sequence stay untouched: clear them
     const int64_t nparts = a.Bsz * a.H * a.nchunks * (a.L / kLs);
     hipError_t e = launch_fill(reinterpret_cast<float *>(a.pA), 2 * nparts, 0.f, s);
@@ -784,11 +784,11 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nwg = a.Bsz * a.G * a.nchunks * (a.L / kLs);
-    if (a.ev_begin != nullptr && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
+    if (ev_begin != nullptr && (e = hipEventRecord(ev_begin, s)) != hipSuccess) return e;
     ssd_bwd_block_kernel<<<static_cast<unsigned>(nwg), kBlkThreads, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.ev_end != nullptr && (e = hipEventRecord(a.ev_end, s)) != hipSuccess) return e;
+    if (ev_end != nullptr && (e = hipEventRecord(ev_end, s)) != hipSuccess) return e;
     ssd_bwd_params_kernel<<<static_cast<unsigned>(a.H), 64, 0, s>>>(a);
     return hipGetLastError();
 }

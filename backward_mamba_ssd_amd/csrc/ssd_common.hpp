@@ -31,7 +31,6 @@ struct SsdBwdArgs {
     const float *dt, *A, *D, *chunk_states, *dh_final;
     void *dx;
     float *dB, *dC, *ddt, *dA, *dD, *dh0;
-    hipEvent_t ev_begin, ev_end;  // optional: recorded around the per-block kernel
     // workspace
     bf16_t *dstates;  // [Bsz, H, nchunks, 64 x 128]: gradient on the state leaving chunk c, in bf16,
                       // in pairs of 16 x 16 tiles in accumulator lane order (dstate_pair)

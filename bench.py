@@ -45,22 +45,29 @@ def fwd_bytes_per_token(w):
     return 2 * H * P + 2 * H * P + 2 * 2 * G * N + 4 * H + 4 * H * P * N / L
 
 
-def bwd_block_bytes_per_token(w):
-    """Algorithmic HBM bytes per token of the per-block backward kernel:
-    x, dy read and dx written (2 B each), the chunk-boundary state (4 B per
-    element) and the chunk-exit state gradient (2 B per element) read once per
-    chunk, B and C read (2 B), dB and dC written (4 B), dt read and ddt written
-    (4 B)."""
+def bwd_method_bytes_per_token(w):
+    """The method's algorithmic HBM bytes per token of the backward: x, dy read and dx
+    written (2 B each), the saved chunk-boundary state read once (4 B per element per
+    chunk), B and C read (2 B), dB and dC written (4 B), dt read and ddt written (4 B).
+    145,408 B/token at 256 heads x 64 x 128, 8 groups, chunk 256."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
-    return (3 * 2 * H * P + (4 + 2) * H * P * N / L + 2 * 2 * G * N + 2 * 4 * G * N + 2 * 4 * H)
+    return 3 * 2 * H * P + 4 * H * P * N / L + 2 * 2 * G * N + 2 * 4 * G * N + 2 * 4 * H
+
+
+def bwd_block_design_bytes_per_token(w):
+    """Bytes per token the per-block backward kernel of this design moves: the method's
+    backward bytes plus its read of the chunk-exit state gradients that the reverse
+    pass leaves in the workspace (bf16, once per chunk)."""
+    H, P, N, L = w.nheads, w.headdim, w.dstate, w.chunk
+    return bwd_method_bytes_per_token(w) + 2 * H * P * N / L
 
 
 def fwd_flops_per_token(w):
     """The method's MFMA-mapped flops of the chunked forward per token (causal halves
     counted once): group Gram L*N/hpg, intra-chunk output L*P, chunk state 2PN,
-    off-diagonal output 2PN, per head."""
+    off-diagonal output 2PN, per head (50,176 per token-head at the head shape above)."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
-    return H * (L * N / (H // G) + L * P + 3 * 2 * P * N)
+    return H * (L * N / (H // G) + L * P + 2 * P * N + 2 * P * N)
 
 
 def bwd_flops_per_token(w):
@@ -70,12 +77,13 @@ def bwd_flops_per_token(w):
     return H * (4 * P * N + 2 * L * P + 3 * L * N / (H // G) + 4 * P * N)
 
 
-def bwd_call_bytes_per_token(w):
-    """Algorithmic HBM bytes per token of the whole backward call of this design: the
-    reverse state pass (dy and C read, chunk-exit state gradients written once per
-    chunk in bf16) plus the per-block kernel (bwd_block_bytes_per_token)."""
+def bwd_call_design_bytes_per_token(w):
+    """Bytes per token the whole backward call of this design moves: the reverse state
+    pass (dy and C read, chunk-exit state gradients written once per chunk in bf16) plus
+    the per-block kernel (bwd_block_design_bytes_per_token).  The reverse pass reads dy,
+    C and dt a second time, so this exceeds the method's bytes."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
-    return 2 * H * P + 2 * G * N + 2 * H * P * N / L + bwd_block_bytes_per_token(w)
+    return 2 * H * P + 2 * G * N + 4 * H + 2 * H * P * N / L + bwd_block_design_bytes_per_token(w)
 
 
 def path_entry(flops, nbytes, ms, flop_peak_tflops=None):
@@ -98,6 +106,7 @@ def path_entry(flops, nbytes, ms, flop_peak_tflops=None):
 KERNEL_SOURCES = {
     "ssd_fwd_kernel": ("ssd_fwd.hip", "ssd_common.hpp", "common.hpp"),
     "ssd_bwd_block_kernel": ("ssd_bwd.hip", "ssd_common.hpp", "common.hpp"),
+    "ssd_bwd_dstate_kernel": ("ssd_bwd.hip", "ssd_common.hpp", "common.hpp"),
 }
 
 
@@ -207,13 +216,14 @@ def time_fwd_bwd(w, dev, steps, warmup):
             ev[0].record()
         ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], chunk=w.chunk,
                             h_final=None, chunk_states=cs, y=y)
+        args = (pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], cs, pr["dy"])
         if ev is not None:
             ev[1].record()
-            ssm.ssm_profile_next_bwd_block(ev[2], ev[3])
-        ssm.ssm_bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], cs, pr["dy"],
-                    chunk=w.chunk, out=grads, workspace=ws)
-        if ev is not None:
+            # the per-block kernel's own duration: the call records ev[2], ev[3] around it
+            ssm.ssm_bwd_timed(*args, (ev[2], ev[3]), chunk=w.chunk, out=grads, workspace=ws)
             ev[4].record()
+        else:
+            ssm.ssm_bwd(*args, chunk=w.chunk, out=grads, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -540,8 +550,11 @@ def long_context_rates(dev):
     log(f"long context: {wl.name}")
     r = time_fwd_bwd(wl, dev, steps=3, warmup=1)
     fb = fwd_flops_per_token(wl) + bwd_flops_per_token(wl)
-    by = fwd_bytes_per_token(wl) + bwd_call_bytes_per_token(wl)
+    by = fwd_bytes_per_token(wl) + bwd_method_bytes_per_token(wl)
     lc = path_entry(fb * r["tokens"], by * r["tokens"], r["step"][1])
+    lc["kernels_ms"] = {"ssd_fwd_kernel": round(r["fwd"][1], 4),
+                        "ssm_bwd_call": round(r["bwd"][1], 4),
+                        "ssd_bwd_block_kernel": round(r["blk"][1], 4)}
     lc["tokens_per_s"] = round(r["tokens"] * 3 / r["wall_s"], 1)
     lc["workload"] = wl.name
     return lc
@@ -611,24 +624,30 @@ def main():
     log(f"step {el / K * 1e3:.3f} ms: forward kernel {fwd_ms:.3f} ms, backward call {bwd_ms:.3f} ms "
         f"(per-block kernel {blk_ms:.3f} ms)")
 
+    # per kernel: (mean ms, the method's algorithmic bytes per launch, this design's bytes)
     kernels = {
-        "ssd_fwd_kernel": (fwd_ms, fwd_bytes_per_token(w) * tokens),
-        "ssd_bwd_block_kernel": (blk_ms, bwd_block_bytes_per_token(w) * tokens),
+        "ssd_fwd_kernel": (fwd_ms, fwd_bytes_per_token(w) * tokens, fwd_bytes_per_token(w) * tokens),
+        "ssd_bwd_block_kernel": (blk_ms, bwd_method_bytes_per_token(w) * tokens,
+                                 bwd_block_design_bytes_per_token(w) * tokens),
     }
     dom = max(kernels, key=lambda k: kernels[k][0])
-    ms, nbytes = kernels[dom]
+    ms, nbytes, dbytes = kernels[dom]
     achieved = nbytes / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(dom, w.name),
-                "kernel": dom, "mean_ms": round(ms, 4), "bytes_per_launch": int(nbytes)}
+                "kernel": dom, "mean_ms": round(ms, 4), "bytes_per_launch": int(nbytes),
+                "design_bytes_per_launch": int(dbytes)}
     ff, bf = fwd_flops_per_token(w) * tokens, bwd_flops_per_token(w) * tokens
-    fb, bb = fwd_bytes_per_token(w) * tokens, bwd_call_bytes_per_token(w) * tokens
+    fb, bb = fwd_bytes_per_token(w) * tokens, bwd_method_bytes_per_token(w) * tokens
     paths = {
         "fwd_chunked": path_entry(ff, fb, r["fwd"][1]),
         "bwd_call": path_entry(bf, bb, r["bwd"][1]),
         "fwd_bwd_step": path_entry(ff + bf, fb + bb, r["step"][1]),
     }
+    paths["bwd_call"]["design_bytes"] = int(bwd_call_design_bytes_per_token(w) * tokens)
+    paths["bwd_call"]["design_over_method_bytes"] = round(
+        bwd_call_design_bytes_per_token(w) / bwd_method_bytes_per_token(w), 3)
     res = {
         "metric": "SSM fwd+bwd tokens/s at 256h x 64 x 128",
         "value": round(value, 1),

@@ -48,7 +48,15 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the two enums get the fixed underlying type int: a caller in C (or through
+ * an FFI) may pass any int, and C++ gives an unfixed enum holding a value outside its
+ * enumerators' range undefined behaviour, before the validation could reject it.  The
+ * ABI is that of int either way. */
+#ifdef __cplusplus
+typedef enum ssm_status_e : int {
+#else
+typedef enum ssm_status_e {
+#endif
     SSM_OK = 0,
     SSM_ERR_NULL = 1,        /* a required pointer is NULL */
     SSM_ERR_DIMS = 2,        /* non-positive dim, nheads % ngroups != 0, ... */
@@ -59,7 +67,11 @@ typedef enum {
     SSM_ERR_HIP = 7          /* a HIP launch reported an error */
 } ssm_status;
 
-typedef enum { SSM_F32 = 0, SSM_BF16 = 1, SSM_F16 = 2 } ssm_dtype;
+#ifdef __cplusplus
+typedef enum ssm_dtype_e : int { SSM_F32 = 0, SSM_BF16 = 1, SSM_F16 = 2 } ssm_dtype;
+#else
+typedef enum ssm_dtype_e { SSM_F32 = 0, SSM_BF16 = 1, SSM_F16 = 2 } ssm_dtype;
+#endif
 
 typedef struct {
     int64_t batch;
@@ -126,6 +138,25 @@ ssm_status ssm_bwd(const ssm_dims *d, ssm_dtype dtype, const void *x, const void
                    const float *chunk_states, const void *dy, const float *dh_final, void *dx,
                    float *dB, float *dC, float *ddt, float *dA, float *dD, float *dh0,
                    void *workspace, size_t ws_bytes, ssm_stream stream);
+
+/*
+ * ssm_bwd with the per-block stage timed (for measurement; the pages print no
+ * such call).  Same arguments, results and validation as ssm_bwd, plus
+ * block_events: two hipEvent_t handles created by the caller on the current
+ * device.  When the chunked MFMA path runs, block_events[0] is recorded on
+ * `stream` immediately before the per-block backward kernel and block_events[1]
+ * immediately after it, so hipEventElapsedTime gives that kernel's duration;
+ * on the other paths both are recorded once at the start of the call.  Both
+ * events are first recorded before any work is enqueued, so an unusable event
+ * returns SSM_ERR_HIP with nothing written; NULL block_events, or a NULL
+ * handle, returns SSM_ERR_NULL.  No state is kept between calls.
+ */
+ssm_status ssm_bwd_timed(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                         const void *C, const float *dt, const float *A, const float *D,
+                         const float *chunk_states, const void *dy, const float *dh_final,
+                         void *dx, float *dB, float *dC, float *ddt, float *dA, float *dD,
+                         float *dh0, void *workspace, size_t ws_bytes, void *const *block_events,
+                         ssm_stream stream);
 
 /*
  * One-token decode state update, in place.  Same page, Kernel 1: decode
@@ -349,16 +380,6 @@ ssm_status ssm_dt_prep_bwd(const ssm_dims *d, const float *dt_raw, const float *
                            const float *logA, float dt_lo, float dt_hi, const float *ddt,
                            const float *dA, float *d_raw, float *d_bias, float *d_logA,
                            void *workspace, size_t ws_bytes, ssm_stream stream);
-
-/*
- * Benchmark timing hook (no counterpart on the pages).  `begin` and `end` are
- * hipEvent_t handles, or NULL to disarm.  The next ssm_bwd call that runs the
- * chunked MFMA path records `begin` on its stream immediately before its
- * per-block backward kernel and `end` immediately after it, then disarms the
- * hook; every other call ignores it.  The hook is process-global: arm it from
- * one thread around one call.  Nothing else changes in the call.
- */
-void ssm_profile_next_bwd_block(void *begin, void *end);
 
 #ifdef __cplusplus
 }

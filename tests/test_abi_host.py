@@ -95,6 +95,23 @@ def test_bwd_validation():
     assert bwd(dims(nheads=3, ngroups=2), ws=FAKE, wsb=need) == DIMS
 
 
+def test_timed_backward_validation():
+    # same validation as ssm_bwd; the event array is required, and both handles too
+    L = ssm.lib()
+    d = dims()
+    need = ssm.ssm_workspace_bytes(d, ssm.SSM_BF16, ssm.SSM_WS_BWD)
+    a = [FAKE] * 7 + [FAKE, None] + [FAKE] * 6 + [None]  # x..chunk_states, dy, dh_final, dx..dD, dh0
+
+    def timed(dd, ev, ws=FAKE, wsb=need):
+        return L.ssm_bwd_timed(ctypes.byref(dd), ssm.SSM_BF16, *a, ws, wsb, ev, None)
+
+    assert timed(d, None) == NULL
+    null_pair = (ctypes.c_void_p * 2)(None, None)
+    assert timed(d, null_pair) == NULL
+    assert timed(dims(nheads=3, ngroups=2), null_pair) == DIMS  # dims are checked first
+    assert timed(d, null_pair, ws=None) == WS
+
+
 def test_decode_replay_sr16_validation():
     L = ssm.lib()
     d = dims(seqlen=1)

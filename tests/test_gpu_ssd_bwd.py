@@ -7,8 +7,11 @@ workload (batch 4, 256 heads, T = 4096) is checked on one whole group over all
 batches (so dA/dD of its heads are complete); each batch of a 256-head problem run
 alone matches the batched run bit for bit (the two runs take the 4-wave and the
 8-wave form of the reverse pass); the long-context workload
-(T = 131,072, 512 saved chunk states per head) is checked per head over the
-full length and on all heads of a group over the final 1024 tokens.
+(T = 131,072, 512 saved chunk states per head) is checked over the full length
+on one whole group (its group-summed dB and dC, and every per-head gradient)
+and on two heads of other groups (outputs and saved states), with every oracle
+input a seeded input; and the ends of the retention range are covered.
+Every chunked case asserts that the MFMA kernels serve it.
 """
 import numpy as np
 import pytest
@@ -70,6 +73,7 @@ def test_shapes_outside_the_mfma_backward(ssm, t, h, g, L):
 def test_backward_deterministic(ssm):
     b, t, h, p, n, g, L = 2, 300, 8, 64, 128, 2, 128
     pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 5, dev, h0="randn", dh_final=True)
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
     _, _, _, g1 = _run(ssm, pr, L)
     _, _, _, g2 = _run(ssm, pr, L)
     torch.cuda.synchronize()
@@ -85,6 +89,7 @@ def test_batch_slices_are_independent(ssm):
     # the batch, so only their batch-summed values are compared, at tolerance.)
     b, t, h, p, n, g, L = 4, 320, 256, 64, 128, 8, 128
     pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 41, dev, h0="randn", dh_final=True)
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
     y, hf, cs, gr = _run(ssm, pr, L)
     dA = torch.zeros_like(gr["dA"], dtype=torch.float64)
     dD = torch.zeros_like(dA)
@@ -105,6 +110,7 @@ def test_batch_slices_are_independent(ssm):
 def test_full_prefill_workload_one_group(ssm):
     w = inputs.WORKLOADS["prefill_b4_t4096"]
     pr = inputs.make_workload_problem(w, dev)
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], w.chunk), ssm.SSM_BF16)
     _, _, _, gr = _run(ssm, pr, w.chunk)
     torch.cuda.synchronize()
     hpg = w.nheads // w.ngroups
@@ -122,38 +128,73 @@ def test_full_prefill_workload_one_group(ssm):
     assert_close("dh0", gr["dh0"][:, hs], ref["dh0"], 2e-2)
 
 
+def _one_head_groups(pr, heads, groups):
+    """The listed heads as one-head groups: x, dt, dy, A, D of those heads and, for each,
+    the B and C of the group that owns it.  The oracle's backward runs independent groups
+    on separate host threads; summing the one-head groups' dB/dC over the heads of a group
+    in ascending order adds exactly the per-head terms the oracle's own group sum adds,
+    in the same order."""
+    hs = list(heads)
+    return dict(x=pr["x"][:, :, hs], B=pr["B"][:, :, list(groups)], C=pr["C"][:, :, list(groups)],
+                dt=pr["dt"][:, :, hs], A=pr["A"][hs], D=pr["D"][hs])
+
+
 def test_long_context_workload(ssm):
     w = inputs.WORKLOADS["long_b1_t131072"]
     pr = inputs.make_workload_problem(w, dev)
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], w.chunk), ssm.SSM_BF16)
     y, hf, cs, gr = _run(ssm, pr, w.chunk)
     torch.cuda.synchronize()
     assert cs.shape[2] == w.seqlen // w.chunk == 512
     hpg = w.nheads // w.ngroups
-    # per head, whole sequence (dx, ddt, dA, dD, dh0 of a head depend on that head only)
-    for h in (0, 131):
-        gg = h // hpg
-        print(f"oracle long head {h}", flush=True)
-        sub = dict(x=pr["x"][:, :, h:h + 1], B=pr["B"][:, :, gg:gg + 1],
-                   C=pr["C"][:, :, gg:gg + 1], dt=pr["dt"][:, :, h:h + 1], A=pr["A"][h:h + 1],
-                   D=pr["D"][h:h + 1])
-        rf = oracle.fwd(**sub, chunk=w.chunk, want_chunk_states=True)
-        assert_close("y", y[:, :, h:h + 1], rf["y"], 2e-2)
-        assert_close("chunk_states", cs[:, h:h + 1], rf["chunk_states"], 2e-2)
-        rb = oracle.bwd(**sub, dy=pr["dy"][:, :, h:h + 1])
-        for k, got in (("dx", gr["dx"][:, :, h:h + 1]), ("ddt", gr["ddt"][:, :, h:h + 1]),
-                       ("dA", gr["dA"][h:h + 1]), ("dD", gr["dD"][h:h + 1]),
-                       ("dh0", gr["dh0"][:, h:h + 1])):
-            assert_close(k, got, rb[k], 2e-2)
-    # all heads of one group over the last 1024 tokens (a suffix: its gradients
-    # need no later tokens); the window starts from the saved chunk state
-    gg, win = 6, 1024
-    hs = slice(gg * hpg, (gg + 1) * hpg)
-    t0 = w.seqlen - win
-    print(f"oracle long group {gg} suffix window", flush=True)
-    rb = oracle.bwd(pr["x"][:, t0:, hs], pr["B"][:, t0:, gg:gg + 1], pr["C"][:, t0:, gg:gg + 1],
-                    pr["dt"][:, t0:, hs], pr["A"][hs], pr["D"][hs], pr["dy"][:, t0:, hs],
-                    h0=cs[:, hs, t0 // w.chunk])
-    assert_close("dB window", gr["dB"][:, t0:, gg:gg + 1], rb["dB"], 2e-2)
-    assert_close("dC window", gr["dC"][:, t0:, gg:gg + 1], rb["dC"], 2e-2)
-    assert_close("dx window", gr["dx"][:, t0:, hs], rb["dx"], 2e-2)
-    assert_close("ddt window", gr["ddt"][:, t0:, hs], rb["ddt"], 2e-2)
+    # Every oracle input below is a seeded input; no GPU output enters an oracle call.
+    # (1) two heads of other groups over the whole sequence: y, the 512 saved states
+    heads = (0, 131)
+    sub = _one_head_groups(pr, heads, [h // hpg for h in heads])
+    print(f"oracle long heads {heads}: forward", flush=True)
+    rf = oracle.fwd(**sub, chunk=w.chunk, want_chunk_states=True)
+    for i, h in enumerate(heads):
+        assert_close(f"y head {h}", y[:, :, h:h + 1], rf["y"][:, :, i:i + 1], 2e-2)
+        assert_close(f"chunk_states head {h}", cs[:, h:h + 1], rf["chunk_states"][:, i:i + 1],
+                     2e-2)
+    # (2) one whole group over the whole sequence: the group-summed dB and dC, and every
+    #     per-head gradient of its 32 heads
+    gg = 6
+    hs = range(gg * hpg, (gg + 1) * hpg)
+    sub = _one_head_groups(pr, hs, [gg] * hpg)
+    print(f"oracle long group {gg}: backward over {w.seqlen} tokens", flush=True)
+    rb = oracle.bwd(**sub, dy=pr["dy"][:, :, list(hs)])
+    dB = np.zeros(rb["dB"][:, :, 0].shape)
+    dC = np.zeros_like(dB)
+    for k in range(hpg):  # the group sum, heads ascending
+        dB += rb["dB"][:, :, k]
+        dC += rb["dC"][:, :, k]
+    hsl = slice(gg * hpg, (gg + 1) * hpg)
+    assert_close("dB group", gr["dB"][:, :, gg], dB, 2e-2)
+    assert_close("dC group", gr["dC"][:, :, gg], dC, 2e-2)
+    for k, got in (("dx", gr["dx"][:, :, hsl]), ("ddt", gr["ddt"][:, :, hsl]),
+                   ("dA", gr["dA"][hsl]), ("dD", gr["dD"][hsl]), ("dh0", gr["dh0"][:, hsl])):
+        assert_close(k, got, rb[k], 2e-2)
+    del rb
+    print(f"oracle long group {gg}: forward", flush=True)
+    rf = oracle.fwd(**sub, chunk=w.chunk, want_chunk_states=True)
+    assert_close("y group", y[:, :, hsl], rf["y"], 2e-2)
+    assert_close("h_final group", hf[:, hsl], rf["h_final"], 2e-2)
+    assert_close("chunk_states group", cs[:, hsl], rf["chunk_states"], 2e-2)
+
+
+@pytest.mark.parametrize("case", ["unit", "underflow", "big_h0"])
+def test_backward_at_the_ends_of_the_retention_range(ssm, case):
+    # retention 1 to float32 precision over T = 4096, retention underflowing within a
+    # token, and a large initial state (see test_gpu_ssd_fwd.retention_extreme)
+    from tests.test_gpu_ssd_fwd import retention_extreme
+    b, t, h, p, n, g, L = 1, 4096, 8, 64, 128, 2, 256
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 61, dev, h0="randn", dh_final=True)
+    pr = retention_extreme(pr, case)
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
+    _, _, _, gr = _run(ssm, pr, L)
+    ref = oracle.bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], pr["dy"],
+                     h0=pr["h0"], dh_final=pr["dh_final"])
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert_close(k, gr[k], ref[k], 2e-2)

@@ -4,7 +4,13 @@ Tolerance 2e-2 scaled error (bf16 MFMA operands, fp32 accumulation) on y,
 h_final and chunk_states.  Sizes span several 64-token blocks, partial chunks
 and ragged tails; the full prefill workload (batch 4, 256 heads, T = 4096,
 chunk 256) is checked on whole (batch, group) units, which the oracle computes
-exactly on their own since groups never interact.
+exactly on their own since groups never interact.  Every chunked case asserts
+that the MFMA kernels serve it.  The ends of the retention range
+exp(dt*A) in (0, 1] ("Nemotron 3 Ultra: replaying a rounded state", section
+"The Mamba state update") are covered too: a retention of 1 to float32
+precision over T = 4096 (the state sums every write), a retention that
+underflows to 0 within a token (dt*A <= -30: only the newest write survives),
+and an initial state 10^4 times the writes.
 """
 import numpy as np
 import pytest
@@ -24,9 +30,8 @@ def ssm():
     return m
 
 
-def _uses_mfma(ssm, pr, L):
-    d = ssm.dims_of(pr["x"], pr["B"], L)
-    return ssm.lib().ssm_uses_mfma_path(__import__("ctypes").byref(d), ssm.SSM_BF16)
+def _assert_mfma(ssm, pr, L):
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
 
 
 @pytest.mark.parametrize("t,L,h0", [(64, 64, "zero"), (200, 64, "randn"), (320, 128, "zero"),
@@ -34,6 +39,7 @@ def _uses_mfma(ssm, pr, L):
 def test_forward_matches_oracle(ssm, t, L, h0):
     b, h, p, n, g = 2, 8, 64, 128, 2
     pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 100 + t, dev, h0=h0)
+    _assert_mfma(ssm, pr, L)
     y, hf, cs = ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
                                     h0=pr["h0"], chunk=L)
     ref = oracle.fwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], h0=pr["h0"],
@@ -47,6 +53,8 @@ def test_forward_matches_oracle(ssm, t, L, h0):
 def test_chunk_size_only_moves_the_saved_states(ssm):
     b, t, h, p, n, g = 1, 512, 4, 64, 128, 1
     pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 7, dev)
+    for L in (64, 128, 256):
+        _assert_mfma(ssm, pr, L)
     outs = {L: ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
                                    chunk=L) for L in (64, 128, 256)}
     for L in (128, 256):
@@ -60,6 +68,7 @@ def test_prefill_equals_repeated_decode(ssm):
     full-sequence scan and repeated one-token decode must agree."""
     b, t, h, p, n, g = 2, 96, 4, 64, 128, 2
     pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 9, dev, h0="randn")
+    _assert_mfma(ssm, pr, 64)
     y, hf, _ = ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
                                    h0=pr["h0"], chunk=64)
     st = pr["h0"].clone()
@@ -76,6 +85,7 @@ def test_prefill_equals_repeated_decode(ssm):
 def test_full_prefill_workload_sampled_groups(ssm):
     w = inputs.WORKLOADS["prefill_b4_t4096"]
     pr = inputs.make_workload_problem(w, dev, with_dy=False)
+    _assert_mfma(ssm, pr, w.chunk)
     y, hf, cs = ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
                                     chunk=w.chunk)
     torch.cuda.synchronize()
@@ -89,3 +99,37 @@ def test_full_prefill_workload_sampled_groups(ssm):
         assert_close("y", y[bb:bb + 1, :, hs], ref["y"], 2e-2)
         assert_close("h_final", hf[bb:bb + 1, hs], ref["h_final"], 2e-2)
         assert_close("chunk_states", cs[bb:bb + 1, hs], ref["chunk_states"], 2e-2)
+
+
+def retention_extreme(pr, case):
+    """Move a seeded problem to one end of the retention range (in place, on the device).
+    unit: A = -exp(-20) per head, so dt*A ~ -3e-10 and exp(dt*A) rounds to 1 in float32;
+    underflow: dt in [1, 2] and A in [-60, -30], so dt*A <= -30 on every token;
+    big_h0: the initial state scaled by 10^4 against writes of order dt*|x||B|."""
+    if case == "unit":
+        pr["A"] = torch.full_like(pr["A"], -float(np.exp(-20.0)))
+    elif case == "underflow":
+        pr["dt"] = 1.0 + torch.rand(pr["dt"].shape, generator=torch.Generator(dev).manual_seed(3),
+                                    device=dev)
+        pr["A"] = -30.0 - 30.0 * torch.rand(pr["A"].shape,
+                                            generator=torch.Generator(dev).manual_seed(4),
+                                            device=dev)
+    elif case == "big_h0":
+        pr["h0"] = pr["h0"] * 1e4
+    return pr
+
+
+@pytest.mark.parametrize("case", ["unit", "underflow", "big_h0"])
+def test_forward_at_the_ends_of_the_retention_range(ssm, case):
+    b, t, h, p, n, g, L = 1, 4096, 8, 64, 128, 2, 256
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 60, dev, h0="randn")
+    pr = retention_extreme(pr, case)
+    _assert_mfma(ssm, pr, L)
+    y, hf, cs = ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"],
+                                    h0=pr["h0"], chunk=L)
+    ref = oracle.fwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], h0=pr["h0"],
+                     chunk=L, want_chunk_states=True)
+    torch.cuda.synchronize()
+    assert_close("y", y, ref["y"], 2e-2)
+    assert_close("h_final", hf, ref["h_final"], 2e-2)
+    assert_close("chunk_states", cs, ref["chunk_states"], 2e-2)
