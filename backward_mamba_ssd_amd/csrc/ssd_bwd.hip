@@ -18,10 +18,13 @@
 //   K[i][j]     = (dy_i . x_j) M[i][j] dt_j
 //   dC_i        = exp(Lam_i) H^T dy_i + sum_j K[i][j] B_j      (summed over heads)
 //   dB_j        = w_j dt_j dH^T x_j + sum_i K[i][j] C_i        (summed over heads)
-//   dLam_i      = sum_j K[i][j] G[i][j] - sum_i' K[i'][i] G[i'][i]
-//               + exp(Lam_i) dy_i . (H C_i) - w_i dt_i x_i . (dH B_i)
-//               + [i = 63] (exp(Lam_63) <dH, H> + sum_j w_j dt_j x_j . (dH B_j))
+//   dLam_i      = sum_{j<i} K[i][j] G[i][j] - sum_{i'>i} K[i'][i] G[i'][i]
+//               + exp(Lam_i) dy_i . (H C_i) - f_i
+//               + [i = 63] (exp(Lam_63) <dH, H> + sum_j f_j),   f_j = w_j dt_j x_j . (dH B_j)
 //   da_j        = sum_{i>=j} dLam_i,  dA += sum_j dt_j da_j,  dD += sum dy . x
+// (the diagonal K[i][i] G[i][i] would enter both sums of dLam_i and cancel; the f terms
+// reach da_j as sum_{i<j} f_i.  Both are summed that way, so that with strong decay the
+// order-one terms that cancel never meet the small ones in float32.)
 //   dH_in       = exp(Lam_63) dH + sum_i exp(Lam_i) dy_i C_i^T
 //
 // Three launches:
@@ -438,17 +441,23 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
             const float2 of = sm.offin[j][w];
-            dl += of.x - of.y;
+            dl += of.x;
             fs += of.y;
         }
-        const float fin_total = wave_total(fs);
         if (j == kLs - 1) {
             float dotv = 0.f;
 #pragma unroll
             for (int w = 0; w < 8; ++w) dotv += sm.dot[w];
-            dl += fin_total + __expf(le - lb0) * dotv;
+            dl += __expf(le - lb0) * dotv;
         }
-        const float da = wave_suffix_sum(dl);  // da_j = sum_{i >= j} dLam_i within the block
+        // The exit-gradient term f_i = w_i dt_i x_i.(dH B_i) enters dLam_i as -f_i and the
+        // block's last token as +sum_i f_i, so it reaches da_j = sum_{i >= j} dLam_i as the
+        // exclusive prefix sum_{i < j} f_i, summed directly (f_63, of order one even when
+        // every other term underflows, never meets the small ones).
+        // (the shuffle runs in all 64 lanes: a lane reading from an inactive one gets 0)
+        float fprev = __shfl_up(fs, 1, 64);
+        fprev = (j > 0) ? fprev : 0.f;
+        const float da = wave_suffix_sum(dl) + wave_prefix_sum(fprev);  // da_j = sum_{i >= j} dLam_i
         buf_st_f32(rddt, (static_cast<uint32_t>(k * kLs + j) * a.H + hc) * 4u, fmaf(head_A(hc - h0), da, ddd));
         const float pa = wave_total(ldc[base + j].y * da);
         if (lane == 0) {
@@ -530,7 +539,10 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     const float m = (j <= i) ? __expf(lam_i[v] - lam_j) : 0.f;
                     const float kv = dW[v] * m * dt_j;
                     Ks[q][v] += kv;
-                    const float r = kv * Gt[q][v];
+                    // R[i][i] enters row sum i and column sum i alike and cancels in
+                    // dLam_i, so it is left out of both: with strong decay it is the only
+                    // O(1) entry, and subtracting it would bury the small terms in rounding
+                    const float r = (j < i) ? kv * Gt[q][v] : 0.f;
                     rowacc[v] += r;
                     colacc += r;
                     qv[v] = Gt[q][v] * m;
