@@ -17,6 +17,7 @@ using namespace ssm;
 namespace {
 
 constexpr size_t kAlign = 256;
+static_assert(kNoAllocScratchBytes == SSM_NOALLOC_SCRATCH_BYTES, "ssm.h states the scratch size");
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -344,6 +345,25 @@ ssm_status ssm_bwd_timed(const ssm_dims *d, ssm_dtype dtype, const void *x, cons
     if (block_events == nullptr) return SSM_ERR_NULL;
     return bwd_impl(d, dtype, x, B, C, dt, A, D, chunk_states, dy, dh_final, dx, dB, dC, ddt, dA,
                     dD, dh0, workspace, ws_bytes, block_events, static_cast<hipStream_t>(stream));
+}
+
+ssm_status ssm_bwd_noalloc(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                           const void *C, const float *dt, const float *A, const float *D,
+                           const float *chunk_states, const void *dy, const float *dh_final,
+                           void *dx, float *dB, float *dC, float *ddt, float *dA, float *dD,
+                           float *dh0, ssm_stream stream) {
+    ssm_status st = check_dims(d, true);
+    if (st != SSM_OK) return st;
+    if (!valid_dtype(dtype)) return SSM_ERR_DTYPE;
+    if (!mfma_bwd_path(d, dtype) && !serial_supported(d)) return SSM_ERR_UNSUPPORTED;
+    const bool tokens = d->batch > 0 && d->seqlen > 0;
+    const size_t need = tokens ? bwd_ws_bytes(d, dtype) : 0;
+    if (need > kNoAllocScratchBytes) return SSM_ERR_WORKSPACE;  // beyond the library's scratch
+    void *ws = nullptr;
+    if (need > 0 && noalloc_scratch(&ws) != hipSuccess) return SSM_ERR_HIP;
+    return bwd_impl(d, dtype, x, B, C, dt, A, D, chunk_states, dy, dh_final, dx, dB, dC, ddt, dA,
+                    dD, dh0, ws, need > 0 ? kNoAllocScratchBytes : 0, nullptr,
+                    static_cast<hipStream_t>(stream));
 }
 
 ssm_status ssm_decode_step(const ssm_dims *d, ssm_dtype dtype, float *state, const void *x,

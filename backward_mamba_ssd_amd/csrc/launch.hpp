@@ -136,6 +136,12 @@ inline int64_t dt_prep_row_tiles(int64_t rows) { return (rows + kDtPrepRowsPerTi
 inline int64_t conv_bwd_tiles(int64_t T) { return (T + kConvBwdTile - 1) / kConvBwdTile; }
 inline int64_t norm_row_tiles(int64_t rows) { return (rows + kNormRows - 1) / kNormRows; }
 
+// Scratch of ssm_bwd_noalloc: one 4096-token sequence at 256 heads x 64 x 128 with chunk 256
+// (64 MiB of chunk-exit state gradients in bf16, 256 KiB of fp64 partials), rounded up.
+constexpr size_t kNoAllocScratchBytes = size_t{65} << 20;
+// The device address of the current device's scratch (looked up once per device).
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);
 hipError_t launch_copy(float *dst, const float *src, int64_t n, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);  // state or state16

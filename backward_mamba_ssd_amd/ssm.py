@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(_HERE, "libssm_mi355x.so")
 
 SSM_F32, SSM_BF16, SSM_F16 = 0, 1, 2
 SSM_WS_FWD, SSM_WS_BWD, SSM_WS_REPLAY, SSM_WS_DT_PREP_BWD = 0, 1, 2, 3
+NOALLOC_SCRATCH_BYTES = 65 << 20  # SSM_NOALLOC_SCRATCH_BYTES: the scratch of ssm_bwd_noalloc
 _SIZE_MAX = ctypes.c_size_t(-1).value
 
-EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_bwd_timed", "ssm_decode_step",
+EXPORTS = ("ssm_fwd_chunked", "ssm_bwd", "ssm_bwd_timed", "ssm_bwd_noalloc", "ssm_decode_step",
            "ssm_decode_step_sr16", "ssm_checkpoint_sr16", "ssm_replay", "ssm_draft_snapshots",
            "ssm_rollback", "ssm_conv1d_silu", "ssm_conv1d_silu_bwd",
            "ssm_conv1d_silu_workspace_bytes", "ssm_gated_rmsnorm", "ssm_gated_rmsnorm_bwd",
@@ -61,6 +62,8 @@ def _load():
     lib.ssm_bwd.restype = i32
     lib.ssm_bwd_timed.argtypes = [D, i32] + [vp] * 16 + [vp, sz, vp, vp]
     lib.ssm_bwd_timed.restype = i32
+    lib.ssm_bwd_noalloc.argtypes = [D, i32] + [vp] * 16 + [vp]
+    lib.ssm_bwd_noalloc.restype = i32
     lib.ssm_decode_step.argtypes = [D, i32] + [vp] * 8 + [vp]
     lib.ssm_decode_step.restype = i32
     lib.ssm_decode_step_sr16.argtypes = [D, i32] + [vp] * 8 + [u64, u64, vp]
@@ -259,7 +262,8 @@ def ssm_fwd_chunked(x, B, C, dt, A, D, h0=None, chunk=256, h_final=True, chunk_s
     return y, hf, cs
 
 
-def _bwd_prepare(x, B, C, dt, A, D, chunk_states, dy, dh_final, chunk, dh0, out, workspace):
+def _bwd_prepare(x, B, C, dt, A, D, chunk_states, dy, dh_final, chunk, dh0, out, workspace,
+                 need_workspace=True):
     b, t, h, p, g, n, dev = _seq_inputs(x, B, C, dt, A, D)
     _int("chunk", chunk, 1)
     nc = (t + chunk - 1) // chunk
@@ -290,7 +294,8 @@ def _bwd_prepare(x, B, C, dt, A, D, chunk_states, dy, dh_final, chunk, dh0, out,
             "dD": torch.empty((h,), **fo),
             "dh0": torch.empty((b, h, p, n), **fo) if dh0 else None,
         }
-    ws, wsb = _workspace(ssm_workspace_bytes(dims, code, SSM_WS_BWD), dev, workspace)
+    ws, wsb = (_workspace(ssm_workspace_bytes(dims, code, SSM_WS_BWD), dev, workspace)
+               if need_workspace else (None, 0))
     args = [ctypes.byref(dims), code, _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D),
             _ptr(chunk_states), _ptr(dy), _ptr(dh_final), _ptr(out["dx"]), _ptr(out["dB"]),
             _ptr(out["dC"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dD"]),
@@ -321,6 +326,18 @@ def ssm_bwd_timed(x, B, C, dt, A, D, chunk_states, dy, block_events, dh_final=No
         handles.append(ev.cuda_event)
     evs = (ctypes.c_void_p * 2)(*handles)
     _check(_lib.ssm_bwd_timed(*args, evs, _stream(stream)), "ssm_bwd_timed")
+    return out
+
+
+def ssm_bwd_noalloc(x, B, C, dt, A, D, chunk_states, dy, out, dh_final=None, chunk=256,
+                    stream=None):
+    """ssm_bwd over the library's own scratch: the caller passes every output in ``out``
+    (dx, dB, dC, ddt, dA, dD and optionally dh0) and nothing is allocated.  Returns ``out``."""
+    if out is None:
+        raise ValueError("out: the no-allocation backward writes into caller-provided outputs")
+    _, args = _bwd_prepare(x, B, C, dt, A, D, chunk_states, dy, dh_final, chunk, False, out,
+                           None, need_workspace=False)
+    _check(_lib.ssm_bwd_noalloc(*args[:-2], _stream(stream)), "ssm_bwd_noalloc")
     return out
 
 

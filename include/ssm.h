@@ -159,6 +159,29 @@ ssm_status ssm_bwd_timed(const ssm_dims *d, ssm_dtype dtype, const void *x, cons
                          ssm_stream stream);
 
 /*
+ * ssm_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same inputs,
+ * outputs, results and validation as ssm_bwd, without the workspace: the
+ * kernels use a scratch array the library holds in device memory, one copy per
+ * GPU it runs on, from module load until the process ends.  The array holds
+ * 65 MiB (SSM_NOALLOC_SCRATCH_BYTES), enough for one 4096-token sequence at
+ * 256 heads x 64 x 128 with chunk 256; when ssm_workspace_bytes(d, dtype,
+ * SSM_WS_BWD, 0) exceeds it the call returns SSM_ERR_WORKSPACE and does nothing.
+ * The call itself allocates nothing and calls no allocating routine; the first
+ * call on a device looks up that device's copy of the array (SSM_ERR_HIP if the
+ * lookup fails, before any work).  Every call on a GPU shares that GPU's array
+ * and leaves its contents behind: calls that overlap on one GPU (on different
+ * streams, or from different threads) race and must be serialised by the
+ * caller.  Results are bit-identical to ssm_bwd's.
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)65 << 20)
+ssm_status ssm_bwd_noalloc(const ssm_dims *d, ssm_dtype dtype, const void *x, const void *B,
+                           const void *C, const float *dt, const float *A, const float *D,
+                           const float *chunk_states, const void *dy, const float *dh_final,
+                           void *dx, float *dB, float *dC, float *ddt, float *dA, float *dD,
+                           float *dh0, ssm_stream stream);
+
+/*
  * One-token decode state update, in place.  Same page, Kernel 1: decode
  * evaluates the same recurrence for one step.  `d->seqlen` and `d->chunk` are
  * ignored.  Shapes: state [batch,nheads,headdim,dstate] float (in/out),

@@ -122,6 +122,23 @@ void chunked() {
     Ws ws(need);
     ACCEPT(ssm_bwd_timed(&db, SSM_BF16, F, F, F, Ff, Ff, Ff, Ff, F, nullptr, F, Ff, Ff, Ff, Ff, Ff,
                          nullptr, ws.p, ws.n, ev, nullptr));
+    // the no-allocation backward: up to the library's scratch, whose regions it carves
+    auto noalloc = [&](const ssm_dims *dd, const float *cs) {
+        return ssm_bwd_noalloc(dd, SSM_BF16, F, F, F, Ff, Ff, Ff, cs, F, nullptr, F, Ff, Ff, Ff,
+                               Ff, Ff, nullptr, nullptr);
+    };
+    const ssm_dims one_seq = dims(1, 4096, 256, 64, 128, 8, 256);   // fits the scratch
+    const ssm_dims two_seq = dims(2, 4096, 256, 64, 128, 8, 256);   // does not
+    EXPECT(ssm_workspace_bytes(&one_seq, SSM_BF16, SSM_WS_BWD, 0) <= SSM_NOALLOC_SCRATCH_BYTES);
+    REJECT(SSM_ERR_WORKSPACE, noalloc(&two_seq, Ff));
+    REJECT(SSM_ERR_DIMS, noalloc(&bad_groups, Ff));
+    REJECT(SSM_ERR_NULL, noalloc(&one_seq, nullptr));
+    {
+        const int ov = stub::overlaps;
+        ACCEPT(noalloc(&one_seq, Ff));
+        ACCEPT(noalloc(&db, Ff));
+        EXPECT(stub::overlaps == ov);
+    }
     EXPECT(ssm_workspace_bytes(&odd_state, SSM_BF16, SSM_WS_BWD, 0) == static_cast<size_t>(-1));
     EXPECT(ssm_workspace_bytes(&d, static_cast<ssm_dtype>(9), SSM_WS_FWD, 0) == static_cast<size_t>(-1));
 }

@@ -8,6 +8,7 @@
 // region that runs past the caller's buffer is an AddressSanitizer error, and two regions
 // that overlap fail the check.
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -45,6 +46,15 @@ void fill_and_check(std::initializer_list<Region> regions) {
 }  // namespace
 
 extern "C" hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
+
+namespace ssm {
+// the no-allocation backward's scratch: a host buffer of the stated size
+hipError_t noalloc_scratch(void **ptr) {
+    static void *buf = std::aligned_alloc(256, kNoAllocScratchBytes);
+    *ptr = buf;
+    return buf ? hipSuccess : hipErrorOutOfMemory;
+}
+}  // namespace ssm
 
 namespace ssm {
 
