@@ -346,6 +346,127 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Replay without the lockstep copy, snapshots or chunk saves: the state (and, when
+// asked, y) of r retained tokens.  No LDS and no barrier: a thread holds 8
+// consecutive rows of 4 coordinates, so each token needs one 16-byte load of x (its 8
+// rows in bf16), 4 values of B (and of C), and every wave streams its own rows.  The
+// retention factors are computed 64 tokens at a time, one token per lane, and each
+// token's dt and exp(dt*A) are then read from its lane with readlane (one transcendental
+// per 64 tokens instead of one per token).  A token's inputs are loaded one token
+// ahead, as raw bits, and widened when used.  The update and the read are row_update /
+// row_step with the retention, B*dt and lane tree of the decode kernel, so the states
+// and outputs equal those of r decode calls bit for bit.  A 256-thread workgroup covers
+// 1024 * 8 / N rows of one (batch, head).  Requires x 16-byte aligned and headdim a
+// multiple of 8 (the host checks); rows past headdim are never touched.
+// ---------------------------------------------------------------------------
+constexpr int kReplayRows = 8;  // rows per thread
+
+template <int N, typename T, typename CK, bool Y>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 4 : (Y ? 6 : 8))))
+replay_kernel(ScanArgs a) {
+    constexpr int LPR = N / 4;  // lanes per state row
+    constexpr int R = kReplayRows;
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int n0 = (tid % LPR) * 4;
+    const int p0 = (tid / LPR) * R;  // first of this thread's rows
+    const int64_t PN = static_cast<int64_t>(a.P) * N;
+    const bool rows = p0 < a.P;      // all R rows exist (P % R == 0); whole lane groups agree
+    const int xoff = rows ? p0 : 0;  // lanes without rows read row 0's x and discard it
+
+    float4 s[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (rows && a.ckpt != nullptr) {
+            const int64_t off = bh * PN + static_cast<int64_t>(p0 + i) * N + n0;
+            const CK *ck = static_cast<const CK *>(a.ckpt);
+            if constexpr (sizeof(CK) == 4) {
+                s[i] = nt_ld4(ck + off);
+            } else {
+                typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+                typedef float f32x4v __attribute__((ext_vector_type(4)));
+                const h16x4 hv = __builtin_nontemporal_load(reinterpret_cast<const h16x4 *>(ck + off));
+                const f32x4v fv = __builtin_convertvector(hv, f32x4v);
+                s[i] = make_float4(fv[0], fv[1], fv[2], fv[3]);
+            }
+        }
+    }
+    if (a.r > 0) {
+        const float Ah = a.A[h], Dh = a.D[h];
+        // token k of the replay is token t0 + k of the sequence
+        const int64_t tok0 = static_cast<int64_t>(b) * a.T + a.t0;
+        const int64_t xs = static_cast<int64_t>(a.H) * a.P, bs = static_cast<int64_t>(a.G) * N;
+        const T *xk = static_cast<const T *>(a.x) + (tok0 * a.H + h) * a.P + xoff;
+        const T *bk = static_cast<const T *>(a.B) + (tok0 * a.G + g) * N + n0;
+        const T *ck = static_cast<const T *>(a.C) + (tok0 * a.G + g) * N + n0;
+        const float *dk = a.dt + tok0 * a.H + h;
+        T *yk = Y ? static_cast<T *>(a.y) + (tok0 * a.H + h) * a.P + p0 : nullptr;
+        using Raw = typename std::conditional<sizeof(T) == 2, u16x4, float4>::type;  // 4 values
+        using RawX = typename std::conditional<sizeof(T) == 2, u16x8, float4>::type;
+        constexpr int XL = sizeof(T) == 2 ? 1 : 2;  // 16-byte loads of x per token
+        auto raw4 = [](const T *q) { return *reinterpret_cast<const Raw *>(q); };
+        auto wide = [](const Raw &v) -> float4 {
+            if constexpr (sizeof(T) == 2)
+                return make_float4(bf16_to_f32(v[0]), bf16_to_f32(v[1]), bf16_to_f32(v[2]), bf16_to_f32(v[3]));
+            else
+                return v;
+        };
+        auto xload = [&](RawX *dst, int64_t k) {
+#pragma unroll
+            for (int q = 0; q < XL; ++q) dst[q] = *reinterpret_cast<const RawX *>(xk + k * xs + q * 4);
+        };
+        auto xwide = [&](const RawX *v, int i) -> float {
+            if constexpr (sizeof(T) == 2) return bf16_to_f32(v[0][i]);
+            else return reinterpret_cast<const float *>(&v[i / 4])[i % 4];
+        };
+        Raw bq = raw4(bk), cq{};
+        if constexpr (Y) cq = raw4(ck);
+        RawX xq[XL];
+        xload(xq, 0);
+        float dt_l = 0.f, av_l = 0.f;  // dt and retention of token k0 + lane
+        for (int64_t k = 0; k < a.r; ++k) {
+            const int kl = static_cast<int>(k & 63);
+            if (kl == 0) {
+                const int64_t kk = k + lane;
+                dt_l = (kk < a.r) ? dk[kk * a.H] : 0.f;
+                av_l = retention(dt_l, Ah);
+            }
+            const float dtv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dt_l), kl));
+            const float av = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(av_l), kl));
+            const Raw bc = bq, cc = cq;
+            RawX xc[XL];
+#pragma unroll
+            for (int q = 0; q < XL; ++q) xc[q] = xq[q];
+            const int64_t kn = (k + 1 < a.r) ? k + 1 : k;  // the last token re-reads itself
+            bq = raw4(bk + kn * bs);
+            if constexpr (Y) cq = raw4(ck + kn * bs);
+            xload(xq, kn);
+            const float4 bdt = scale4(wide(bc), dtv);
+            if constexpr (Y) {
+                const float4 c = wide(cc);
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const float xp = xwide(xc, i);
+                    float acc = row_step(s[i], av, xp, bdt, c);
+                    acc = row_reduce<LPR>(acc);
+                    if (rows && (tid % LPR) == 0) IO<T>::st(yk, k * xs + i, fmaf(Dh, xp, acc));
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < R; ++i) row_update(s[i], av, xwide(xc, i), bdt);
+            }
+        }
+    }
+    if (a.state_out != nullptr && rows) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            *reinterpret_cast<float4 *>(a.state_out + bh * PN + static_cast<int64_t>(p0 + i) * N + n0) = s[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Rollback after verification of a draft ("Nemotron 3 Ultra: replaying a rounded
 // state", section "Rolling back rejected draft tokens": the selected snapshot is
 // the state after the accepted prefix).  A gather copy, 16 bytes per lane: grid
@@ -652,8 +773,31 @@ static hipError_t launch_scan_tcl(const ScanArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <typename T, typename CK, bool Y>
+static hipError_t launch_replay_tcy(const ScanArgs &a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.Bsz * a.H)), block(256);
+    switch (a.N) {
+        case 16: replay_kernel<16, T, CK, Y><<<grid, block, 0, s>>>(a); break;
+        case 32: replay_kernel<32, T, CK, Y><<<grid, block, 0, s>>>(a); break;
+        case 64: replay_kernel<64, T, CK, Y><<<grid, block, 0, s>>>(a); break;
+        case 128: replay_kernel<128, T, CK, Y><<<grid, block, 0, s>>>(a); break;
+        case 256: replay_kernel<256, T, CK, Y><<<grid, block, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename CK>
+static hipError_t launch_replay_tc(const ScanArgs &a, hipStream_t s) {
+    return a.y ? launch_replay_tcy<T, CK, true>(a, s) : launch_replay_tcy<T, CK, false>(a, s);
+}
+
 template <typename T, typename CK>
 static hipError_t launch_scan_tc(const ScanArgs &a, hipStream_t s) {
+    // the state (and y) alone, x in whole 16-byte pieces per thread: the replay kernel
+    const bool plain = a.live == nullptr && a.snap == nullptr && a.chunk_states == nullptr;
+    const bool xvec = (reinterpret_cast<uintptr_t>(a.x) % 16) == 0 && (a.P % kReplayRows) == 0;
+    if (plain && xvec) return launch_replay_tc<T, CK>(a, s);
     return a.live ? launch_scan_tcl<T, CK, true>(a, s) : launch_scan_tcl<T, CK, false>(a, s);
 }
 

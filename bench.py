@@ -560,6 +560,23 @@ def long_context_rates(dev):
     return lc
 
 
+def copy_calibration(dev):
+    """Three plain 1 GiB device-to-device copies: the known-size reference that scales
+    the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of a profiled run."""
+    import torch
+
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    n = src.numel() * 4
+    del src, dst
+    torch.cuda.empty_cache()
+    return n
+
+
 SECTIONS = {
     "decode": decode_rates,
     "dt_prep": dt_prep_rates,
@@ -609,8 +626,10 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.section:
-        print(json.dumps({"section": args.section, **{"result": SECTIONS[args.section](dev)}}),
-              flush=True)
+        out = {"section": args.section, "result": SECTIONS[args.section](dev)}
+        if args.copy_calibration:
+            out["copy_calibration_bytes"] = copy_calibration(dev)
+        print(json.dumps(out), flush=True)
         return
     w = inputs.WORKLOADS[args.workload]
     log(f"workload {w.name}: batch {w.batch} T {w.seqlen} heads {w.nheads} P {w.headdim} "
@@ -682,14 +701,7 @@ def main():
         res["secondary"] = secondary(dev)
         torch.cuda.empty_cache()
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        res["copy_calibration_bytes"] = src.numel() * 4
-        del src, dst
+        res["copy_calibration_bytes"] = copy_calibration(dev)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(w)
