@@ -28,8 +28,35 @@ __device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
 }
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 
-__device__ __forceinline__ uint16_t sr16_bits(float v, uint32_t u) {
-    const uint32_t b = __float_as_uint(v);
+// The same rule in the binary16 normal range, 2^-14 <= |v| < 65536 (float32 biased
+// exponent 113..142), on the float32 bit pattern directly.  There the kept integer and
+// the 13 discarded bits d are the top and bottom of the magnitude's bits, R = d << 19,
+// and u < R holds exactly when (u >> 19) < d, that is when adding 8191 - (u >> 19) to
+// the magnitude carries out of the 13 discarded bits.  So the result is
+// sign | (((mag + 8191 - (u >> 19)) >> 13) - (112 << 10)): the exponent is rebiased by
+// the subtraction, and a carry moves to the next binade by itself, from the top binade
+// to 0x7C00 (infinity), as in sr16_bits.  Bit for bit equal to sr16_bits on that range.
+__host__ __device__ __forceinline__ bool sr16_in_normal_range(float v) {
+    return ((__builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu) - 0x38800000u) < 0x0F000000u;
+}
+__host__ __device__ __forceinline__ uint16_t sr16_bits_normal(float v, uint32_t u) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const uint32_t mag = b & 0x7FFFFFFFu;
+    const uint32_t r = ((mag + (8191u - (u >> 19))) >> 13) - (112u << 10);
+    return static_cast<uint16_t>(((b >> 16) & 0x8000u) | r);
+}
+
+// The rule for any float32: the short form in the binary16 normal range (almost every
+// value of a state), the general one for the rest (a wave skips either branch when none
+// of its lanes needs it).
+__host__ __device__ __forceinline__ uint16_t sr16_bits_general(float v, uint32_t u);
+__host__ __device__ __forceinline__ uint16_t sr16_bits(float v, uint32_t u) {
+    if (sr16_in_normal_range(v)) return sr16_bits_normal(v, u);
+    return sr16_bits_general(v, u);
+}
+
+__host__ __device__ __forceinline__ uint16_t sr16_bits_general(float v, uint32_t u) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
     const uint32_t sign = (b >> 16) & 0x8000u;
     const uint32_t mag = b & 0x7FFFFFFFu;
     if (mag > 0x7F800000u) return static_cast<uint16_t>(sign | 0x7E00u);  // NaN

@@ -186,6 +186,22 @@ def test_sr16_bits_match_oracle(ssm):
         want = oracle.sr16(vals, seed, ck, off)
         g = got.cpu().numpy().view(np.uint16)
         assert np.array_equal(g, want), int(np.sum(g != want))
+    # values in the binary16 normal range only, so whole waves take the short form of the
+    # rule: binade edges, the top binade's carry into infinity, both signs
+    edges = np.array([2.0 ** e * (1.0 + f) for e in range(-14, 16)
+                      for f in (0.0, 2.0 ** -11, 0.5, 1.0 - 2.0 ** -11, 1.0 - 2.0 ** -23)])
+    normal = np.concatenate([
+        np.tile(np.concatenate([edges, -edges, [65504.0, 65519.0, 65520.0, 65535.99, -65530.0]]),
+                200),
+        r.choice([-1.0, 1.0], 300000) * 2.0 ** r.uniform(-14, 16, 300000),
+    ]).astype(np.float32)
+    normal = normal[(np.abs(normal) >= 2.0 ** -14) & (np.abs(normal) < 65536.0)]
+    for seed, ck, off in ((3, 1, 0), (2 ** 40 + 1, 9, 12345)):
+        got = ssm.ssm_checkpoint_sr16(torch.from_numpy(normal).to(dev), seed, ck, off)
+        torch.cuda.synchronize()
+        want = oracle.sr16(normal, seed, ck, off)
+        g = got.cpu().numpy().view(np.uint16)
+        assert np.array_equal(g, want), int(np.sum(g != want))
     # ragged length and a non-multiple-of-8 offset into a larger state
     v = torch.from_numpy(vals[:1003]).to(dev)
     got = ssm.ssm_checkpoint_sr16(v, 99, 2, 17).cpu().numpy().view(np.uint16)
