@@ -235,8 +235,15 @@ struct __align__(16) BlkSmem {
     // previous head during S2, so they are double-buffered by head parity
     // (token-major, so the combine reads each token's partials with a few wide loads)
     float row[2][2][kLs], col[2][kLs][4], dd[kLs][4];  // row: [wh][token], 4 tokens per write
-    float2 offin[kLs][8];  // (dy.(H C), x.(dH B)) partials per token and n-tile wave
+    float fp[kLs][4];      // f_j = w_j dt_j x_j.(dH B_j) partials per token and p-tile wave
+    float offin[kLs][8];   // dy_i.(H C_i) exp(Lam_i) partials per token and n-tile wave
     float dot[8], dd_sum[2][8];
+    // Per-token decay factors of a head, by head parity, computed once per head one phase
+    // ahead of their use (instead of an exponential per thread per use): fac[t] for a
+    // chunk token t outside block k is the factor that scales its row for the state
+    // products, for t in block k it is exp(Lam_t - Lam_blk0); w[i] = exp(Lam_e - Lam_i)
+    // for the tokens of block k; es = exp(Lam_blk0), ee = exp(Lam_end - Lam_e).
+    float fac[2][kMaxBlk * kLs], w[2][kLs], es[2], ee[2];
 };
 static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the state tiles");
 
@@ -256,6 +263,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const int64_t cend = (cstart + a.L < T) ? cstart + a.L : T;
     const int nbc = static_cast<int>((cend - cstart + kLs - 1) / kLs);
     const int hpg = a.H / a.G;
+    const int kS_ = 64 * k - 1, kE_ = 64 * k + kLs - 1, kEnd_ = 64 * nbc - 1, base_ = 64 * k;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int wq = wave & 3, wh = wave >> 2;
     // Lane-derived indices are re-formed at the top of every head iteration from a
@@ -355,6 +363,26 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         dstp[0] = f32x4v{off + v0, dtr[0], off + v1, dtr[1]};
         dstp[1] = f32x4v{off + v2, dtr[2], off + v3, dtr[3]};
     };
+    // the decay factors of the head whose (Lam, dt) sit in ld[par] (threads 0..255, one
+    // chunk token each; two exponentials where the token is in block k, one elsewhere)
+    auto factors = [&](int par) {
+        const int t = static_cast<int>(threadIdx.x);
+        if (t < kMaxBlk * kLs) {
+            const float2 *lp = sm.ld[par];
+            const float lb0 = kS_ >= 0 ? lp[kS_].x : 0.f, le = lp[kE_].x;
+            const float2 lt = lp[t];
+            if (t >= base_ && t < base_ + kLs) {  // whole waves: block k is 64 aligned tokens
+                sm.fac[par][t] = __expf(lt.x - lb0);
+                sm.w[par][t - base_] = __expf(le - lt.x);
+            } else {
+                sm.fac[par][t] = t < base_ ? __expf(lb0 - lt.x) * lt.y : __expf(lt.x - le);
+            }
+            if (t == 0) {
+                sm.es[par] = __expf(lb0);
+                sm.ee[par] = __expf(lp[kEnd_].x - le);
+            }
+        }
+    };
     // states in accumulators, [n][p], 2 x 2 tiles per wave: q -> n-tile 2wq + q/2,
     // p-tile 2wh + q%2
     // raw chunk-boundary state and chunk-exit gradient of the next head, loaded a full
@@ -380,6 +408,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     load_states(h0);
     if (wave == 0) scan(h0, 0);
     __syncthreads();
+    factors(0);
     // Gram tiles of block k, [i][j]: i-tile wq, j-tiles 2wh, 2wh+1
     f32x4 Gt[2];
 #pragma unroll
@@ -393,17 +422,13 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                               &sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk], Gt[q]);
         }
     }
-    // B and C of block k at this lane's (token, n) positions of the Phase III/IV tiles
-    float cC[4][4], cB[4][4];
+    // C of block k at this lane's (token, n) positions of the Phase III tiles
+    float cC[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const u16x4 c4 = *reinterpret_cast<const u16x4 *>(&sm.C[(16 * tt + lr) * kS128 + 16 * wave + lq]);
-        const u16x4 b4 = *reinterpret_cast<const u16x4 *>(&sm.B[(16 * tt + lr) * kS128 + 16 * wave + lq]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            cC[tt][v] = bf16_to_f32(c4[v]);
-            cB[tt][v] = bf16_to_f32(b4[v]);
-        }
+        for (int v = 0; v < 4; ++v) cC[tt][v] = bf16_to_f32(c4[v]);
     }
     f32x4 Ks[2], dCa[4], dBa[4];  // Ks like Gt; dCa/dBa [n][tok]: n-tile = wave, tok-tiles 0..3
 #pragma unroll
@@ -413,10 +438,10 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         dCa[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         dBa[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int kS = 64 * k - 1;              // chunk-local index of the token before block k
-    const int kE = 64 * k + kLs - 1;        // last token of block k
-    const int kEnd = 64 * nbc - 1;          // last (padded) token of the chunk
-    const int base = 64 * k;
+    const int kS = kS_;      // chunk-local index of the token before block k
+    const int kE = kE_;      // last token of block k
+    const int base = base_;
+    __syncthreads();  // the first head's decay factors
 
     // Per-token combine of head hc (wave 0, lane = token of the block): the dLam terms,
     // da = reverse cumulative sum within the block, ddt, and the dA/dD partials.  Runs
@@ -431,19 +456,21 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const float2 rw = make_float2(sm.row[pc][0][j], sm.row[pc][1][j]);
         const f32x4v cl = *reinterpret_cast<const f32x4v *>(sm.col[pc][j]);
         const f32x4v dv = *reinterpret_cast<const f32x4v *>(sm.dd[j]);
+        const f32x4v fv = *reinterpret_cast<const f32x4v *>(sm.fp[j]);
+        const f32x4v o0 = *reinterpret_cast<const f32x4v *>(&sm.offin[j][0]);
+        const f32x4v o1 = *reinterpret_cast<const f32x4v *>(&sm.offin[j][4]);
         float dl = rw.x + rw.y;
         float ddd = 0.f, fs = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             dl -= cl[w];
             ddd += dv[w];
+            fs += fv[w];
         }
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            const float2 of = sm.offin[j][w];
-            dl += of.x;
-            fs += of.y;
-        }
+        for (int w = 0; w < 4; ++w) dl += o0[w];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dl += o1[w];
         if (j == kLs - 1) {
             float dotv = 0.f;
 #pragma unroll
@@ -476,8 +503,6 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const int64_t bh = static_cast<int64_t>(b) * a.H + h;
         const float Ah = head_A(hh), Dh = head_D(hh);
         const float2 *ld = sm.ld[par];  // (Lam, dt) of this head's chunk
-        const float lam_blk0 = kS >= 0 ? ld[kS].x : 0.f;  // block-local Lam_i = Lam[base+i] - lam_blk0
-        const float lam_e = ld[kE].x;
         // The next head's loads are issued on every iteration (the last one re-reads its own
         // head), so each iteration issues the same memory operations and the waits on them
         // count exactly instead of draining everything in flight.
@@ -493,8 +518,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 *reinterpret_cast<u16x8 *>(&sm.dY[pr_tok * kS64 + pr_col]) = yk;
                 continue;
             }
-            const float2 lt = ld[tl];
-            const float cf = kb < k ? __expf(lam_blk0 - lt.x) * lt.y : __expf(lt.x - lam_e);
+            const float cf = sm.fac[par][tl];
             const int slot = kb < k ? kb : kb - 1;
             const u16x8 v = xr[kb];
             typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -598,8 +622,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         // ---- S3: block-entry state and exit gradient in bf16, [p][n] ----
         bf16_t *Hb = sm.R, *dHb = sm.R + kT128;
         {
-            const float es = __expf(lam_blk0);           // chunk start -> block k start
-            const float ee = __expf(ld[kEnd].x - lam_e);  // block k end -> chunk end
+            const float es = sm.es[par];  // chunk start -> block k start
+            const float ee = sm.ee[par];  // block k end -> chunk end
             float dotp = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -624,6 +648,17 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         // the next head's chunk-boundary state and exit gradient (this head's were consumed
         // in S3); issued here rather than inside S3, where they queued behind the row prefetch
         load_states(hn);
+        // the next head's decay factors (waves 0..3, which reach the next barrier first)
+        factors(par ^ 1);
+        // this head's per-token scales of the Phase III/IV tiles (token 16 tt + lr), read here
+        // so that the reads are in flight during Phase II
+        float ei_t[4], wdt_t[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int i = 16 * tt + lr;
+            ei_t[tt] = sm.fac[par][base + i];
+            wdt_t[tt] = sm.w[par][i] * ld[base + i].y;
+        }
         // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tiles 2wh, 2wh+1) ----
         u16x4 dxo[2];
         uint32_t dxoff[2];
@@ -652,21 +687,28 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int j = 16 * (2 * wh + q) + lr;
-                const float2 lj = ld[base + j];
-                const float wj = __expf(lam_e - lj.x), dt_j = lj.y;
+                const float wj = sm.w[par][j], dt_j = ld[base + j].y;
                 const u16x4 x4 = *reinterpret_cast<const u16x4 *>(&sm.X[j * kS64 + 16 * wq + lq]);
                 const u16x4 y4 = *reinterpret_cast<const u16x4 *>(&sm.dY[j * kS64 + 16 * wq + lq]);
-                float ddp = 0.f, dxv[4];
+                // acc4[j][p] = (dH B_j)[p]: with x it also gives the exit-gradient term
+                // f_j = w_j dt_j x_j.(dH B_j) of dLam (this wave's p-tile)
+                float ddp = 0.f, xb = 0.f, dxv[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
+                    const float xv = bf16_to_f32(x4[v]);
                     const float pre = fmaf(wj, acc4[q][v], acc[q][v]);
-                    ddp = fmaf(bf16_to_f32(x4[v]), pre, ddp);
+                    ddp = fmaf(xv, pre, ddp);
+                    xb = fmaf(xv, acc4[q][v], xb);
                     dxv[v] = fmaf(Dh, bf16_to_f32(y4[v]), dt_j * pre);
                 }
                 dxoff[q] = static_cast<uint32_t>(k * kLs + j) * tokb + (h * kP + 16 * wq + lq) * 2;
                 dxo[q] = pack4(dxv[0], dxv[1], dxv[2], dxv[3]);
                 ddp = rows4_sum(ddp);
-                if (lane < 16) sm.dd[j][wq] = ddp;
+                xb = rows4_sum(xb) * (wj * dt_j);
+                if (lane < 16) {
+                    sm.dd[j][wq] = ddp;
+                    sm.fp[j][wq] = xb;
+                }
             }
         }
         // Phase III / IV: per-head dC, dB contributions (n-tile = wave, tok-tiles 0..3);
@@ -678,31 +720,41 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 fH[kk] = frag_tr(Hb, kS128, 16 * wave, 32 * kk, lane);
                 fdH[kk] = frag_tr(dHb, kS128, 16 * wave, 32 * kk, lane);
             }
+            bf16x8 fy[2][2], fxx[2][2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                fy[0][kk] = frag_row(&sm.dY[lr * kS64 + 32 * kk + lk]);
+                fxx[0][kk] = frag_row(&sm.X[lr * kS64 + 32 * kk + lk]);
+            }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const int i = 16 * tt + lr;
+                const int cb = tt & 1;
+                if (tt + 1 < 4) {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        fy[cb ^ 1][kk] = frag_row(&sm.dY[(16 * (tt + 1) + lr) * kS64 + 32 * kk + lk]);
+                        fxx[cb ^ 1][kk] = frag_row(&sm.X[(16 * (tt + 1) + lr) * kS64 + 32 * kk + lk]);
+                    }
+                }
                 f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    ac = mfma(fH[kk], frag_row(&sm.dY[(16 * tt + lr) * kS64 + 32 * kk + lk]), ac);
-                    ab = mfma(fdH[kk], frag_row(&sm.X[(16 * tt + lr) * kS64 + 32 * kk + lk]), ab);
+                    ac = mfma(fH[kk], fy[cb][kk], ac);
+                    ab = mfma(fdH[kk], fxx[cb][kk], ab);
                 }
-                const float2 li = ld[base + i];
-                const float ei = __expf(li.x - lam_blk0);
-                const float wdt = __expf(lam_e - li.x) * li.y;
-                // the token's scale (ei, wdt) is fused into the accumulate and applied to
-                // the dot products once after their reduction
-                float o = 0.f, f = 0.f;
+                const float ei = ei_t[tt], wdt = wdt_t[tt];
+                // the token's scale ei is fused into the accumulate and applied to the dot
+                // product once after its reduction
+                float o = 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     o = fmaf(cC[tt][v], ac[v], o);
-                    f = fmaf(cB[tt][v], ab[v], f);
                     dCa[tt][v] = fmaf(ac[v], ei, dCa[tt][v]);
                     dBa[tt][v] = fmaf(ab[v], wdt, dBa[tt][v]);
                 }
                 o = rows4_sum(o) * ei;
-                f = rows4_sum(f) * wdt;
-                if (lane < 16) sm.offin[i][wave] = make_float2(o, f);
+                if (lane < 16) sm.offin[i][wave] = o;
             }
         }
         // dx leaves after Phases III/IV rather than in the middle of Phase II (1.636 ->
