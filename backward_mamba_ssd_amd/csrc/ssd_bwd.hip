@@ -209,16 +209,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
 // ===========================================================================
 // 2. per (batch, group, chunk, block): everything else
 // ===========================================================================
-// All LDS tiles keep the natural global row layout ([tok][p] or [tok][n]);
-// operands that contract over a tile's row index are read with frag_tr.
+// All LDS tiles keep the natural global row layout ([tok][p] or [tok][n]), unpadded, with
+// the 16-byte pieces of each row permuted (SwzLane); operands that contract over a tile's
+// row index are read with the transposing read.
 //
 // Per head the block-entry state and block-exit gradient are single products
 // over the chunk's other blocks, with chunk-local cumulative Lc:
 //   H_k^T  = exp(Lc[s]) H_c^T + sum_{tok < 64k} B_tok (x) [exp(Lc[s]-Lc[tok]) dt_tok x_tok]
 //   dH^T   = exp(Lc[end]-Lc[e]) dH_{c+1}^T + sum_{tok > e} C_tok (x) [exp(Lc[tok]-Lc[e]) dy_tok]
 // (s = last token before block k, e = last token of block k; every exponent <= 0).
-constexpr int kT64 = kLs * kS64;    // a [64][72] tile
-constexpr int kT128 = kLs * kS128;  // a [64][136] tile
+constexpr int kT64 = kLs * 64;    // a [64][64] tile (swizzled)
+constexpr int kT128 = kLs * 128;  // a [64][128] tile (swizzled)
 constexpr int kMaxBlk = 4;          // blocks per chunk (chunk <= 256)
 
 constexpr int kBlkThreads = 512;  // 8 waves: w = 4*wh + wq
@@ -269,16 +270,18 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     // Lane-derived indices are re-formed at the top of every head iteration from a
     // value the compiler cannot see through, so the LDS addresses built from them are
     // computed next to their uses instead of occupying registers across the loop.
-    int tid, lane, lr, lk, lq, pr_tok, pr_col;
+    int tid, lane, lr, lq, pr_tok;
+    uint32_t stg;  // this thread's piece of the per-head row staging
+    SwzLane sl;
     auto refresh_lane = [&]() {
         tid = static_cast<int>(threadIdx.x);
         asm volatile("" : "+v"(tid));
         lane = tid & 63;
         lr = lane & 15;
-        lk = (lane >> 4) * 8;
         lq = (lane >> 4) * 4;
         pr_tok = tid >> 3;
-        pr_col = (tid & 7) * 8;
+        stg = swz_stage64(pr_tok, tid & 7);
+        sl = swz_lane(lane);
     };
     refresh_lane();
     // A and D of the group's heads, lane l holding head h0 + l; a head's value is read
@@ -301,8 +304,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
     bf16_t *dx = static_cast<bf16_t *>(a.dx);
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    // row staging: [tok][p] tiles: one 16-byte chunk per thread; [tok][n] tiles: two
+    // row staging: [tok][p] tiles: one 16-byte piece per thread; [tok][n] tiles: two
     const int nr_tok = tid >> 4, nr_col = (tid & 15) * 8;
+    const uint32_t nr_stg = swz_stage128(nr_tok, tid & 15);
 
     auto load_rows_n = [&](const bf16_t *src, int64_t t0, bf16_t *dst) {
         u16x8 r[2];
@@ -312,7 +316,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             r[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(src + ((b * T + t) * a.G + g) * kN + nr_col) : z8;
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<u16x8 *>(&dst[(nr_tok + 32 * i) * kS128 + nr_col]) = r[i];
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(dst) + i * 8192 + nr_stg) = r[i];
     };
     // head-independent tiles: block k B and C rows, B rows of earlier blocks, C rows of later ones
     load_rows_n(Bm, tk, sm.B);
@@ -337,7 +341,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const rsrc_t rdx = make_rsrc(dx + row0 * kP, nvalid * tokb);
     const rsrc_t rdt = make_rsrc(a.dt + row0, nvalid * a.H * 4u);
     const rsrc_t rddt = make_rsrc(a.ddt + row0, nvalid * a.H * 4u);
-    const uint32_t row_off = static_cast<uint32_t>(pr_tok) * tokb + pr_col * 2;  // this thread's row segment
+    const uint32_t row_off = static_cast<uint32_t>(pr_tok) * tokb + (tid & 7) * 16;  // this thread's row segment
     auto prefetch = [&](int h) {
         const uint32_t o = row_off + static_cast<uint32_t>(h) * (kP * 2);
 #pragma unroll
@@ -418,15 +422,14 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         if (jt <= wq) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                Gt[q] = mma16(&sm.C[(16 * wq + lr) * kS128 + 32 * kk + lk],
-                              &sm.B[(16 * jt + lr) * kS128 + 32 * kk + lk], Gt[q]);
+                Gt[q] = mfma(lds_frag(sm.C, swz_row128(sl, wq, kk)), lds_frag(sm.B, swz_row128(sl, jt, kk)), Gt[q]);
         }
     }
     // C of block k at this lane's (token, n) positions of the Phase III tiles
     float cC[4][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        const u16x4 c4 = *reinterpret_cast<const u16x4 *>(&sm.C[(16 * tt + lr) * kS128 + 16 * wave + lq]);
+        const u16x4 c4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.C) + swz_pc128(sl, tt, wave));
 #pragma unroll
         for (int v = 0; v < 4; ++v) cC[tt][v] = bf16_to_f32(c4[v]);
     }
@@ -514,8 +517,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             if (kb >= nbc) break;
             const int tl = 64 * kb + pr_tok;  // chunk-local token
             if (kb == k) {
-                *reinterpret_cast<u16x8 *>(&sm.X[pr_tok * kS64 + pr_col]) = xr[kb];
-                *reinterpret_cast<u16x8 *>(&sm.dY[pr_tok * kS64 + pr_col]) = yk;
+                *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(sm.X) + stg) = xr[kb];
+                *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(sm.dY) + stg) = yk;
                 continue;
             }
             const float cf = sm.fac[par][tl];
@@ -526,7 +529,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                              pack2_bf16(bf16_to_f32(v[2]) * cf, bf16_to_f32(v[3]) * cf),
                              pack2_bf16(bf16_to_f32(v[4]) * cf, bf16_to_f32(v[5]) * cf),
                              pack2_bf16(bf16_to_f32(v[6]) * cf, bf16_to_f32(v[7]) * cf)};
-            *reinterpret_cast<u32x4 *>(&sm.R[slot * kT64 + pr_tok * kS64 + pr_col]) = w;
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(sm.R + slot * kT64) + stg) = w;
         }
         __syncthreads();
         prefetch(hn);  // registers are free once staged
@@ -538,7 +541,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             float lam_i[4], rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
             bf16x8 fY[2];  // dY rows of the wave's i-tile, shared by both j-tiles
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) fY[kk] = frag_row(&sm.dY[(16 * wq + lr) * kS64 + 32 * kk + lk]);
+            for (int kk = 0; kk < 2; ++kk) fY[kk] = lds_frag(sm.dY, swz_row64(sl, wq, kk));
 #pragma unroll
             for (int v = 0; v < 4; ++v) lam_i[v] = ld[base + 16 * wq + lq + v].x;
 #pragma unroll
@@ -548,7 +551,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 f32x4 dW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    dW = mfma(fY[kk], frag_row(&sm.X[(16 * jt + lr) * kS64 + 32 * kk + lk]), dW);
+                    dW = mfma(fY[kk], lds_frag(sm.X, swz_row64(sl, jt, kk)), dW);
                 if (jt == wq) {  // diagonal tile: dW[i][i] = dy_i . x_i feeds dD
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
@@ -571,7 +574,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     colacc += r;
                     qv[v] = Gt[q][v] * m;
                 }
-                *reinterpret_cast<u16x4 *>(&sm.QT[j * kS64 + 16 * wq + lq]) = pack4(qv[0], qv[1], qv[2], qv[3]);
+                *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, jt, wq)) = pack4(qv[0], qv[1], qv[2], qv[3]);
                 colacc = rows4_sum(colacc);
                 if (lane < 16) sm.col[par][j][wq] = colacc;
             }
@@ -600,8 +603,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     bf16x8 fa[2], fb[2];
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        fa[t] = frag_tr(bc, kS128, 16 * (2 * wq + t), 32 * kk, lane);
-                        fb[t] = frag_tr(xs, kS64, 16 * (2 * wh + t), 32 * kk, lane);
+                        fa[t] = frag_tr128(bc, sl, 2 * wq + t, kk);
+                        fb[t] = frag_tr64(xs, sl, 2 * wh + t, kk);
                     }
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acc[q] = mfma(fa[q >> 1], fb[q & 1], acc[q]);
@@ -613,9 +616,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 chain(sm.chainBC + kb * kT128, sm.R + kb * kT64, aH);
             }
 #pragma unroll
-            for (int sl = 0; sl < kMaxBlk - 1; ++sl) {  // dH_{k+1} = e dH_c + sum over later blocks (slot sl = block sl+1)
-                if (sl < k || sl + 1 >= nbc) continue;
-                chain(sm.chainBC + sl * kT128, sm.R + sl * kT64, adH);
+            for (int sb = 0; sb < kMaxBlk - 1; ++sb) {  // dH_{k+1} = e dH_c + sum over later blocks (slot sb = block sb+1)
+                if (sb < k || sb + 1 >= nbc) continue;
+                chain(sm.chainBC + sb * kT128, sm.R + sb * kT64, adH);
             }
         }
         __syncthreads();
@@ -627,7 +630,6 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             float dotp = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = 16 * (2 * wq + (q >> 1)) + lq, p = 16 * (2 * wh + (q & 1)) + lr;
                 f32x4 hv, gv;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -635,8 +637,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                     gv[v] = fmaf(ee, bf16_to_f32(dHr[q >> 1][4 * (q & 1) + v]), adH[q][v]);
                     dotp = fmaf(hv[v], gv[v], dotp);
                 }
-                *reinterpret_cast<u16x4 *>(&Hb[p * kS128 + n]) = pack4(hv[0], hv[1], hv[2], hv[3]);
-                *reinterpret_cast<u16x4 *>(&dHb[p * kS128 + n]) = pack4(gv[0], gv[1], gv[2], gv[3]);
+                const uint32_t o = swz_pc128(sl, 2 * wh + (q & 1), 2 * wq + (q >> 1));  // [p][n]
+                *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(Hb) + o) = pack4(hv[0], hv[1], hv[2], hv[3]);
+                *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(dHb) + o) = pack4(gv[0], gv[1], gv[2], gv[3]);
             }
             dotp = wave_total(dotp);
             if (lane == 0) sm.dot[wave] = dotp;
@@ -672,24 +675,25 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 // Q[i][j] = 0 for i < j, so the kk block below the diagonal adds zeros
-                const bf16x8 fa = frag_tr(sm.dY, kS64, 16 * wq, 32 * kk, lane);
+                const bf16x8 fa = frag_tr64(sm.dY, sl, wq, kk);
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    acc[q] = mfma(fa, frag_row(&sm.QT[(16 * (2 * wh + q) + lr) * kS64 + 32 * kk + lk]), acc[q]);
+                    acc[q] = mfma(fa, lds_frag(sm.QT, swz_row64(sl, 2 * wh + q, kk)), acc[q]);
             }
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 fa = frag_row(&dHb[(16 * wq + lr) * kS128 + 32 * kk + lk]);
+                const bf16x8 fa = lds_frag(dHb, swz_row128(sl, wq, kk));
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    acc4[q] = mfma(fa, frag_row(&sm.B[(16 * (2 * wh + q) + lr) * kS128 + 32 * kk + lk]), acc4[q]);
+                    acc4[q] = mfma(fa, lds_frag(sm.B, swz_row128(sl, 2 * wh + q, kk)), acc4[q]);
             }
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int j = 16 * (2 * wh + q) + lr;
                 const float wj = sm.w[par][j], dt_j = ld[base + j].y;
-                const u16x4 x4 = *reinterpret_cast<const u16x4 *>(&sm.X[j * kS64 + 16 * wq + lq]);
-                const u16x4 y4 = *reinterpret_cast<const u16x4 *>(&sm.dY[j * kS64 + 16 * wq + lq]);
+                const uint32_t o = swz_pc64(sl, 2 * wh + q, wq);
+                const u16x4 x4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.X) + o);
+                const u16x4 y4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.dY) + o);
                 // acc4[j][p] = (dH B_j)[p]: with x it also gives the exit-gradient term
                 // f_j = w_j dt_j x_j.(dH B_j) of dLam (this wave's p-tile)
                 float ddp = 0.f, xb = 0.f, dxv[4];
@@ -717,14 +721,14 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             bf16x8 fH[2], fdH[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                fH[kk] = frag_tr(Hb, kS128, 16 * wave, 32 * kk, lane);
-                fdH[kk] = frag_tr(dHb, kS128, 16 * wave, 32 * kk, lane);
+                fH[kk] = frag_tr128(Hb, sl, wave, kk);
+                fdH[kk] = frag_tr128(dHb, sl, wave, kk);
             }
             bf16x8 fy[2][2], fxx[2][2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                fy[0][kk] = frag_row(&sm.dY[lr * kS64 + 32 * kk + lk]);
-                fxx[0][kk] = frag_row(&sm.X[lr * kS64 + 32 * kk + lk]);
+                fy[0][kk] = lds_frag(sm.dY, swz_row64(sl, 0, kk));
+                fxx[0][kk] = lds_frag(sm.X, swz_row64(sl, 0, kk));
             }
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
@@ -733,8 +737,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 if (tt + 1 < 4) {
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
-                        fy[cb ^ 1][kk] = frag_row(&sm.dY[(16 * (tt + 1) + lr) * kS64 + 32 * kk + lk]);
-                        fxx[cb ^ 1][kk] = frag_row(&sm.X[(16 * (tt + 1) + lr) * kS64 + 32 * kk + lk]);
+                        fy[cb ^ 1][kk] = lds_frag(sm.dY, swz_row64(sl, tt + 1, kk));
+                        fxx[cb ^ 1][kk] = lds_frag(sm.X, swz_row64(sl, tt + 1, kk));
                     }
                 }
                 f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
@@ -771,8 +775,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int j = 16 * (2 * wh + q) + lr;
-        *reinterpret_cast<u16x4 *>(&sm.QT[j * kS64 + 16 * wq + lq]) = pack4(Ks[q][0], Ks[q][1], Ks[q][2], Ks[q][3]);
+        *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, 2 * wh + q, wq)) =
+            pack4(Ks[q][0], Ks[q][1], Ks[q][2], Ks[q][3]);
     }
     __syncthreads();
     {
@@ -781,10 +785,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                dCa[tt] = mfma(frag_tr(sm.B, kS128, 16 * wave, 32 * kk, lane),
-                               frag_tr(KT, kS64, 16 * tt, 32 * kk, lane), dCa[tt]);
-                dBa[tt] = mfma(frag_tr(sm.C, kS128, 16 * wave, 32 * kk, lane),
-                               frag_row(&KT[(16 * tt + lr) * kS64 + 32 * kk + lk]), dBa[tt]);
+                dCa[tt] = mfma(frag_tr128(sm.B, sl, wave, kk), frag_tr64(KT, sl, tt, kk), dCa[tt]);
+                dBa[tt] = mfma(frag_tr128(sm.C, sl, wave, kk), lds_frag(KT, swz_row64(sl, tt, kk)), dBa[tt]);
             }
             const int t = 16 * tt + lr;
             if (tk + t < T) {
