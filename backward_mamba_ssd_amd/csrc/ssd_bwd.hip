@@ -222,7 +222,7 @@ constexpr int kT64 = kLs * 64;    // a [64][64] tile (swizzled)
 constexpr int kT128 = kLs * 128;  // a [64][128] tile (swizzled)
 constexpr int kMaxBlk = 4;          // blocks per chunk (chunk <= 256)
 
-constexpr int kBlkThreads = 512;  // 8 waves: w = 4*wh + wq
+constexpr int kBlkThreads = 1024;  // 16 waves
 
 struct __align__(16) BlkSmem {
     bf16_t B[kT128];                    // block k rows of B [j][n]
@@ -235,10 +235,10 @@ struct __align__(16) BlkSmem {
     // row, col, dd_sum are written before the S2 barrier and read by the combine of the
     // previous head during S2, so they are double-buffered by head parity
     // (token-major, so the combine reads each token's partials with a few wide loads)
-    float row[2][2][kLs], col[2][kLs][4], dd[kLs][4];  // row: [wh][token], 4 tokens per write
-    float fp[kLs][4];      // f_j = w_j dt_j x_j.(dH B_j) partials per token and p-tile wave
-    float offin[kLs][8];   // dy_i.(H C_i) exp(Lam_i) partials per token and n-tile wave
-    float dot[8], dd_sum[2][8];
+    float row[2][4][kLs], col[2][kLs][4], dd[kLs][4];  // row: [j-tile][token], col: [token][i-tile]
+    float fp[kLs][4];      // f_j = w_j dt_j x_j.(dH B_j) partials per token and p-tile
+    float offin[kLs][8];   // dy_i.(H C_i) exp(Lam_i) partials per token and n-tile
+    float dot[16], dd_sum[2][16];
     // Per-token decay factors of a head, by head parity, computed once per head one phase
     // ahead of their use (instead of an exponential per thread per use): fac[t] for a
     // chunk token t outside block k is the factor that scales its row for the state
@@ -248,6 +248,12 @@ struct __align__(16) BlkSmem {
 };
 static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the state tiles");
 
+// Sixteen waves, four per SIMD, so that each SIMD has other waves to issue from while
+// one waits on LDS, an MFMA result or a barrier.  Wave w's tiles (every tile 16 x 16):
+//   Gram / K / Phase I, [i][j]:   i-tile wq = w % 4, j-tile wj = w / 4
+//   state products, [n][p]:       n-tile wn = w % 8, p-tiles 2 wm, 2 wm + 1 (wm = w / 8)
+//   Phase II, [p][j]:             p-tile wq, j-tile wj
+//   Phase III/IV and K, [n][tok]: n-tile wn, token tiles 2 wm, 2 wm + 1
 __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a) {
     __shared__ BlkSmem sm;
     const int nb = static_cast<int>(a.L / kLs);
@@ -266,11 +272,11 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const int hpg = a.H / a.G;
     const int kS_ = 64 * k - 1, kE_ = 64 * k + kLs - 1, kEnd_ = 64 * nbc - 1, base_ = 64 * k;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int wq = wave & 3, wh = wave >> 2;
+    const int wq = wave & 3, wj = wave >> 2, wn = wave & 7, wm = wave >> 3;
     // Lane-derived indices are re-formed at the top of every head iteration from a
     // value the compiler cannot see through, so the LDS addresses built from them are
     // computed next to their uses instead of occupying registers across the loop.
-    int tid, lane, lr, lq, pr_tok;
+    int tid, lane, lr, lq, pid;
     uint32_t stg;  // this thread's piece of the per-head row staging
     SwzLane sl;
     auto refresh_lane = [&]() {
@@ -279,8 +285,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         lane = tid & 63;
         lr = lane & 15;
         lq = (lane >> 4) * 4;
-        pr_tok = tid >> 3;
-        stg = swz_stage64(pr_tok, tid & 7);
+        pid = tid & 511;  // staging piece: row pid / 8, piece pid % 8 (two threads per piece)
+        stg = swz_stage64(pid >> 3, pid & 7);
         sl = swz_lane(lane);
     };
     refresh_lane();
@@ -304,19 +310,14 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
     bf16_t *dx = static_cast<bf16_t *>(a.dx);
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    // row staging: [tok][p] tiles: one 16-byte piece per thread; [tok][n] tiles: two
+    // [tok][n] tiles: one 16-byte piece per thread
     const int nr_tok = tid >> 4, nr_col = (tid & 15) * 8;
     const uint32_t nr_stg = swz_stage128(nr_tok, tid & 15);
 
     auto load_rows_n = [&](const bf16_t *src, int64_t t0, bf16_t *dst) {
-        u16x8 r[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t t = t0 + nr_tok + 32 * i;
-            r[i] = (t < T) ? *reinterpret_cast<const u16x8 *>(src + ((b * T + t) * a.G + g) * kN + nr_col) : z8;
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(dst) + i * 8192 + nr_stg) = r[i];
+        const int64_t t = t0 + nr_tok;
+        const u16x8 r = (t < T) ? *reinterpret_cast<const u16x8 *>(src + ((b * T + t) * a.G + g) * kN + nr_col) : z8;
+        *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(dst) + nr_stg) = r;
     };
     // head-independent tiles: block k B and C rows, B rows of earlier blocks, C rows of later ones
     load_rows_n(Bm, tk, sm.B);
@@ -327,9 +328,10 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         load_rows_n(kb < k ? Bm : Cm, cstart + static_cast<int64_t>(kb) * kLs, sm.chainBC + slot * kT128);
     }
 
-    // per-head inputs held in registers one head ahead
-    u16x8 xr[kMaxBlk];  // x rows of blocks <= k, dy rows of blocks > k
-    u16x8 yk;           // dy rows of block k
+    // per-head inputs held in registers one head ahead: waves 0..7 stage blocks 0, 1 and
+    // the dy rows of block k, waves 8..15 blocks 2, 3
+    u16x8 xr[2];  // x rows of blocks 2 wm + i <= k, dy rows of later blocks
+    u16x8 yk;     // dy rows of block k (wm = 0)
     float dtr[4];
     // Per-head rows of x, dy, dx and dt, ddt through buffer descriptors over this
     // chunk: offsets past the chunk's valid tokens read zero / drop the write.
@@ -341,13 +343,15 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const rsrc_t rdx = make_rsrc(dx + row0 * kP, nvalid * tokb);
     const rsrc_t rdt = make_rsrc(a.dt + row0, nvalid * a.H * 4u);
     const rsrc_t rddt = make_rsrc(a.ddt + row0, nvalid * a.H * 4u);
-    const uint32_t row_off = static_cast<uint32_t>(pr_tok) * tokb + (tid & 7) * 16;  // this thread's row segment
+    const uint32_t row_off = static_cast<uint32_t>(pid >> 3) * tokb + (pid & 7) * 16;  // this thread's row segment
     auto prefetch = [&](int h) {
         const uint32_t o = row_off + static_cast<uint32_t>(h) * (kP * 2);
 #pragma unroll
-        for (int kb = 0; kb < kMaxBlk; ++kb)  // blocks past the chunk read zero
-            xr[kb] = buf_ld_16b(kb <= k ? rx : ry, o + kb * kLs * tokb);
-        yk = buf_ld_16b(ry, o + k * kLs * tokb);
+        for (int i = 0; i < 2; ++i) {  // blocks past the chunk read zero
+            const int kb = 2 * wm + i;
+            xr[i] = buf_ld_16b(kb <= k ? rx : ry, o + kb * kLs * tokb);
+        }
+        if (wm == 0) yk = buf_ld_16b(ry, o + k * kLs * tokb);
     };
     // dt of head h, four tokens per lane (wave 0 only; consumed by the scan)
     auto prefetch_dt = [&](int h) {
@@ -387,24 +391,22 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             }
         }
     };
-    // states in accumulators, [n][p], 2 x 2 tiles per wave: q -> n-tile 2wq + q/2,
-    // p-tile 2wh + q%2
     // raw chunk-boundary state and chunk-exit gradient of the next head, loaded a full
-    // head ahead of their use in S3
-    f32x4 Hs[4];
-    u16x8 dHr[2];  // chunk-exit gradient tile pairs (n-tile 2wq + j, p-tiles 2wh, 2wh + 1), bf16
+    // head ahead of their use in S3; the state tiles in accumulator layout, [n][p]:
+    // q -> n-tile wn, p-tile 2 wm + q
+    f32x4 Hs[2];
+    u16x8 dHr;  // chunk-exit gradient tile pair (n-tile wn, p-tiles 2wm, 2wm + 1), bf16
     auto load_states = [&](int h) {
         const int64_t bh = static_cast<int64_t>(b) * a.H + h;
         const float *hc = a.chunk_states + (bh * a.nchunks + c) * PN;
         const bf16_t *dc = a.dstates + (bh * a.nchunks + c) * PN;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = 16 * (2 * wq + (q >> 1)) + lq, p = 16 * (2 * wh + (q & 1)) + lr;
+        for (int q = 0; q < 2; ++q) {
+            const int n = 16 * wn + lq, p = 16 * (2 * wm + q) + lr;
             const float4 u = *reinterpret_cast<const float4 *>(hc + p * kN + n);
             Hs[q] = f32x4{u.x, u.y, u.z, u.w};
         }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dHr[j] = *reinterpret_cast<const u16x8 *>(dc + dstate_pair(2 * wq + j, wh, lane));
+        dHr = *reinterpret_cast<const u16x8 *>(dc + dstate_pair(wn, wm, lane));
     };
 
     prefetch(h0);
@@ -413,33 +415,26 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     if (wave == 0) scan(h0, 0);
     __syncthreads();
     factors(0);
-    // Gram tiles of block k, [i][j]: i-tile wq, j-tiles 2wh, 2wh+1
-    f32x4 Gt[2];
+    // Gram tile of block k, [i][j]: i-tile wq, j-tile wj
+    f32x4 Gt = {0.f, 0.f, 0.f, 0.f};
+    if (wj <= wq) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int jt = 2 * wh + q;
-        Gt[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (jt <= wq) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                Gt[q] = mfma(lds_frag(sm.C, swz_row128(sl, wq, kk)), lds_frag(sm.B, swz_row128(sl, jt, kk)), Gt[q]);
-        }
+        for (int kk = 0; kk < 4; ++kk)
+            Gt = mfma(lds_frag(sm.C, swz_row128(sl, wq, kk)), lds_frag(sm.B, swz_row128(sl, wj, kk)), Gt);
     }
     // C of block k at this lane's (token, n) positions of the Phase III tiles
-    float cC[4][4];
+    float cC[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const u16x4 c4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.C) + swz_pc128(sl, tt, wave));
+    for (int t = 0; t < 2; ++t) {
+        const u16x4 c4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.C) + swz_pc128(sl, 2 * wm + t, wn));
 #pragma unroll
-        for (int v = 0; v < 4; ++v) cC[tt][v] = bf16_to_f32(c4[v]);
+        for (int v = 0; v < 4; ++v) cC[t][v] = bf16_to_f32(c4[v]);
     }
-    f32x4 Ks[2], dCa[4], dBa[4];  // Ks like Gt; dCa/dBa [n][tok]: n-tile = wave, tok-tiles 0..3
+    f32x4 Ks = {0.f, 0.f, 0.f, 0.f}, dCa[2], dBa[2];  // Ks like Gt; dCa/dBa [n][tok]: n-tile wn, tok-tiles 2wm + t
 #pragma unroll
-    for (int q = 0; q < 2; ++q) Ks[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        dCa[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dBa[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 2; ++t) {
+        dCa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dBa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int kS = kS_;      // chunk-local index of the token before block k
     const int kE = kE_;      // last token of block k
@@ -456,13 +451,12 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const float lb0 = kS >= 0 ? ldc[kS].x : 0.f;
         const float le = ldc[kE].x;
         typedef float f32x4v __attribute__((ext_vector_type(4)));
-        const float2 rw = make_float2(sm.row[pc][0][j], sm.row[pc][1][j]);
         const f32x4v cl = *reinterpret_cast<const f32x4v *>(sm.col[pc][j]);
         const f32x4v dv = *reinterpret_cast<const f32x4v *>(sm.dd[j]);
         const f32x4v fv = *reinterpret_cast<const f32x4v *>(sm.fp[j]);
         const f32x4v o0 = *reinterpret_cast<const f32x4v *>(&sm.offin[j][0]);
         const f32x4v o1 = *reinterpret_cast<const f32x4v *>(&sm.offin[j][4]);
-        float dl = rw.x + rw.y;
+        float dl = (sm.row[pc][0][j] + sm.row[pc][1][j]) + (sm.row[pc][2][j] + sm.row[pc][3][j]);
         float ddd = 0.f, fs = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -477,7 +471,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         if (j == kLs - 1) {
             float dotv = 0.f;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) dotv += sm.dot[w];
+            for (int w = 0; w < 16; ++w) dotv += sm.dot[w];
             dl += __expf(le - lb0) * dotv;
         }
         // The exit-gradient term f_i = w_i dt_i x_i.(dH B_i) enters dLam_i as -f_i and the
@@ -493,7 +487,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         if (lane == 0) {
             float ds = 0.f;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) ds += sm.dd_sum[pc][w];
+            for (int w = 0; w < 16; ++w) ds += sm.dd_sum[pc][w];
             const int64_t pi = ((static_cast<int64_t>(b) * a.H + hc) * a.nchunks + c) * nb + k;
             a.pA[pi] = static_cast<double>(pa);
             a.pD[pi] = static_cast<double>(ds);
@@ -503,8 +497,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     for (int hh = 0; hh < hpg; ++hh) {
         refresh_lane();
         const int h = h0 + hh, par = hh & 1;
-        const int64_t bh = static_cast<int64_t>(b) * a.H + h;
-        const float Ah = head_A(hh), Dh = head_D(hh);
+        const float Dh = head_D(hh);
         const float2 *ld = sm.ld[par];  // (Lam, dt) of this head's chunk
         // The next head's loads are issued on every iteration (the last one re-reads its own
         // head), so each iteration issues the same memory operations and the waits on them
@@ -512,102 +505,94 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const int hn = (hh + 1 < hpg) ? h + 1 : h;
         prefetch_dt(hn);  // used by the next head's scan in S3
         // ---- S1: stage this head's rows (scaled for the state products) ----
-#pragma unroll
-        for (int kb = 0; kb < kMaxBlk; ++kb) {
-            if (kb >= nbc) break;
-            const int tl = 64 * kb + pr_tok;  // chunk-local token
-            if (kb == k) {
-                *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(sm.X) + stg) = xr[kb];
-                *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(sm.dY) + stg) = yk;
-                continue;
-            }
-            const float cf = sm.fac[par][tl];
-            const int slot = kb < k ? kb : kb - 1;
-            const u16x8 v = xr[kb];
+        {
             typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-            const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * cf, bf16_to_f32(v[1]) * cf),
-                             pack2_bf16(bf16_to_f32(v[2]) * cf, bf16_to_f32(v[3]) * cf),
-                             pack2_bf16(bf16_to_f32(v[4]) * cf, bf16_to_f32(v[5]) * cf),
-                             pack2_bf16(bf16_to_f32(v[6]) * cf, bf16_to_f32(v[7]) * cf)};
-            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(sm.R + slot * kT64) + stg) = w;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int kb = 2 * wm + i;
+                if (kb >= nbc) break;
+                if (kb == k) {
+                    *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(sm.X) + stg) = xr[i];
+                    continue;
+                }
+                const float cf = sm.fac[par][64 * kb + (pid >> 3)];
+                const int slot = kb < k ? kb : kb - 1;
+                const u16x8 v = xr[i];
+                const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * cf, bf16_to_f32(v[1]) * cf),
+                                 pack2_bf16(bf16_to_f32(v[2]) * cf, bf16_to_f32(v[3]) * cf),
+                                 pack2_bf16(bf16_to_f32(v[4]) * cf, bf16_to_f32(v[5]) * cf),
+                                 pack2_bf16(bf16_to_f32(v[6]) * cf, bf16_to_f32(v[7]) * cf)};
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(sm.R + slot * kT64) + stg) = w;
+            }
+            if (wm == 0) *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(sm.dY) + stg) = yk;
         }
         __syncthreads();
         prefetch(hn);  // registers are free once staged
-        // ---- S2: Phase I of block k, then the state products over the other blocks
-        //      (in this order 1.628 -> 1.616 ms; the two are independent) ----
+        // ---- S2: Phase I of block k, then the state products over the other blocks ----
         if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
-        // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile wq, j-tiles 2wh, 2wh+1)
-        {
-            float lam_i[4], rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
-            bf16x8 fY[2];  // dY rows of the wave's i-tile, shared by both j-tiles
+        // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile wq, j-tile wj)
+        if (wj > wq) {
+            // above the diagonal every entry is zero: Q^T's tile and the partial sums
+            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, wj, wq)) = u16x4{0, 0, 0, 0};
+            if (lane < 16) sm.col[par][16 * wj + lr][wq] = 0.f;
+            typedef float f32x4v __attribute__((ext_vector_type(4)));
+            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][wj][16 * wq + lq]) = f32x4v{0.f, 0.f, 0.f, 0.f};
+            if (lane == 0) sm.dd_sum[par][wave] = 0.f;
+        } else {
+            float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
+            f32x4 dW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) fY[kk] = lds_frag(sm.dY, swz_row64(sl, wq, kk));
+            for (int kk = 0; kk < 2; ++kk)
+                dW = mfma(lds_frag(sm.dY, swz_row64(sl, wq, kk)), lds_frag(sm.X, swz_row64(sl, wj, kk)), dW);
+            if (wj == wq) {  // diagonal tile: dW[i][i] = dy_i . x_i feeds dD
 #pragma unroll
-            for (int v = 0; v < 4; ++v) lam_i[v] = ld[base + 16 * wq + lq + v].x;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int jt = 2 * wh + q, j = 16 * jt + lr;
-                // tiles above the diagonal are computed too: the mask below zeroes them
-                f32x4 dW = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    dW = mfma(fY[kk], lds_frag(sm.X, swz_row64(sl, jt, kk)), dW);
-                if (jt == wq) {  // diagonal tile: dW[i][i] = dy_i . x_i feeds dD
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (lq + v == lr) diag += dW[v];
-                }
-                const float2 lj = ld[base + j];
-                const float lam_j = lj.x, dt_j = lj.y;
-                float qv[4], colacc = 0.f;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int i = 16 * wq + lq + v;
-                    const float m = (j <= i) ? __expf(lam_i[v] - lam_j) : 0.f;
-                    const float kv = dW[v] * m * dt_j;
-                    Ks[q][v] += kv;
-                    // R[i][i] enters row sum i and column sum i alike and cancels in
-                    // dLam_i, so it is left out of both: with strong decay it is the only
-                    // O(1) entry, and subtracting it would bury the small terms in rounding
-                    const float r = (j < i) ? kv * Gt[q][v] : 0.f;
-                    rowacc[v] += r;
-                    colacc += r;
-                    qv[v] = Gt[q][v] * m;
-                }
-                *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, jt, wq)) = pack4(qv[0], qv[1], qv[2], qv[3]);
-                colacc = rows4_sum(colacc);
-                if (lane < 16) sm.col[par][j][wq] = colacc;
+                for (int v = 0; v < 4; ++v)
+                    if (lq + v == lr) diag += dW[v];
             }
-            {
-                typedef float f32x4v __attribute__((ext_vector_type(4)));
-                f32x4v r;
+            const int j = 16 * wj + lr;
+            const float2 lj = ld[base + j];
+            const float lam_j = lj.x, dt_j = lj.y;
+            float qv[4], colacc = 0.f;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) r[v] = row16_sum(rowacc[v]);
-                if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][wh][16 * wq + lq]) = r;
+            for (int v = 0; v < 4; ++v) {
+                const int i = 16 * wq + lq + v;
+                const float m = (j <= i) ? __expf(ld[base + i].x - lam_j) : 0.f;
+                const float kv = dW[v] * m * dt_j;
+                Ks[v] += kv;
+                // R[i][i] enters row sum i and column sum i alike and cancels in
+                // dLam_i, so it is left out of both: with strong decay it is the only
+                // O(1) entry, and subtracting it would bury the small terms in rounding
+                const float r = (j < i) ? kv * Gt[v] : 0.f;
+                rowacc[v] += r;
+                colacc += r;
+                qv[v] = Gt[v] * m;
             }
+            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, wj, wq)) = pack4(qv[0], qv[1], qv[2], qv[3]);
+            colacc = rows4_sum(colacc);
+            if (lane < 16) sm.col[par][j][wq] = colacc;
+            typedef float f32x4v __attribute__((ext_vector_type(4)));
+            f32x4v r;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) r[v] = row16_sum(rowacc[v]);
+            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][wj][16 * wq + lq]) = r;
             diag = wave_total(diag);
             if (lane == 0) sm.dd_sum[par][wave] = diag;
         }
-        // Each A fragment (16 state rows n of one block's B or C) is read once and used
-        // for all four p-tiles.
         // The sums start from zero; the decayed chunk-boundary terms are added in S3.
-        f32x4 aH[4], adH[4];
+        // Per 32-token step the wave reads one n fragment and two p fragments.
+        f32x4 aH[2], adH[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) aH[q] = adH[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // 2 x 2 register blocking: per 32-token step the wave reads two n fragments and
-        // two p fragments for four products.
+        for (int q = 0; q < 2; ++q) aH[q] = adH[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
             auto chain = [&](const bf16_t *bc, const bf16_t *xs, f32x4 *acc) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8 fa[2], fb[2];
+                    const bf16x8 fa = frag_tr128(bc, sl, wn, kk);
+                    bf16x8 fb[2];
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        fa[t] = frag_tr128(bc, sl, 2 * wq + t, kk);
-                        fb[t] = frag_tr64(xs, sl, 2 * wh + t, kk);
-                    }
+                    for (int t = 0; t < 2; ++t) fb[t] = frag_tr64(xs, sl, 2 * wm + t, kk);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[q] = mfma(fa[q >> 1], fb[q & 1], acc[q]);
+                    for (int t = 0; t < 2; ++t) acc[t] = mfma(fa, fb[t], acc[t]);
                 }
             };
 #pragma unroll
@@ -629,15 +614,15 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             const float ee = sm.ee[par];  // block k end -> chunk end
             float dotp = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2; ++q) {
                 f32x4 hv, gv;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     hv[v] = fmaf(es, Hs[q][v], aH[q][v]);
-                    gv[v] = fmaf(ee, bf16_to_f32(dHr[q >> 1][4 * (q & 1) + v]), adH[q][v]);
+                    gv[v] = fmaf(ee, bf16_to_f32(dHr[4 * q + v]), adH[q][v]);
                     dotp = fmaf(hv[v], gv[v], dotp);
                 }
-                const uint32_t o = swz_pc128(sl, 2 * wh + (q & 1), 2 * wq + (q >> 1));  // [p][n]
+                const uint32_t o = swz_pc128(sl, 2 * wm + q, wn);  // [p][n]
                 *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(Hb) + o) = pack4(hv[0], hv[1], hv[2], hv[3]);
                 *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(dHb) + o) = pack4(gv[0], gv[1], gv[2], gv[3]);
             }
@@ -649,122 +634,89 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         if (wave == 0) scan(hn, par ^ 1);
         __syncthreads();
         // the next head's chunk-boundary state and exit gradient (this head's were consumed
-        // in S3); issued here rather than inside S3, where they queued behind the row prefetch
+        // in S3)
         load_states(hn);
-        // the next head's decay factors (waves 0..3, which reach the next barrier first)
+        // the next head's decay factors (waves 0..3)
         factors(par ^ 1);
-        // this head's per-token scales of the Phase III/IV tiles (token 16 tt + lr), read here
-        // so that the reads are in flight during Phase II
-        float ei_t[4], wdt_t[4];
+        // this head's per-token scales of the Phase III/IV tiles (token 16 (2 wm + t) + lr)
+        float ei_t[2], wdt_t[2];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int i = 16 * tt + lr;
-            ei_t[tt] = sm.fac[par][base + i];
-            wdt_t[tt] = sm.w[par][i] * ld[base + i].y;
+        for (int t = 0; t < 2; ++t) {
+            const int i = 16 * (2 * wm + t) + lr;
+            ei_t[t] = sm.fac[par][base + i];
+            wdt_t[t] = sm.w[par][i] * ld[base + i].y;
         }
-        // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tiles 2wh, 2wh+1) ----
-        u16x4 dxo[2];
-        uint32_t dxoff[2];
+        // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tile wj) ----
+        u16x4 dxo;
+        uint32_t dxoff;
         {
-            f32x4 acc[2], acc4[2];
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc4 = {0.f, 0.f, 0.f, 0.f};
+            // Q[i][j] = 0 for i < j, so the kk block below the diagonal adds zeros
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-                acc4[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < 2; ++kk)
+                acc = mfma(frag_tr64(sm.dY, sl, wq, kk), lds_frag(sm.QT, swz_row64(sl, wj, kk)), acc);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                acc4 = mfma(lds_frag(dHb, swz_row128(sl, wq, kk)), lds_frag(sm.B, swz_row128(sl, wj, kk)), acc4);
+            const int j = 16 * wj + lr;
+            const float wjv = sm.w[par][j], dt_j = ld[base + j].y;
+            const uint32_t o = swz_pc64(sl, wj, wq);
+            const u16x4 x4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.X) + o);
+            const u16x4 y4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.dY) + o);
+            // acc4[j][p] = (dH B_j)[p]: with x it also gives the exit-gradient term
+            // f_j = w_j dt_j x_j.(dH B_j) of dLam (this wave's p-tile)
+            float ddp = 0.f, xb = 0.f, dxv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float xv = bf16_to_f32(x4[v]);
+                const float pre = fmaf(wjv, acc4[v], acc[v]);
+                ddp = fmaf(xv, pre, ddp);
+                xb = fmaf(xv, acc4[v], xb);
+                dxv[v] = fmaf(Dh, bf16_to_f32(y4[v]), dt_j * pre);
             }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                // Q[i][j] = 0 for i < j, so the kk block below the diagonal adds zeros
-                const bf16x8 fa = frag_tr64(sm.dY, sl, wq, kk);
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    acc[q] = mfma(fa, lds_frag(sm.QT, swz_row64(sl, 2 * wh + q, kk)), acc[q]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 fa = lds_frag(dHb, swz_row128(sl, wq, kk));
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    acc4[q] = mfma(fa, lds_frag(sm.B, swz_row128(sl, 2 * wh + q, kk)), acc4[q]);
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int j = 16 * (2 * wh + q) + lr;
-                const float wj = sm.w[par][j], dt_j = ld[base + j].y;
-                const uint32_t o = swz_pc64(sl, 2 * wh + q, wq);
-                const u16x4 x4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.X) + o);
-                const u16x4 y4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.dY) + o);
-                // acc4[j][p] = (dH B_j)[p]: with x it also gives the exit-gradient term
-                // f_j = w_j dt_j x_j.(dH B_j) of dLam (this wave's p-tile)
-                float ddp = 0.f, xb = 0.f, dxv[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float xv = bf16_to_f32(x4[v]);
-                    const float pre = fmaf(wj, acc4[q][v], acc[q][v]);
-                    ddp = fmaf(xv, pre, ddp);
-                    xb = fmaf(xv, acc4[q][v], xb);
-                    dxv[v] = fmaf(Dh, bf16_to_f32(y4[v]), dt_j * pre);
-                }
-                dxoff[q] = static_cast<uint32_t>(k * kLs + j) * tokb + (h * kP + 16 * wq + lq) * 2;
-                dxo[q] = pack4(dxv[0], dxv[1], dxv[2], dxv[3]);
-                ddp = rows4_sum(ddp);
-                xb = rows4_sum(xb) * (wj * dt_j);
-                if (lane < 16) {
-                    sm.dd[j][wq] = ddp;
-                    sm.fp[j][wq] = xb;
-                }
+            dxoff = static_cast<uint32_t>(k * kLs + j) * tokb + (h * kP + 16 * wq + lq) * 2;
+            dxo = pack4(dxv[0], dxv[1], dxv[2], dxv[3]);
+            ddp = rows4_sum(ddp);
+            xb = rows4_sum(xb) * (wjv * dt_j);
+            if (lane < 16) {
+                sm.dd[j][wq] = ddp;
+                sm.fp[j][wq] = xb;
             }
         }
-        // Phase III / IV: per-head dC, dB contributions (n-tile = wave, tok-tiles 0..3);
-        // the state fragments are read once for the four token tiles.
+        // Phase III / IV: per-head dC, dB contributions (n-tile wn, tok-tiles 2wm, 2wm+1);
+        // the state fragments are read once for both token tiles.
         {
             bf16x8 fH[2], fdH[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                fH[kk] = frag_tr128(Hb, sl, wave, kk);
-                fdH[kk] = frag_tr128(dHb, sl, wave, kk);
-            }
-            bf16x8 fy[2][2], fxx[2][2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                fy[0][kk] = lds_frag(sm.dY, swz_row64(sl, 0, kk));
-                fxx[0][kk] = lds_frag(sm.X, swz_row64(sl, 0, kk));
+                fH[kk] = frag_tr128(Hb, sl, wn, kk);
+                fdH[kk] = frag_tr128(dHb, sl, wn, kk);
             }
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+            for (int t = 0; t < 2; ++t) {
+                const int tt = 2 * wm + t;
                 const int i = 16 * tt + lr;
-                const int cb = tt & 1;
-                if (tt + 1 < 4) {
-#pragma unroll
-                    for (int kk = 0; kk < 2; ++kk) {
-                        fy[cb ^ 1][kk] = lds_frag(sm.dY, swz_row64(sl, tt + 1, kk));
-                        fxx[cb ^ 1][kk] = lds_frag(sm.X, swz_row64(sl, tt + 1, kk));
-                    }
-                }
                 f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    ac = mfma(fH[kk], fy[cb][kk], ac);
-                    ab = mfma(fdH[kk], fxx[cb][kk], ab);
+                    ac = mfma(fH[kk], lds_frag(sm.dY, swz_row64(sl, tt, kk)), ac);
+                    ab = mfma(fdH[kk], lds_frag(sm.X, swz_row64(sl, tt, kk)), ab);
                 }
-                const float ei = ei_t[tt], wdt = wdt_t[tt];
+                const float ei = ei_t[t], wdt = wdt_t[t];
                 // the token's scale ei is fused into the accumulate and applied to the dot
                 // product once after its reduction
                 float o = 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    o = fmaf(cC[tt][v], ac[v], o);
-                    dCa[tt][v] = fmaf(ac[v], ei, dCa[tt][v]);
-                    dBa[tt][v] = fmaf(ab[v], wdt, dBa[tt][v]);
+                    o = fmaf(cC[t][v], ac[v], o);
+                    dCa[t][v] = fmaf(ac[v], ei, dCa[t][v]);
+                    dBa[t][v] = fmaf(ab[v], wdt, dBa[t][v]);
                 }
                 o = rows4_sum(o) * ei;
-                if (lane < 16) sm.offin[i][wave] = o;
+                if (lane < 16) sm.offin[i][wn] = o;
             }
         }
-        // dx leaves after Phases III/IV rather than in the middle of Phase II (1.636 ->
-        // 1.623 ms)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) buf_st_8b(rdx, dxoff[q], dxo[q]);
+        buf_st_8b(rdx, dxoff, dxo);
         __syncthreads();
     }
     // the last head's combine (its partials were published by the final S4 barrier)
@@ -773,26 +725,23 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     // sum_h K applied once: dC^T[n][i] += sum_j B[j][n] K[i][j]; dB^T[n][j] += sum_i C[i][n] K[i][j]
     refresh_lane();
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, 2 * wh + q, wq)) =
-            pack4(Ks[q][0], Ks[q][1], Ks[q][2], Ks[q][3]);
-    }
+    *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, wj, wq)) = pack4(Ks[0], Ks[1], Ks[2], Ks[3]);
     __syncthreads();
     {
         const bf16_t *KT = sm.QT;  // [j][i]
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int t = 0; t < 2; ++t) {
+            const int tt = 2 * wm + t;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                dCa[tt] = mfma(frag_tr128(sm.B, sl, wave, kk), frag_tr64(KT, sl, tt, kk), dCa[tt]);
-                dBa[tt] = mfma(frag_tr128(sm.C, sl, wave, kk), lds_frag(KT, swz_row64(sl, tt, kk)), dBa[tt]);
+                dCa[t] = mfma(frag_tr128(sm.B, sl, wn, kk), frag_tr64(KT, sl, tt, kk), dCa[t]);
+                dBa[t] = mfma(frag_tr128(sm.C, sl, wn, kk), lds_frag(KT, swz_row64(sl, tt, kk)), dBa[t]);
             }
-            const int t = 16 * tt + lr;
-            if (tk + t < T) {
-                const int64_t o = ((b * T + tk + t) * a.G + g) * kN + 16 * wave + lq;
-                *reinterpret_cast<float4 *>(a.dC + o) = make_float4(dCa[tt][0], dCa[tt][1], dCa[tt][2], dCa[tt][3]);
-                *reinterpret_cast<float4 *>(a.dB + o) = make_float4(dBa[tt][0], dBa[tt][1], dBa[tt][2], dBa[tt][3]);
+            const int tl = 16 * tt + lr;
+            if (tk + tl < T) {
+                const int64_t o = ((b * T + tk + tl) * a.G + g) * kN + 16 * wn + lq;
+                *reinterpret_cast<float4 *>(a.dC + o) = make_float4(dCa[t][0], dCa[t][1], dCa[t][2], dCa[t][3]);
+                *reinterpret_cast<float4 *>(a.dB + o) = make_float4(dBa[t][0], dBa[t][1], dBa[t][2], dBa[t][3]);
             }
         }
     }
