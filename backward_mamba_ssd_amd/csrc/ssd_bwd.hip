@@ -250,15 +250,21 @@ static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the stat
 
 // Sixteen waves, four per SIMD, so that each SIMD has other waves to issue from while
 // one waits on LDS, an MFMA result or a barrier.  Wave w's tiles (every tile 16 x 16):
-//   Gram / K / Phase I, [i][j]:   i-tile wq = w % 4, j-tile wj = w / 4
+//   Gram / K / Phase I, [i][j]:   i-tile gi, j-tile gj from kGramTiles
 //   state products, [n][p]:       n-tile wn = w % 8, p-tiles 2 wm, 2 wm + 1 (wm = w / 8)
 //   Phase II, [p][j]:             p-tile wq, j-tile wj
 //   Phase III/IV and K, [n][tok]: n-tile wn, token tiles 2 wm, 2 wm + 1
+// Gram tile (i-tile << 2 | j-tile) of wave w in bits 4w .. 4w + 3.  The ten tiles on or
+// below the diagonal carry Phase I's work; wave w runs on SIMD w % 4, and the table gives
+// SIMDs 0 .. 3 two, three, three and two of them (wave 0, which also runs the per-token
+// combine, holds a zero tile), instead of one to four with i = w % 4, j = w / 4.
+constexpr uint64_t kGramTiles = 0xb6327d94fc80ea51ull;
+
 __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a) {
     __shared__ BlkSmem sm;
     const int nb = static_cast<int>(a.L / kLs);
     int id = xcd_remap(blockIdx.x, gridDim.x);
-    const int k = id % nb;
+    int k = id % nb;
     id /= nb;
     const int c = static_cast<int>(id % a.nchunks);
     id = static_cast<int>(id / a.nchunks);
@@ -268,11 +274,12 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const int64_t tk = cstart + static_cast<int64_t>(k) * kLs;
     if (tk >= T) return;  // uniform for the whole workgroup, before any barrier
     const int64_t cend = (cstart + a.L < T) ? cstart + a.L : T;
-    const int nbc = static_cast<int>((cend - cstart + kLs - 1) / kLs);
+    int nbc = static_cast<int>((cend - cstart + kLs - 1) / kLs);
     const int hpg = a.H / a.G;
-    const int kS_ = 64 * k - 1, kE_ = 64 * k + kLs - 1, kEnd_ = 64 * nbc - 1, base_ = 64 * k;
+    int kS_ = 64 * k - 1, kE_ = 64 * k + kLs - 1, kEnd_ = 64 * nbc - 1, base_ = 64 * k;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int wq = wave & 3, wj = wave >> 2, wn = wave & 7, wm = wave >> 3;
+    int wq = wave & 3, wj = wave >> 2, wn = wave & 7, wm = wave >> 3;
+    int gi = static_cast<int>((kGramTiles >> (4 * wave)) >> 2) & 3, gj = static_cast<int>(kGramTiles >> (4 * wave)) & 3;
     // Lane-derived indices are re-formed at the top of every head iteration from a
     // value the compiler cannot see through, so the LDS addresses built from them are
     // computed next to their uses instead of occupying registers across the loop.
@@ -415,12 +422,12 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     if (wave == 0) scan(h0, 0);
     __syncthreads();
     factors(0);
-    // Gram tile of block k, [i][j]: i-tile wq, j-tile wj
+    // Gram tile of block k, [i][j]: i-tile gi, j-tile gj
     f32x4 Gt = {0.f, 0.f, 0.f, 0.f};
-    if (wj <= wq) {
+    if (gj <= gi) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            Gt = mfma(lds_frag(sm.C, swz_row128(sl, wq, kk)), lds_frag(sm.B, swz_row128(sl, wj, kk)), Gt);
+            Gt = mfma(lds_frag(sm.C, swz_row128(sl, gi, kk)), lds_frag(sm.B, swz_row128(sl, gj, kk)), Gt);
     }
     // C of block k at this lane's (token, n) positions of the Phase III tiles
     float cC[2][4];
@@ -496,6 +503,12 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 
     for (int hh = 0; hh < hpg; ++hh) {
         refresh_lane();
+        // The block and wave indices pass through an empty asm at every head, so that the
+        // comparisons and offsets derived from them are re-formed in scalar registers at
+        // their uses rather than hoisted out of the loop, where they outnumber the scalar
+        // registers and are parked in vector lanes (one readlane per use).
+        asm volatile("" : "+s"(k), "+s"(nbc), "+s"(wq), "+s"(wj), "+s"(wn), "+s"(wm), "+s"(gi), "+s"(gj));
+        asm volatile("" : "+s"(kS_), "+s"(kE_), "+s"(kEnd_), "+s"(base_));
         const int h = h0 + hh, par = hh & 1;
         const float Dh = head_D(hh);
         const float2 *ld = sm.ld[par];  // (Lam, dt) of this head's chunk
@@ -530,32 +543,32 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         prefetch(hn);  // registers are free once staged
         // ---- S2: Phase I of block k, then the state products over the other blocks ----
         if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
-        // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile wq, j-tile wj)
-        if (wj > wq) {
+        // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile gi, j-tile gj)
+        if (gj > gi) {
             // above the diagonal every entry is zero: Q^T's tile and the partial sums
-            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, wj, wq)) = u16x4{0, 0, 0, 0};
-            if (lane < 16) sm.col[par][16 * wj + lr][wq] = 0.f;
+            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = u16x4{0, 0, 0, 0};
+            if (lane < 16) sm.col[par][16 * gj + lr][gi] = 0.f;
             typedef float f32x4v __attribute__((ext_vector_type(4)));
-            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][wj][16 * wq + lq]) = f32x4v{0.f, 0.f, 0.f, 0.f};
+            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][gj][16 * gi + lq]) = f32x4v{0.f, 0.f, 0.f, 0.f};
             if (lane == 0) sm.dd_sum[par][wave] = 0.f;
         } else {
             float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
             f32x4 dW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                dW = mfma(lds_frag(sm.dY, swz_row64(sl, wq, kk)), lds_frag(sm.X, swz_row64(sl, wj, kk)), dW);
-            if (wj == wq) {  // diagonal tile: dW[i][i] = dy_i . x_i feeds dD
+                dW = mfma(lds_frag(sm.dY, swz_row64(sl, gi, kk)), lds_frag(sm.X, swz_row64(sl, gj, kk)), dW);
+            if (gj == gi) {  // diagonal tile: dW[i][i] = dy_i . x_i feeds dD
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     if (lq + v == lr) diag += dW[v];
             }
-            const int j = 16 * wj + lr;
+            const int j = 16 * gj + lr;
             const float2 lj = ld[base + j];
             const float lam_j = lj.x, dt_j = lj.y;
             float qv[4], colacc = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int i = 16 * wq + lq + v;
+                const int i = 16 * gi + lq + v;
                 const float m = (j <= i) ? __expf(ld[base + i].x - lam_j) : 0.f;
                 const float kv = dW[v] * m * dt_j;
                 Ks[v] += kv;
@@ -567,14 +580,14 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 colacc += r;
                 qv[v] = Gt[v] * m;
             }
-            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, wj, wq)) = pack4(qv[0], qv[1], qv[2], qv[3]);
+            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = pack4(qv[0], qv[1], qv[2], qv[3]);
             colacc = rows4_sum(colacc);
-            if (lane < 16) sm.col[par][j][wq] = colacc;
+            if (lane < 16) sm.col[par][j][gi] = colacc;
             typedef float f32x4v __attribute__((ext_vector_type(4)));
             f32x4v r;
 #pragma unroll
             for (int v = 0; v < 4; ++v) r[v] = row16_sum(rowacc[v]);
-            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][wj][16 * wq + lq]) = r;
+            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][gj][16 * gi + lq]) = r;
             diag = wave_total(diag);
             if (lane == 0) sm.dd_sum[par][wave] = diag;
         }
@@ -725,7 +738,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     // sum_h K applied once: dC^T[n][i] += sum_j B[j][n] K[i][j]; dB^T[n][j] += sum_i C[i][n] K[i][j]
     refresh_lane();
     __syncthreads();
-    *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, wj, wq)) = pack4(Ks[0], Ks[1], Ks[2], Ks[3]);
+    *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = pack4(Ks[0], Ks[1], Ks[2], Ks[3]);
     __syncthreads();
     {
         const bf16_t *KT = sm.QT;  // [j][i]
