@@ -245,6 +245,7 @@ struct __align__(16) BlkSmem {
     // products, for t in block k it is exp(Lam_t - Lam_blk0); w[i] = exp(Lam_e - Lam_i)
     // for the tokens of block k; es = exp(Lam_blk0), ee = exp(Lam_end - Lam_e).
     float fac[2][kMaxBlk * kLs], w[2][kLs], es[2], ee[2];
+    uint32_t lanetab[64][8];  // SwzLane of lane l, formed once (6 words and 2 of padding)
 };
 static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the state tiles");
 
@@ -294,9 +295,31 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         lq = (lane >> 4) * 4;
         pid = tid & 511;  // staging piece: row pid / 8, piece pid % 8 (two threads per piece)
         stg = swz_stage64(pid >> 3, pid & 7);
-        sl = swz_lane(lane);
+        // two LDS reads instead of the thirty-odd operations that form the offsets
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x4 t0 = *reinterpret_cast<const u32x4 *>(&sm.lanetab[lane][0]);
+        const u32x2 t1 = *reinterpret_cast<const u32x2 *>(&sm.lanetab[lane][4]);
+        sl.row64 = t0[0];
+        sl.row128 = t0[1];
+        sl.tr64 = t0[2];
+        sl.tr128 = t0[3];
+        sl.pc64 = t1[0];
+        sl.pc128 = t1[1];
     };
-    refresh_lane();
+    tid = static_cast<int>(threadIdx.x);
+    lane = tid & 63;
+    lr = lane & 15;
+    lq = (lane >> 4) * 4;
+    pid = tid & 511;
+    stg = swz_stage64(pid >> 3, pid & 7);
+    sl = swz_lane(lane);
+    if (wave == 0) {  // read inside the head loop, after several barriers
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x4 *>(&sm.lanetab[lane][0]) = u32x4{sl.row64, sl.row128, sl.tr64, sl.tr128};
+        *reinterpret_cast<u32x2 *>(&sm.lanetab[lane][4]) = u32x2{sl.pc64, sl.pc128};
+    }
     // A and D of the group's heads, lane l holding head h0 + l; a head's value is read
     // with readlane (a scalar, no memory wait).  Loads through the kernel's pointers would
     // be vector loads whose waits also drain every row and state load in flight.
@@ -545,12 +568,15 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
         // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile gi, j-tile gj)
         if (gj > gi) {
-            // above the diagonal every entry is zero: Q^T's tile and the partial sums
-            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = u16x4{0, 0, 0, 0};
-            if (lane < 16) sm.col[par][16 * gj + lr][gi] = 0.f;
+            // above the diagonal every entry is zero: Q^T's tile and the partial sums (the
+            // zero is formed here, not held in registers across the loop)
+            float z = 0.f;
+            asm volatile("" : "+v"(z));
+            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = pack4(z, z, z, z);
+            if (lane < 16) sm.col[par][16 * gj + lr][gi] = z;
             typedef float f32x4v __attribute__((ext_vector_type(4)));
-            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][gj][16 * gi + lq]) = f32x4v{0.f, 0.f, 0.f, 0.f};
-            if (lane == 0) sm.dd_sum[par][wave] = 0.f;
+            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][gj][16 * gi + lq]) = f32x4v{z, z, z, z};
+            if (lane == 0) sm.dd_sum[par][wave] = z;
         } else {
             float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
             f32x4 dW = {0.f, 0.f, 0.f, 0.f};
@@ -591,11 +617,21 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             diag = wave_total(diag);
             if (lane == 0) sm.dd_sum[par][wave] = diag;
         }
-        // The sums start from zero; the decayed chunk-boundary terms are added in S3.
-        // Per 32-token step the wave reads one n fragment and two p fragments.
+        // The sums start from the decayed chunk-boundary terms (the state entering the
+        // chunk, the gradient leaving it).  Per 32-token step the wave reads one n fragment
+        // and two p fragments.
         f32x4 aH[2], adH[2];
+        {
+            const float es = sm.es[par];  // chunk start -> block k start
+            const float ee = sm.ee[par];  // block k end -> chunk end
 #pragma unroll
-        for (int q = 0; q < 2; ++q) aH[q] = adH[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    aH[q][v] = es * Hs[q][v];
+                    adH[q][v] = ee * bf16_to_f32(dHr[4 * q + v]);
+                }
+        }
         {
             auto chain = [&](const bf16_t *bc, const bf16_t *xs, f32x4 *acc) {
 #pragma unroll
@@ -623,18 +659,12 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         // ---- S3: block-entry state and exit gradient in bf16, [p][n] ----
         bf16_t *Hb = sm.R, *dHb = sm.R + kT128;
         {
-            const float es = sm.es[par];  // chunk start -> block k start
-            const float ee = sm.ee[par];  // block k end -> chunk end
             float dotp = 0.f;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                f32x4 hv, gv;
+                const f32x4 hv = aH[q], gv = adH[q];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    hv[v] = fmaf(es, Hs[q][v], aH[q][v]);
-                    gv[v] = fmaf(ee, bf16_to_f32(dHr[4 * q + v]), adH[q][v]);
-                    dotp = fmaf(hv[v], gv[v], dotp);
-                }
+                for (int v = 0; v < 4; ++v) dotp = fmaf(hv[v], gv[v], dotp);
                 const uint32_t o = swz_pc128(sl, 2 * wm + q, wn);  // [p][n]
                 *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(Hb) + o) = pack4(hv[0], hv[1], hv[2], hv[3]);
                 *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(dHb) + o) = pack4(gv[0], gv[1], gv[2], gv[3]);
