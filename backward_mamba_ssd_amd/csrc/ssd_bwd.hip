@@ -261,6 +261,25 @@ static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the stat
 // combine, holds a zero tile), instead of one to four with i = w % 4, j = w / 4.
 constexpr uint64_t kGramTiles = 0xb6327d94fc80ea51ull;
 
+// Sums over the 16 lanes of a row for four values at once: lane lr of the row returns
+// the row's total of v[lr / 4].  Row mirror, then half-row mirror, exchange the values a
+// lane does not keep (two of four, then one of two); two quad swaps finish the sums.
+// The additions run in a fixed order, so the sums are deterministic.
+__device__ __forceinline__ float row16_sum4(const float (&v)[4], int lr) {
+#define SSM_DPP(x, ctrl) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), (ctrl), 0xf, 0xf, false))
+    const bool lo8 = lr < 8, lo4 = (lr & 7) < 4;
+    float a = lo8 ? v[0] : v[2], b = lo8 ? v[1] : v[3];
+    a += SSM_DPP(lo8 ? v[2] : v[0], 0x140);  // row_mirror: lane lr <-> 15 - lr
+    b += SSM_DPP(lo8 ? v[3] : v[1], 0x140);
+    float k = lo4 ? a : b;
+    k += SSM_DPP(lo4 ? b : a, 0x141);        // row_half_mirror: lr <-> 7 - lr within halves
+    k += SSM_DPP(k, 0xB1);                    // quad_perm [1,0,3,2]
+    k += SSM_DPP(k, 0x4E);                    // quad_perm [2,3,0,1]
+#undef SSM_DPP
+    return k;
+}
+
 __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a) {
     __shared__ BlkSmem sm;
     const int nb = static_cast<int>(a.L / kLs);
@@ -578,44 +597,53 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][gj][16 * gi + lq]) = f32x4v{z, z, z, z};
             if (lane == 0) sm.dd_sum[par][wave] = z;
         } else {
-            float rowacc[4] = {0.f, 0.f, 0.f, 0.f}, diag = 0.f;
             f32x4 dW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
                 dW = mfma(lds_frag(sm.dY, swz_row64(sl, gi, kk)), lds_frag(sm.X, swz_row64(sl, gj, kk)), dW);
-            if (gj == gi) {  // diagonal tile: dW[i][i] = dy_i . x_i feeds dD
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (lq + v == lr) diag += dW[v];
-            }
             const int j = 16 * gj + lr;
             const float2 lj = ld[base + j];
             const float lam_j = lj.x, dt_j = lj.y;
-            float qv[4], colacc = 0.f;
+            float rowv[4], qv[4], colacc = 0.f;
+            // off the diagonal every (i, j) has j < i; on it the masks apply
+            auto entries = [&](bool on_diag) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int i = 16 * gi + lq + v;
-                const float m = (j <= i) ? __expf(ld[base + i].x - lam_j) : 0.f;
-                const float kv = dW[v] * m * dt_j;
-                Ks[v] += kv;
-                // R[i][i] enters row sum i and column sum i alike and cancels in
-                // dLam_i, so it is left out of both: with strong decay it is the only
-                // O(1) entry, and subtracting it would bury the small terms in rounding
-                const float r = (j < i) ? kv * Gt[v] : 0.f;
-                rowacc[v] += r;
-                colacc += r;
-                qv[v] = Gt[v] * m;
+                for (int v = 0; v < 4; ++v) {
+                    const int i = 16 * gi + lq + v;
+                    float m = __expf(ld[base + i].x - lam_j);
+                    if (on_diag) m = (j <= i) ? m : 0.f;
+                    const float kv = dW[v] * dt_j * m;
+                    Ks[v] += kv;
+                    // R[i][i] enters row sum i and column sum i alike and cancels in
+                    // dLam_i, so it is left out of both: with strong decay it is the only
+                    // O(1) entry, and subtracting it would bury the small terms in rounding
+                    float r = kv * Gt[v];
+                    if (on_diag) r = (j < i) ? r : 0.f;
+                    rowv[v] = r;
+                    colacc += r;
+                    qv[v] = Gt[v] * m;
+                }
+            };
+            if (gj == gi) {
+                entries(true);
+                float diag = 0.f;  // dW[i][i] = dy_i . x_i feeds dD
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (lq + v == lr) diag += dW[v];
+                diag = wave_total(diag);
+                if (lane == 0) sm.dd_sum[par][wave] = diag;
+            } else {
+                entries(false);
+                float z = 0.f;
+                asm volatile("" : "+v"(z));
+                if (lane == 0) sm.dd_sum[par][wave] = z;
             }
             *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = pack4(qv[0], qv[1], qv[2], qv[3]);
             colacc = rows4_sum(colacc);
             if (lane < 16) sm.col[par][j][gi] = colacc;
-            typedef float f32x4v __attribute__((ext_vector_type(4)));
-            f32x4v r;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) r[v] = row16_sum(rowacc[v]);
-            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][gj][16 * gi + lq]) = r;
-            diag = wave_total(diag);
-            if (lane == 0) sm.dd_sum[par][wave] = diag;
+            // row sums of the tile's four rows in one pass: lane lr ends with row lq + lr / 4
+            const float rs = row16_sum4(rowv, lr);
+            if ((lr & 3) == 0) sm.row[par][gj][16 * gi + lq + (lr >> 2)] = rs;
         }
         // The sums start from the decayed chunk-boundary terms (the state entering the
         // chunk, the gradient leaving it).  Per 32-token step the wave reads one n fragment
