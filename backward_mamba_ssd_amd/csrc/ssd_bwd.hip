@@ -527,9 +527,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         // block's last token as +sum_i f_i, so it reaches da_j = sum_{i >= j} dLam_i as the
         // exclusive prefix sum_{i < j} f_i, summed directly (f_63, of order one even when
         // every other term underflows, never meets the small ones).
-        // (the shuffle runs in all 64 lanes: a lane reading from an inactive one gets 0)
-        float fprev = __shfl_up(fs, 1, 64);
-        fprev = (j > 0) ? fprev : 0.f;
+        // (a whole-wave DPP shift by one lane: lane j reads lane j - 1, lane 0 reads 0)
+        const float fprev = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, fs), 0x138, 0xf, 0xf, true));
         const float da = wave_suffix_sum(dl) + wave_prefix_sum(fprev);  // da_j = sum_{i >= j} dLam_i
         buf_st_f32(rddt, (static_cast<uint32_t>(k * kLs + j) * a.H + hc) * 4u, fmaf(head_A(hc - h0), da, ddd));
         const float pa = wave_total(ldc[base + j].y * da);
