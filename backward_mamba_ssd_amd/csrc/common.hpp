@@ -107,6 +107,13 @@ __device__ __forceinline__ float swap_pair_sum32(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float rows4_sum(float v) { return swap_pair_sum32(swap_pair_sum16(v)); }
+// rows4_sum of two values in one pass: the total of a in rows 0 and 2, of b in rows 1 and
+// 3.  The 16-lane swap of (a, b) gives rows (a0, b0, a2, b2) and (a1, b1, a3, b3), whose
+// sum pairs the rows of each value; the 32-lane pair sum then adds the halves.
+__device__ __forceinline__ float rows4_sum2(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return swap_pair_sum32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float wave_total(float v) { return rows4_sum(row16_sum(v)); }
 #undef SSM_DPP
 

@@ -492,8 +492,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 
     // Per-token combine of head hc (wave 0, lane = token of the block): the dLam terms,
     // da = reverse cumulative sum within the block, ddt, and the dA/dD partials.  Runs
-    // for head h-1 during head h's S2 (the arrays it reads are rewritten only after
-    // that phase's barrier, or are double-buffered by head parity).
+    // for head h-1 at the end of head h's S2 (the arrays it reads are rewritten only
+    // after that phase's barrier, or are double-buffered by head parity).
     auto combine = [&](int hc, int pc) {
         const int j = lane;
         const float2 *ldc = sm.ld[pc];
@@ -583,7 +583,6 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         __syncthreads();
         prefetch(hn);  // registers are free once staged
         // ---- S2: Phase I of block k, then the state products over the other blocks ----
-        if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
         // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile gi, j-tile gj)
         if (gj > gi) {
             // above the diagonal every entry is zero: Q^T's tile and the partial sums (the
@@ -682,6 +681,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 chain(sm.chainBC + sb * kT128, sm.R + sb * kT64, adH);
             }
         }
+        // the previous head's per-token combine, after this wave's products (wave 0, which
+        // holds a zero Gram tile; 1.313 -> 1.297 ms against running it first)
+        if (wave == 0 && hh > 0) combine(h - 1, par ^ 1);
         __syncthreads();
         // ---- S3: block-entry state and exit gradient in bf16, [p][n] ----
         bf16_t *Hb = sm.R, *dHb = sm.R + kT128;
@@ -746,12 +748,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             }
             dxoff = static_cast<uint32_t>(k * kLs + j) * tokb + (h * kP + 16 * wq + lq) * 2;
             dxo = pack4(dxv[0], dxv[1], dxv[2], dxv[3]);
-            ddp = rows4_sum(ddp);
-            xb = rows4_sum(xb) * (wjv * dt_j);
-            if (lane < 16) {
-                sm.dd[j][wq] = ddp;
-                sm.fp[j][wq] = xb;
-            }
+            // both sums over the tile's four lane rows in one pass: row 0 holds dd, row 1 f
+            const float sums = rows4_sum2(ddp, xb * (wjv * dt_j));
+            if (lane < 32) *(lane < 16 ? &sm.dd[j][wq] : &sm.fp[j][wq]) = sums;
         }
         // Phase III / IV: per-head dC, dB contributions (n-tile wn, tok-tiles 2wm, 2wm+1);
         // the state fragments are read once for both token tiles.
@@ -762,10 +761,10 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 fH[kk] = frag_tr128(Hb, sl, wn, kk);
                 fdH[kk] = frag_tr128(dHb, sl, wn, kk);
             }
+            float o[2];  // dy_i.(H C_i) exp(Lam_i), partial over the lane's n
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int tt = 2 * wm + t;
-                const int i = 16 * tt + lr;
                 f32x4 ac = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
@@ -774,17 +773,19 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 }
                 const float ei = ei_t[t], wdt = wdt_t[t];
                 // the token's scale ei is fused into the accumulate and applied to the dot
-                // product once after its reduction
-                float o = 0.f;
+                // product once per lane
+                float ot = 0.f;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    o = fmaf(cC[t][v], ac[v], o);
+                    ot = fmaf(cC[t][v], ac[v], ot);
                     dCa[t][v] = fmaf(ac[v], ei, dCa[t][v]);
                     dBa[t][v] = fmaf(ab[v], wdt, dBa[t][v]);
                 }
-                o = rows4_sum(o) * ei;
-                if (lane < 16) sm.offin[i][wn] = o;
+                o[t] = ot * ei;
             }
+            // both token tiles' sums over the four lane rows in one pass: row t holds tile t
+            const float os = rows4_sum2(o[0], o[1]);
+            if (lane < 32) sm.offin[16 * (2 * wm + (lane >> 4)) + lr][wn] = os;
         }
         buf_st_8b(rdx, dxoff, dxo);
         __syncthreads();
