@@ -9,10 +9,11 @@
 // integer k and the discarded bits; R = discarded bits scaled to 32 bits (floor),
 // and k+1 is taken iff u < R.
 //
-// The entropy word u is keyed by (seed, key, element): u = high 32 bits of output e
-// of a SplitMix64 stream (Steele, Lea & Flood 2014) whose seed is output `key` of
-// the stream seeded with `seed`; output k of a stream seeded with s is
-// mix64(s + (k+1)*gamma) with SplitMix64's published finaliser and gamma.
+// The entropy word u is keyed by (seed, key, element): for element e, the high (e even)
+// or low (e odd) 32 bits of output floor(e / 2) of a SplitMix64 stream (Steele, Lea &
+// Flood 2014) whose seed is output `key` of the stream seeded with `seed`; output k of
+// a stream seeded with s is mix64(s + (k+1)*gamma) with SplitMix64's published
+// finaliser and gamma.
 #pragma once
 
 #include "common.hpp"
@@ -81,38 +82,35 @@ __host__ __device__ __forceinline__ uint16_t sr16_bits_general(float v, uint32_t
     return static_cast<uint16_t>(sign | ((es << 10) + k + (u < R ? 1u : 0u)));
 }
 
-// The high 32 bits of sm64_mix(z), computed on 32-bit halves (the same value bit for
-// bit): only the high word of the second product is needed, and the high word of
-// z ^ (z >> 31) is hi ^ (hi >> 31).
-__device__ __forceinline__ uint32_t sm64_mix_hi(uint64_t z) {
-    const uint32_t zl = static_cast<uint32_t>(z), zh = static_cast<uint32_t>(z >> 32);
-    const uint32_t yl = zl ^ ((zl >> 30) | (zh << 2)), yh = zh ^ (zh >> 30);
-    constexpr uint32_t c1l = 0x1CE4E5B9u, c1h = 0xBF58476Du;  // 0xBF58476D1CE4E5B9
-    const uint64_t p = static_cast<uint64_t>(yl) * c1l;
-    const uint32_t ml = static_cast<uint32_t>(p);
-    const uint32_t mh = static_cast<uint32_t>(p >> 32) + yl * c1h + yh * c1l;
-    const uint32_t wl = ml ^ ((ml >> 27) | (mh << 5)), wh = mh ^ (mh >> 27);
-    constexpr uint32_t c2l = 0x133111EBu, c2h = 0x94D049BBu;  // 0x94D049BB133111EB
-    const uint32_t hi = __umulhi(wl, c2l) + wl * c2h + wh * c2l;
-    return hi ^ (hi >> 31);
-}
-
-// u for element e under (seed, key): sub = sr16_stream(seed, key) once per call
+// Entropy words: output k of the sub-stream sub = sr16_stream(seed, key) serves the two
+// elements 2k (its high 32 bits) and 2k + 1 (its low 32 bits), so one 64-bit finaliser
+// (six 32-bit multiplies at a quarter of the vector rate) covers two elements.
 __device__ __forceinline__ uint64_t sr16_stream(uint64_t seed, uint64_t key) {
     return sm64_mix(seed + (key + 1ull) * kGamma);
 }
 __device__ __forceinline__ uint32_t sr16_entropy(uint64_t sub, uint64_t e) {
-    return sm64_mix_hi(sub + (e + 1ull) * kGamma);
+    const uint64_t r = sm64_mix(sub + ((e >> 1) + 1ull) * kGamma);
+    return (e & 1ull) ? static_cast<uint32_t>(r) : static_cast<uint32_t>(r >> 32);
 }
-// u for the K consecutive elements e .. e+K-1: the stream counter advances by one
-// gamma per element, so only the first needs a 64-bit multiply.
+// u for the K consecutive elements e .. e+K-1 (K even): the stream counter advances by
+// one gamma per output, so only the first needs a 64-bit multiply.  e is even wherever
+// the kernels call this with a whole run (rows of an even state width); an odd e takes
+// the general path.
 template <int K>
 __device__ __forceinline__ void sr16_entropy_run(uint64_t sub, uint64_t e, uint32_t (&u)[K]) {
-    uint64_t z = sub + (e + 1ull) * kGamma;
+    static_assert(K % 2 == 0, "runs of whole outputs");
+    if ((e & 1ull) == 0) {
+        uint64_t z = sub + ((e >> 1) + 1ull) * kGamma;
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-        u[j] = sm64_mix_hi(z);
-        z += kGamma;
+        for (int j = 0; j < K; j += 2) {
+            const uint64_t r = sm64_mix(z);
+            u[j] = static_cast<uint32_t>(r >> 32);
+            u[j + 1] = static_cast<uint32_t>(r);
+            z += kGamma;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) u[j] = sr16_entropy(sub, e + j);
     }
 }
 

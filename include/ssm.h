@@ -201,7 +201,8 @@ ssm_status ssm_decode_step(const ssm_dims *d, ssm_dtype dtype, float *state, con
  * bits (8-byte aligned); each element is widened exactly to float32, advanced
  * by the same arithmetic as ssm_decode_step, and stored back with the rounding
  * rule of ssm_checkpoint_sr16 keyed by (seed, step): element i (flat index of
- * state16) uses u = high32( SM(SM(seed, step), i) ).  y is what ssm_decode_step
+ * state16) uses the entropy word of element i with ckpt_index = step (the high or
+ * low half of SM(SM(seed, step), i / 2) for even or odd i).  y is what ssm_decode_step
  * writes from the widened state, bit for bit.  Inputs as for ssm_decode_step;
  * the caller passes a distinct `step` per decode step so rounding choices are
  * independent across steps and reproducible for replay.
@@ -217,9 +218,12 @@ ssm_status ssm_decode_step_sr16(const ssm_dims *d, ssm_dtype dtype, uint16_t *st
  * mean state" (round up when the entropy residue is below the discarded
  * remainder) and "Recovering the state by replay" (a random step keeps its
  * random choices, so the entropy is a pure function of a key).
- * Element i of `state` (n_elems of them) is rounded with the entropy word
- *   u = high32( SM(SM(seed, ckpt_index), elem_offset + i) )
- * where SM(s, k) is output k (0-based) of a SplitMix64 stream seeded with s.
+ * Element i of `state` (n_elems of them), e = elem_offset + i, is rounded with
+ * the entropy word
+ *   u = high32( SM(SM(seed, ckpt_index), e / 2) )  for even e,
+ *   u = low32(  SM(SM(seed, ckpt_index), e / 2) )  for odd e,
+ * where SM(s, k) is output k (0-based) of a SplitMix64 stream seeded with s
+ * (one output serves two elements).
  * With R = floor(remainder * 2^32), the magnitude goes to the upper binary16
  * neighbour iff u < R.  Magnitudes reaching 65536 become infinity; NaN keeps
  * its sign as 0x7E00.  `out` receives binary16 bits and must not alias state.

@@ -308,11 +308,13 @@ uint64_t oracle_splitmix64_output(uint64_t seed, uint64_t k) {
     return sm64_mix(seed + (k + 1) * SM64_GAMMA);
 }
 
-/* Entropy word of element e of checkpoint j: the high 32 bits of output e of a
- * SplitMix64 stream whose seed is output j of the stream seeded with `seed`. */
+/* Entropy word of element e of checkpoint j: output floor(e/2) of a SplitMix64
+ * stream whose seed is output j of the stream seeded with `seed`, its high 32 bits
+ * for even e and its low 32 bits for odd e (one output serves two elements). */
 uint32_t oracle_hash32(uint64_t seed, uint64_t ckpt, uint64_t elem) {
     const uint64_t sub = oracle_splitmix64_output(seed, ckpt);
-    return (uint32_t)(oracle_splitmix64_output(sub, elem) >> 32);
+    const uint64_t out = oracle_splitmix64_output(sub, elem / 2);
+    return (elem % 2 == 0) ? (uint32_t)(out >> 32) : (uint32_t)(out & 0xFFFFFFFFu);
 }
 
 /*

@@ -35,9 +35,13 @@ def test_hash_is_keyed_by_all_three_counters():
     assert base != oracle.hash32(8, 3, 100)
     assert base != oracle.hash32(7, 4, 100)
     assert base != oracle.hash32(7, 3, 101)
-    # definition: high word of output e of the stream seeded by output j
+    # definition: output e // 2 of the stream seeded by output j, high word for even e,
+    # low word for odd e (one output serves two elements)
     sub = oracle.splitmix64_output(7, 3)
-    assert base == oracle.splitmix64_output(sub, 100) >> 32
+    out = oracle.splitmix64_output(sub, 50)
+    assert base == out >> 32
+    assert oracle.hash32(7, 3, 101) == out & 0xFFFFFFFF
+    assert oracle.hash32(7, 3, 102) == oracle.splitmix64_output(sub, 51) >> 32
 
 
 def test_hash_uniform_top_byte():
