@@ -445,17 +445,18 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     // q -> n-tile wn, p-tile 2 wm + q
     f32x4 Hs[2];
     u16x8 dHr;  // chunk-exit gradient tile pair (n-tile wn, p-tiles 2wm, 2wm + 1), bf16
+    // (through buffer descriptors over the head's tile: the 64-bit address arithmetic
+    // stays in scalar registers and the lanes add 32-bit offsets)
     auto load_states = [&](int h) {
-        const int64_t bh = static_cast<int64_t>(b) * a.H + h;
-        const float *hc = a.chunk_states + (bh * a.nchunks + c) * PN;
-        const bf16_t *dc = a.dstates + (bh * a.nchunks + c) * PN;
+        const int64_t tile = ((static_cast<int64_t>(b) * a.H + h) * a.nchunks + c) * PN;
+        const rsrc_t rh = make_rsrc(a.chunk_states + tile, PN * 4u);
+        const rsrc_t rd = make_rsrc(a.dstates + tile, PN * 2u);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int n = 16 * wn + lq, p = 16 * (2 * wm + q) + lr;
-            const float4 u = *reinterpret_cast<const float4 *>(hc + p * kN + n);
-            Hs[q] = f32x4{u.x, u.y, u.z, u.w};
+            const uint32_t n = 16 * wn + lq, p = 16 * (2 * wm + q) + lr;
+            Hs[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (p * kN + n) * 4u, 0, 0));
         }
-        dHr = *reinterpret_cast<const u16x8 *>(dc + dstate_pair(wn, wm, lane));
+        dHr = buf_ld_16b(rd, static_cast<uint32_t>(dstate_pair(wn, wm, lane)) * 2u);
     };
 
     prefetch(h0);
