@@ -67,7 +67,7 @@ __device__ __forceinline__ int dstate_pair(int nt, int m, int lane) {
     return ((nt * (kP / 32) + m) * 64 + lane) * 8;
 }
 
-struct DstSmem {
+struct __align__(16) DstSmem {
     bf16_t C[kLs * kSC];     // [tok][n]
     bf16_t EdY[kLs * kSY];   // [tok][p] = dy[tok][p] * exp(Lam_tok)
     float lam[2][kLs];
