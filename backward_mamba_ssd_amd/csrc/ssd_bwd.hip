@@ -227,7 +227,8 @@ constexpr int kBlkThreads = 1024;  // 16 waves
 struct __align__(16) BlkSmem {
     bf16_t B[kT128];                    // block k rows of B [j][n]
     bf16_t C[kT128];                    // block k rows of C [i][n]
-    bf16_t chainBC[(kMaxBlk - 1) * kT128];  // B rows of earlier blocks / C rows of later blocks
+    bf16_t chainBC[(kMaxBlk - 1) * kT128];  // B rows of earlier blocks / C rows of later blocks,
+                                            // transposed: [n][token], 64-wide rows
     bf16_t R[2 * kT128];                // per head: scaled x / dy rows of the other blocks,
                                         // then H and dH in bf16 ([p][n])
     bf16_t X[kT64], dY[kT64], QT[kT64]; // block k rows of x, dy; Q^T [j][i]
@@ -248,6 +249,10 @@ struct __align__(16) BlkSmem {
     uint32_t lanetab[64][8];  // SwzLane of lane l, formed once (6 words and 2 of padding)
 };
 static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the state tiles");
+static_assert(offsetof(BlkSmem, X) == offsetof(BlkSmem, R) + sizeof(BlkSmem::R) &&
+                  offsetof(BlkSmem, dY) == offsetof(BlkSmem, X) + sizeof(BlkSmem::X) &&
+                  sizeof(BlkSmem::R) + sizeof(BlkSmem::X) + sizeof(BlkSmem::dY) >= (kMaxBlk - 1) * kT128 * sizeof(bf16_t),
+              "R, X and dY hold the chain's B/C rows before their transposition");
 
 // Sixteen waves, four per SIMD, so that each SIMD has other waves to issue from while
 // one waits on LDS, an MFMA result or a barrier.  Wave w's tiles (every tile 16 x 16):
@@ -368,13 +373,16 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const u16x8 r = (t < T) ? *reinterpret_cast<const u16x8 *>(src + ((b * T + t) * a.G + g) * kN + nr_col) : z8;
         *reinterpret_cast<u16x8 *>(reinterpret_cast<char *>(dst) + nr_stg) = r;
     };
-    // head-independent tiles: block k B and C rows, B rows of earlier blocks, C rows of later ones
+    // head-independent tiles: block k B and C rows, B rows of earlier blocks, C rows of later
+    // ones (the latter staged in R, X and dY, free until the first head's staging, and
+    // transposed into chainBC below)
+    bf16_t *chain_tmp = sm.R;
     load_rows_n(Bm, tk, sm.B);
     load_rows_n(Cm, tk, sm.C);
     for (int kb = 0; kb < nbc; ++kb) {
         if (kb == k) continue;
         const int slot = kb < k ? kb : kb - 1;
-        load_rows_n(kb < k ? Bm : Cm, cstart + static_cast<int64_t>(kb) * kLs, sm.chainBC + slot * kT128);
+        load_rows_n(kb < k ? Bm : Cm, cstart + static_cast<int64_t>(kb) * kLs, chain_tmp + slot * kT128);
     }
 
     // per-head inputs held in registers one head ahead: waves 0..7 stage blocks 0, 1 and
@@ -465,6 +473,16 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     if (wave == 0) scan(h0, 0);
     __syncthreads();
     factors(0);
+    // The chain's B/C tiles transposed once to [n][token]: every state product of every head
+    // then reads its B/C operand as one 16-byte row fragment instead of two transposing reads.
+    // Fragment (n-tile nt, 32-token step kk) of a slot is read where the transposing read
+    // leaves it, so lane l writes exactly the piece it would have read.
+    for (int f = wave; f < (kMaxBlk - 1) * 16; f += 16) {
+        const int slot = f >> 4, nt = (f >> 1) & 7, kk = f & 1;
+        if (slot >= nbc - 1) break;
+        const bf16x8 v = frag_tr128(chain_tmp + slot * kT128, sl, nt, kk);
+        *reinterpret_cast<bf16x8 *>(reinterpret_cast<char *>(sm.chainBC + slot * kT128) + swz_row64(sl, nt, kk)) = v;
+    }
     // Gram tile of block k, [i][j]: i-tile gi, j-tile gj
     f32x4 Gt = {0.f, 0.f, 0.f, 0.f};
     if (gj <= gi) {
@@ -663,7 +681,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             auto chain = [&](const bf16_t *bc, const bf16_t *xs, f32x4 *acc) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 fa = frag_tr128(bc, sl, wn, kk);
+                    const bf16x8 fa = lds_frag(bc, swz_row64(sl, wn, kk));
                     bf16x8 fb[2];
 #pragma unroll
                     for (int t = 0; t < 2; ++t) fb[t] = frag_tr64(xs, sl, 2 * wm + t, kk);
