@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int lr = lane & 15, lk = (lane >> 4) * 8, lq = (lane >> 4) * 4;
+    const int lr = lane & 15, lq = (lane >> 4) * 4;
     const int64_t T = a.T;
     const float Ah = a.A[h];
     const bf16_t *dy = static_cast<const bf16_t *>(a.dy);
