@@ -56,15 +56,16 @@ namespace {
 // on distinct banks, and a wave's 16-byte row writes are conflict-free.
 constexpr int kSC = kN + 16;
 constexpr int kSY = kP + 16;
-// Offset (bf16 elements) of lane `lane`'s eight values of the tile pair (n-tile nt,
-// p-tiles 2m and 2m + 1) in one chunk's gradient of the workspace: the four
-// accumulator values of tile (nt, 2m) followed by those of tile (nt, 2m + 1), lane l
-// holding p = 16 pt + l % 16, n = 16 nt + 4 (l / 16) + 0..3.  Each lane moves 16
-// bytes, and a wave a whole 1 KB, in both kernels.  The gradient is rounded to bf16
-// here: every use in the per-block kernel rounds the block-exit gradient it builds
-// from it to bf16 for the MFMA operands anyway.
-__device__ __forceinline__ int dstate_pair(int nt, int m, int lane) {
-    return ((nt * (kP / 32) + m) * 64 + lane) * 8;
+// Offset (bf16 elements) of lane `lane`'s eight values of the tile pair (n-tiles 2 np
+// and 2 np + 1, p-tile pt) in one chunk's gradient of the workspace: the four
+// accumulator values of tile (2 np, pt) followed by those of tile (2 np + 1, pt), lane l
+// holding p = 16 pt + l % 16, n = 16 nt + 4 (l / 16) + 0..3.  Each lane moves 16 bytes,
+// and a wave a whole 1 KB, in both kernels (the 8-wave reverse pass, one n-tile per
+// wave, writes 8-byte halves).  The gradient is rounded to bf16 here: every use in the
+// per-block kernel rounds the block-exit gradient it builds from it to bf16 for the
+// MFMA operands anyway.
+__device__ __forceinline__ int dstate_pair(int np, int pt, int lane) {
+    return ((np * (kP / 16) + pt) * 64 + lane) * 8;
 }
 
 struct __align__(16) DstSmem {
@@ -79,6 +80,7 @@ struct __align__(16) DstSmem {
 // tile sees the same MFMA sequence either way, so the results do not depend on NW.
 template <int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
+    static_assert(NW == 4 || NW == 8, "two n-tiles per wave, or one");
     constexpr int kTiles = 32 / NW;  // dH^T tiles per wave
     constexpr int kNT = 8 / NW;      // n-tiles per wave
     __shared__ DstSmem sm;
@@ -146,15 +148,21 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
         const int buf = s & 1;
         if (s == nblk - 1 || (s + 1) % bpc == 0) {
             // gradient on the state leaving chunk c (everything after it), stored by tile
-            // pairs in accumulator lane order (tiles q and q + 1 share an n-tile)
+            // pairs in accumulator lane order (tiles q and q + 4 share a p-tile)
             bf16_t *dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
+            if constexpr (kNT == 2) {
 #pragma unroll
-            for (int q = 0; q < kTiles; q += 2) {
-                const int nt = kNT * wave + q / 4, m = (q % 4) / 2;
-                const u16x4 lo = pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
-                const u16x4 hi = pack4(G[q + 1][0], G[q + 1][1], G[q + 1][2], G[q + 1][3]);
-                const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                *reinterpret_cast<u16x8 *>(dst + dstate_pair(nt, m, lane)) = v;
+                for (int q = 0; q < 4; ++q) {
+                    const u16x4 lo = pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
+                    const u16x4 hi = pack4(G[q + 4][0], G[q + 4][1], G[q + 4][2], G[q + 4][3]);
+                    const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    *reinterpret_cast<u16x8 *>(dst + dstate_pair(wave, q, lane)) = v;
+                }
+            } else {  // one n-tile per wave: its half of each pair
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<u16x4 *>(dst + dstate_pair(wave >> 1, q, lane) + 4 * (wave & 1)) =
+                        pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
             }
         }
         if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(R.dtr * Ah);
@@ -257,7 +265,7 @@ static_assert(offsetof(BlkSmem, X) == offsetof(BlkSmem, R) + sizeof(BlkSmem::R) 
 // Sixteen waves, four per SIMD, so that each SIMD has other waves to issue from while
 // one waits on LDS, an MFMA result or a barrier.  Wave w's tiles (every tile 16 x 16):
 //   Gram / K / Phase I, [i][j]:   i-tile gi, j-tile gj from kGramTiles
-//   state products, [n][p]:       n-tile wn = w % 8, p-tiles 2 wm, 2 wm + 1 (wm = w / 8)
+//   state products, [n][p]:       n-tiles 2 wq, 2 wq + 1, p-tile wj
 //   Phase II, [p][j]:             p-tile wq, j-tile wj
 //   Phase III/IV and K, [n][tok]: n-tile wn, token tiles 2 wm, 2 wm + 1
 // Gram tile (i-tile << 2 | j-tile) of wave w in bits 4w .. 4w + 3.  The ten tiles on or
@@ -449,10 +457,10 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         }
     };
     // raw chunk-boundary state and chunk-exit gradient of the next head, loaded a full
-    // head ahead of their use in S3; the state tiles in accumulator layout, [n][p]:
-    // q -> n-tile wn, p-tile 2 wm + q
+    // head ahead of their use in S2; the state tiles in accumulator layout, [n][p]:
+    // q -> n-tile 2 wq + q, p-tile wj
     f32x4 Hs[2];
-    u16x8 dHr;  // chunk-exit gradient tile pair (n-tile wn, p-tiles 2wm, 2wm + 1), bf16
+    u16x8 dHr;  // chunk-exit gradient tile pair (n-tiles 2 wq, 2 wq + 1, p-tile wj), bf16
     // (through buffer descriptors over the head's tile: the 64-bit address arithmetic
     // stays in scalar registers and the lanes add 32-bit offsets)
     auto load_states = [&](int h) {
@@ -461,10 +469,10 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         const rsrc_t rd = make_rsrc(a.dstates + tile, PN * 2u);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const uint32_t n = 16 * wn + lq, p = 16 * (2 * wm + q) + lr;
+            const uint32_t n = 16 * (2 * wq + q) + lq, p = 16 * wj + lr;
             Hs[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (p * kN + n) * 4u, 0, 0));
         }
-        dHr = buf_ld_16b(rd, static_cast<uint32_t>(dstate_pair(wn, wm, lane)) * 2u);
+        dHr = buf_ld_16b(rd, static_cast<uint32_t>(dstate_pair(wq, wj, lane)) * 2u);
     };
 
     prefetch(h0);
@@ -663,8 +671,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             if ((lr & 3) == 0) sm.row[par][gj][16 * gi + lq + (lr >> 2)] = rs;
         }
         // The sums start from the decayed chunk-boundary terms (the state entering the
-        // chunk, the gradient leaving it).  Per 32-token step the wave reads one n fragment
-        // and two p fragments.
+        // chunk, the gradient leaving it).  Per 32-token step the wave reads two n fragments
+        // (row reads) and one p fragment (the transposing read).
         f32x4 aH[2], adH[2];
         {
             const float es = sm.es[par];  // chunk start -> block k start
@@ -681,12 +689,12 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             auto chain = [&](const bf16_t *bc, const bf16_t *xs, f32x4 *acc) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 fa = lds_frag(bc, swz_row64(sl, wn, kk));
-                    bf16x8 fb[2];
+                    bf16x8 fa[2];
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) fb[t] = frag_tr64(xs, sl, 2 * wm + t, kk);
+                    for (int q = 0; q < 2; ++q) fa[q] = lds_frag(bc, swz_row64(sl, 2 * wq + q, kk));
+                    const bf16x8 fb = frag_tr64(xs, sl, wj, kk);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) acc[t] = mfma(fa, fb[t], acc[t]);
+                    for (int q = 0; q < 2; ++q) acc[q] = mfma(fa[q], fb, acc[q]);
                 }
             };
 #pragma unroll
@@ -713,7 +721,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 const f32x4 hv = aH[q], gv = adH[q];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) dotp = fmaf(hv[v], gv[v], dotp);
-                const uint32_t o = swz_pc128(sl, 2 * wm + q, wn);  // [p][n]
+                const uint32_t o = swz_pc128(sl, wj, 2 * wq + q);  // [p][n]
                 *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(Hb) + o) = pack4(hv[0], hv[1], hv[2], hv[3]);
                 *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(dHb) + o) = pack4(gv[0], gv[1], gv[2], gv[3]);
             }
