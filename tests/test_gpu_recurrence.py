@@ -170,6 +170,32 @@ def test_exact_replay_reproduces_checkpoints(ssm):
     assert torch.equal(whole["state"], ck[-1])
 
 
+@pytest.mark.parametrize("shape", [(11, 100, 4, 70), (16, 256, 8, 16), (2, 8, 2, 0)])
+def test_replay_from_binary16_checkpoint(ssm, shape):
+    """Replay from SR16 bits equals replay from the same values widened to float32, state
+    and y bit for bit (the two checkpoint types take different load paths into the same
+    update; TorchLean page, "Recovering the state by replay").  1100 and 4096 (batch, head)
+    pairs fill the GPU more than once, 70 tokens need a second retention refresh, r = 0
+    returns the widened checkpoint."""
+    b, h, g, r = shape
+    t = r + 5
+    pr = _seq_problem(b, t, h, 64, 128, g, "bf16", 61)
+    bits = ssm.ssm_checkpoint_sr16(pr["h0"] * 3.0, 9, 1, 0)
+    wide = bits.view(torch.float16).float()
+    y_bits, y_wide = torch.zeros_like(pr["x"]), torch.zeros_like(pr["x"])
+    got = ssm.ssm_replay(bits, pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], 2, r,
+                         y=y_bits)["state"]
+    want = ssm.ssm_replay(wide, pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], 2, r,
+                          y=y_wide)["state"]
+    alone = ssm.ssm_replay(bits, pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], 2, r)["state"]
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    assert torch.equal(alone, want)
+    assert torch.equal(y_bits, y_wide)
+    if r == 0:
+        assert torch.equal(got, wide)
+
+
 def test_sr16_bits_match_oracle(ssm):
     r = np.random.default_rng(5)
     vals = np.concatenate([
