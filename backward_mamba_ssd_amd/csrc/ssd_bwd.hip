@@ -251,9 +251,11 @@ struct __align__(16) BlkSmem {
     // Per-token decay factors of a head, by head parity, computed once per head one phase
     // ahead of their use (instead of an exponential per thread per use): fac[t] for a
     // chunk token t outside block k is the factor that scales its row for the state
-    // products, for t in block k it is exp(Lam_t - Lam_blk0); w[i] = exp(Lam_e - Lam_i)
-    // for the tokens of block k; es = exp(Lam_blk0), ee = exp(Lam_end - Lam_e).
-    float fac[2][kMaxBlk * kLs], w[2][kLs], es[2], ee[2];
+    // products; es = exp(Lam_blk0), ee = exp(Lam_end - Lam_e); w_i = exp(Lam_e - Lam_i).
+    float fac[2][kMaxBlk * kLs], es[2], ee[2];
+    // block k's tokens, by head parity: (exp(Lam_i - Lam_blk0), w_i dt_i, w_i, dt_i), read
+    // as two pairs by the last phase
+    float4 tk[2][kLs];
     uint32_t lanetab[64][8];  // SwzLane of lane l, formed once (6 words and 2 of padding)
 };
 static_assert((kMaxBlk - 1) * kT64 <= 2 * kT128, "scaled rows fit under the state tiles");
@@ -445,8 +447,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             const float lb0 = kS_ >= 0 ? lp[kS_].x : 0.f, le = lp[kE_].x;
             const float2 lt = lp[t];
             if (t >= base_ && t < base_ + kLs) {  // whole waves: block k is 64 aligned tokens
-                sm.fac[par][t] = __expf(lt.x - lb0);
-                sm.w[par][t - base_] = __expf(le - lt.x);
+                const float wt = __expf(le - lt.x);
+                sm.tk[par][t - base_] = make_float4(__expf(lt.x - lb0), wt * lt.y, wt, lt.y);
             } else {
                 sm.fac[par][t] = t < base_ ? __expf(lb0 - lt.x) * lt.y : __expf(lt.x - le);
             }
@@ -742,8 +744,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int i = 16 * (2 * wm + t) + lr;
-            ei_t[t] = sm.fac[par][base + i];
-            wdt_t[t] = sm.w[par][i] * ld[base + i].y;
+            const float2 e = *reinterpret_cast<const float2 *>(&sm.tk[par][i]);
+            ei_t[t] = e.x;
+            wdt_t[t] = e.y;
         }
         // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tile wj) ----
         u16x4 dxo;
@@ -758,7 +761,8 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             for (int kk = 0; kk < 4; ++kk)
                 acc4 = mfma(lds_frag(dHb, swz_row128(sl, wq, kk)), lds_frag(sm.B, swz_row128(sl, wj, kk)), acc4);
             const int j = 16 * wj + lr;
-            const float wjv = sm.w[par][j], dt_j = ld[base + j].y;
+            const float2 wd = *reinterpret_cast<const float2 *>(&sm.tk[par][j].z);
+            const float wjv = wd.x, dt_j = wd.y;
             const uint32_t o = swz_pc64(sl, wj, wq);
             const u16x4 x4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.X) + o);
             const u16x4 y4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.dY) + o);
