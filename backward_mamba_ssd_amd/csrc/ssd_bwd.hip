@@ -307,10 +307,19 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
     const int64_t T = a.T;
     const int64_t cstart = static_cast<int64_t>(c) * a.L;
     const int64_t tk = cstart + static_cast<int64_t>(k) * kLs;
-    if (tk >= T) return;  // uniform for the whole workgroup, before any barrier
+    const int hpg = a.H / a.G;
+    if (tk >= T) {  // uniform for the whole workgroup, before any barrier
+        // a block past the end of the sequence: its heads' dA, dD partials are zero
+        const int hl = static_cast<int>(threadIdx.x);
+        if (hl < hpg) {
+            const int64_t pi = ((static_cast<int64_t>(b) * a.H + g * hpg + hl) * a.nchunks + c) * nb + k;
+            a.pA[pi] = 0.0;
+            a.pD[pi] = 0.0;
+        }
+        return;
+    }
     const int64_t cend = (cstart + a.L < T) ? cstart + a.L : T;
     int nbc = static_cast<int>((cend - cstart + kLs - 1) / kLs);
-    const int hpg = a.H / a.G;
     int kS_ = 64 * k - 1, kE_ = 64 * k + kLs - 1, kEnd_ = 64 * nbc - 1, base_ = 64 * k;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     int wq = wave & 3, wj = wave >> 2, wn = wave & 7, wm = wave >> 3;
@@ -884,13 +893,10 @@ __global__ void __launch_bounds__(64) ssd_bwd_params_kernel(SsdBwdArgs a) {
 }  // namespace
 
 hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipEvent_t ev_begin, hipEvent_t ev_end, hipStream_t s) {
-    // partials of blocks past the end of the sequence stay untouched: clear them
-    const int64_t nparts = a.Bsz * a.H * a.nchunks * (a.L / kLs);
-    hipError_t e = launch_fill(reinterpret_cast<float *>(a.pA), 2 * nparts, 0.f, s);
-    if (e != hipSuccess) return e;
-    e = launch_fill(reinterpret_cast<float *>(a.pD), 2 * nparts, 0.f, s);
-    if (e != hipSuccess) return e;
+    // (every dA, dD partial is written by the per-block kernel, zero for blocks past the end
+    // of the sequence, so the workspace needs no clearing)
     // four 4-wave workgroups per CU when the grid fills the chip that deep, else 8 waves
+    hipError_t e;
     int cus = 0;
     if ((e = device_cu_count(&cus)) != hipSuccess) return e;
     const int64_t nbh = a.Bsz * a.H;
