@@ -523,6 +523,22 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         dCa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         dBa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // Tiles above the diagonal are zero for every head: their Q^T pieces and partial
+    // sums, and the dD partials of the off-diagonal tiles, are written once here (for both
+    // head parities) rather than in every head's Phase I.
+    if (gj > gi) {
+        *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = pack4(0.f, 0.f, 0.f, 0.f);
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if (lane < 16) sm.col[q][16 * gj + lr][gi] = 0.f;
+            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[q][gj][16 * gi + lq]) = f32x4v{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (gj != gi && lane == 0) {
+        sm.dd_sum[0][wave] = 0.f;
+        sm.dd_sum[1][wave] = 0.f;
+    }
     const int kS = kS_;      // chunk-local index of the token before block k
     const int kE = kE_;      // last token of block k
     const int base = base_;
@@ -622,17 +638,9 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         prefetch(hn);  // registers are free once staged
         // ---- S2: Phase I of block k, then the state products over the other blocks ----
         // Phase I: dW = dY X^T, K, R = K G, Q = G M   (i-tile gi, j-tile gj)
-        if (gj > gi) {
-            // above the diagonal every entry is zero: Q^T's tile and the partial sums (the
-            // zero is formed here, not held in registers across the loop)
-            float z = 0.f;
-            asm volatile("" : "+v"(z));
-            *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = pack4(z, z, z, z);
-            if (lane < 16) sm.col[par][16 * gj + lr][gi] = z;
-            typedef float f32x4v __attribute__((ext_vector_type(4)));
-            if (lr == 0) *reinterpret_cast<f32x4v *>(&sm.row[par][gj][16 * gi + lq]) = f32x4v{z, z, z, z};
-            if (lane == 0) sm.dd_sum[par][wave] = z;
-        } else {
+        // (above the diagonal every entry is zero: those tiles' Q^T pieces and partial sums
+        // were written once, before the head loop)
+        if (gj <= gi) {
             f32x4 dW = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -670,9 +678,6 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
                 if (lane == 0) sm.dd_sum[par][wave] = diag;
             } else {
                 entries(false);
-                float z = 0.f;
-                asm volatile("" : "+v"(z));
-                if (lane == 0) sm.dd_sum[par][wave] = z;
             }
             *reinterpret_cast<u16x4 *>(reinterpret_cast<char *>(sm.QT) + swz_pc64(sl, gj, gi)) = pack4(qv[0], qv[1], qv[2], qv[3]);
             colacc = rows4_sum(colacc);
