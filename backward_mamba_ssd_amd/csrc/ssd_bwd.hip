@@ -268,7 +268,7 @@ static_assert(offsetof(BlkSmem, X) == offsetof(BlkSmem, R) + sizeof(BlkSmem::R) 
 // one waits on LDS, an MFMA result or a barrier.  Wave w's tiles (every tile 16 x 16):
 //   Gram / K / Phase I, [i][j]:   i-tile gi, j-tile gj from kGramTiles
 //   state products, [n][p]:       n-tiles 2 wq, 2 wq + 1, p-tile wj
-//   Phase II, [p][j]:             p-tile wq, j-tile wj
+//   Phase II, [p][j]:             p-tile wq, j-tiles 2 wj, 2 wj + 1 (waves 0 .. 7)
 //   Phase III/IV and K, [n][tok]: n-tile wn, token tiles 2 wm, 2 wm + 1
 // Gram tile (i-tile << 2 | j-tile) of wave w in bits 4w .. 4w + 3.  The ten tiles on or
 // below the diagonal carry Phase I's work; wave w runs on SIMD w % 4, and the table gives
@@ -762,40 +762,51 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             ei_t[t] = e.x;
             wdt_t[t] = e.y;
         }
-        // ---- S4: Phase II (dx, ddt direct; p-tile wq, j-tile wj) ----
-        u16x4 dxo;
-        uint32_t dxoff;
-        {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc4 = {0.f, 0.f, 0.f, 0.f};
+        // ---- S4: Phase II (dx, ddt direct) on waves 0..7: p-tile wq, j-tiles 2 wj, 2 wj + 1.
+        // Waves 8..15, the youngest of each SIMD and the last to reach every barrier, go
+        // straight to Phases III/IV; the two j-tiles of a wave share its dy and dH fragments.
+        if (wave < 8) {
+            const int jb = 2 * wj;
+            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            f32x4 acc4[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             // Q[i][j] = 0 for i < j, so the kk block below the diagonal adds zeros
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                acc = mfma(frag_tr64(sm.dY, sl, wq, kk), lds_frag(sm.QT, swz_row64(sl, wj, kk)), acc);
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 fy = frag_tr64(sm.dY, sl, wq, kk);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                acc4 = mfma(lds_frag(dHb, swz_row128(sl, wq, kk)), lds_frag(sm.B, swz_row128(sl, wj, kk)), acc4);
-            const int j = 16 * wj + lr;
-            const float2 wd = *reinterpret_cast<const float2 *>(&sm.tk[par][j].z);
-            const float wjv = wd.x, dt_j = wd.y;
-            const uint32_t o = swz_pc64(sl, wj, wq);
-            const u16x4 x4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.X) + o);
-            const u16x4 y4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.dY) + o);
-            // acc4[j][p] = (dH B_j)[p]: with x it also gives the exit-gradient term
-            // f_j = w_j dt_j x_j.(dH B_j) of dLam (this wave's p-tile)
-            float ddp = 0.f, xb = 0.f, dxv[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float xv = bf16_to_f32(x4[v]);
-                const float pre = fmaf(wjv, acc4[v], acc[v]);
-                ddp = fmaf(xv, pre, ddp);
-                xb = fmaf(xv, acc4[v], xb);
-                dxv[v] = fmaf(Dh, bf16_to_f32(y4[v]), dt_j * pre);
+                for (int t = 0; t < 2; ++t) acc[t] = mfma(fy, lds_frag(sm.QT, swz_row64(sl, jb + t, kk)), acc[t]);
             }
-            dxoff = static_cast<uint32_t>(k * kLs + j) * tokb + (h * kP + 16 * wq + lq) * 2;
-            dxo = pack4(dxv[0], dxv[1], dxv[2], dxv[3]);
-            // both sums over the tile's four lane rows in one pass: row 0 holds dd, row 1 f
-            const float sums = rows4_sum2(ddp, xb * (wjv * dt_j));
-            if (lane < 32) *(lane < 16 ? &sm.dd[j][wq] : &sm.fp[j][wq]) = sums;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 fd = lds_frag(dHb, swz_row128(sl, wq, kk));
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc4[t] = mfma(fd, lds_frag(sm.B, swz_row128(sl, jb + t, kk)), acc4[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int j = 16 * (jb + t) + lr;
+                const float2 wd = *reinterpret_cast<const float2 *>(&sm.tk[par][j].z);
+                const float wjv = wd.x, dt_j = wd.y;
+                const uint32_t o = swz_pc64(sl, jb + t, wq);
+                const u16x4 x4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.X) + o);
+                const u16x4 y4 = *reinterpret_cast<const u16x4 *>(reinterpret_cast<const char *>(sm.dY) + o);
+                // acc4[j][p] = (dH B_j)[p]: with x it also gives the exit-gradient term
+                // f_j = w_j dt_j x_j.(dH B_j) of dLam (this wave's p-tile)
+                float ddp = 0.f, xb = 0.f, dxv[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float xv = bf16_to_f32(x4[v]);
+                    const float pre = fmaf(wjv, acc4[t][v], acc[t][v]);
+                    ddp = fmaf(xv, pre, ddp);
+                    xb = fmaf(xv, acc4[t][v], xb);
+                    dxv[v] = fmaf(Dh, bf16_to_f32(y4[v]), dt_j * pre);
+                }
+                buf_st_8b(rdx, static_cast<uint32_t>(k * kLs + j) * tokb + (h * kP + 16 * wq + lq) * 2,
+                          pack4(dxv[0], dxv[1], dxv[2], dxv[3]));
+                // both sums over the tile's four lane rows in one pass: row 0 holds dd, row 1 f
+                const float sums = rows4_sum2(ddp, xb * (wjv * dt_j));
+                if (lane < 32) *(lane < 16 ? &sm.dd[j][wq] : &sm.fp[j][wq]) = sums;
+            }
         }
         // Phase III / IV: per-head dC, dB contributions (n-tile wn, tok-tiles 2wm, 2wm+1);
         // the state fragments are read once for both token tiles.
@@ -832,7 +843,6 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
             const float os = rows4_sum2(o[0], o[1]);
             if (lane < 32) sm.offin[16 * (2 * wm + (lane >> 4)) + lr][wn] = os;
         }
-        buf_st_8b(rdx, dxoff, dxo);
         __syncthreads();
     }
     // the last head's combine (its partials were published by the final S4 barrier)
