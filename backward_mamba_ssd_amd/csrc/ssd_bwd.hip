@@ -749,7 +749,7 @@ __global__ void __launch_bounds__(kBlkThreads) ssd_bwd_block_kernel(SsdBwdArgs a
         if (wave == 0) scan(hn, par ^ 1);
         __syncthreads();
         // the next head's chunk-boundary state and exit gradient (this head's were consumed
-        // in S3)
+        // by the state products in S2)
         load_states(hn);
         // the next head's decay factors (waves 0..3)
         factors(par ^ 1);
