@@ -40,10 +40,12 @@
 //     to B and C once after the loop.  ddt is complete per block.
 //  3. ssd_bwd_params: dA, dD as fixed-order fp64 sums of per-block partials.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
 #include "ssd_common.hpp"
+
 
 namespace ssm {
 namespace {
@@ -73,20 +75,41 @@ struct __align__(16) DstSmem {
     bf16_t EdY[kLs * kSY];   // [tok][p] = dy[tok][p] * exp(Lam_tok)
     float lam[2][kLs];
 };
+// The small-grid form also stages a chunk's exit gradient here for its store wave.
+struct __align__(16) DstSmemSW {
+    DstSmem s;
+    bf16_t gout[kP * kN];  // one chunk's gradient in the workspace's order
+};
 
 // NW waves per workgroup: 4 when the (batch, head) workgroups fill every CU four deep,
-// 8 for smaller grids (batch 1 at long context), so each CU still runs 16 waves.  Wave w
-// owns n-tiles (8 / NW) w .. (8 / NW) w + 8 / NW - 1 of dH^T and all four p-tiles; every
-// tile sees the same MFMA sequence either way, so the results do not depend on NW.
+// 8 for smaller grids (batch 1 at long context).  Each wave w < NW owns two n-tiles of dH^T
+// and four p-tiles (NW = 4) or two (NW = 8), so its 32-token steps read two C fragments
+// and as many dy fragments as it has p-tiles; every tile sees the same MFMA sequence
+// either way, so the results do not depend on NW.
+//
+// With four workgroups per CU (NW = 4) the other workgroups cover each one's load latency:
+// the rows of one block are loaded ahead and the waves store the chunk-exit gradients
+// themselves.  The small-grid form (NW = 8), alone on its CU, keeps three blocks of rows in
+// flight, and its compute waves issue no stores: loads and stores share one completion
+// counter and complete out of order with respect to each other, so a wave with a store
+// issued after its pending loads can only wait for all of them, which would drain the row
+// queue at every chunk end.  The compute waves put a chunk's gradient in LDS instead, and a
+// ninth wave that issues no loads copies it out.
 template <int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
-    static_assert(NW == 4 || NW == 8, "two n-tiles per wave, or one");
+__global__ void __launch_bounds__(NW == 8 ? 9 * 64 : NW * 64)
+__attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
+    static_assert(NW == 4 || NW == 8, "two n-tiles of four p-tiles per wave, or of two");
     constexpr int kTiles = 32 / NW;  // dH^T tiles per wave
-    constexpr int kNT = 8 / NW;      // n-tiles per wave
-    __shared__ DstSmem sm;
+    constexpr int kPT = kTiles / 2;  // p-tiles per wave (of n-tiles 2 np, 2 np + 1)
+    constexpr bool kSW = (NW == 8);  // a store wave
+    constexpr int DEPTH = kSW ? 3 : 1;  // blocks of rows in flight
+    typedef typename std::conditional<kSW, DstSmemSW, DstSmem>::type Smem;
+    __shared__ Smem smw;
+    DstSmem &sm = *reinterpret_cast<DstSmem *>(&smw);
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool store_wave = kSW && wave == NW;  // uniform per wave
     const int lr = lane & 15, lq = (lane >> 4) * 4;
     const int64_t T = a.T;
     const float Ah = a.A[h];
@@ -94,12 +117,16 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     const bf16_t *Cm = static_cast<const bf16_t *>(a.C);
     constexpr int PN = kP * kN;
 
-    // dH^T accumulators: tile q: nt = kNT w + q/4, pt = q%4; n = 16nt + lq + v, p = 16pt + lr
+    // dH^T accumulators: tile q: n-tile 2 np + q / kPT, p-tile p0 + q % kPT (np = w, p0 = 0
+    // with four waves; np = w / 2, p0 = 2 (w % 2) with eight); n = 16 nt + lq + v, p = 16 pt + lr
+    const int np = (NW == 4) ? wave : wave >> 1, p0 = (NW == 4) ? 0 : 2 * (wave & 1);
+    auto tile_nt = [&](int q) { return 2 * np + q / kPT; };
+    auto tile_pt = [&](int q) { return p0 + q % kPT; };
     f32x4 G[kTiles];
 #pragma unroll
     for (int q = 0; q < kTiles; ++q) {
-        const int n = 16 * (kNT * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
-        if (a.dh_final != nullptr) {
+        const int n = 16 * tile_nt(q) + lq, p = 16 * tile_pt(q) + lr;
+        if (a.dh_final != nullptr && !store_wave) {
             const float4 v = *reinterpret_cast<const float4 *>(a.dh_final + static_cast<int64_t>(bh) * PN + p * kN + n);
             G[q] = f32x4{v.x, v.y, v.z, v.w};
         } else {
@@ -143,26 +170,22 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
     const int nblk = static_cast<int>((T + kLs - 1) / kLs);
     const int bpc = static_cast<int>(a.L / kLs);  // blocks per chunk
     bf16_t *const dst0 = a.dstates + static_cast<int64_t>(bh) * a.nchunks * PN;
-    // one block of the reverse walk; R is refilled with block s - 1 once staged
+    // one block of the reverse walk; R is refilled with block s - DEPTH once staged
     auto step = [&](int s, Rows &R) {
         const int buf = s & 1;
-        if (s == nblk - 1 || (s + 1) % bpc == 0) {
+        if (s >= 0 && (s == nblk - 1 || (s + 1) % bpc == 0)) {
             // gradient on the state leaving chunk c (everything after it), stored by tile
-            // pairs in accumulator lane order (tiles q and q + 4 share a p-tile)
-            bf16_t *dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
-            if constexpr (kNT == 2) {
+            // pairs in accumulator lane order (tiles q and q + kPT share a p-tile); the
+            // small-grid form puts it in LDS in the same order
+            bf16_t *dst;
+            if constexpr (kSW) dst = reinterpret_cast<DstSmemSW &>(smw).gout;
+            else dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const u16x4 lo = pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
-                    const u16x4 hi = pack4(G[q + 4][0], G[q + 4][1], G[q + 4][2], G[q + 4][3]);
-                    const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    *reinterpret_cast<u16x8 *>(dst + dstate_pair(wave, q, lane)) = v;
-                }
-            } else {  // one n-tile per wave: its half of each pair
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<u16x4 *>(dst + dstate_pair(wave >> 1, q, lane) + 4 * (wave & 1)) =
-                        pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
+            for (int q = 0; q < kPT; ++q) {
+                const u16x4 lo = pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
+                const u16x4 hi = pack4(G[q + kPT][0], G[q + kPT][1], G[q + kPT][2], G[q + kPT][3]);
+                const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                *reinterpret_cast<u16x8 *>(dst + dstate_pair(np, tile_pt(q), lane)) = v;
             }
         }
         if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(R.dtr * Ah);
@@ -185,12 +208,19 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
             for (int i = 0; i < kCR; ++i)
                 *reinterpret_cast<u16x8 *>(&sm.C[(ct0 + 4 * NW * i) * kSC + cn0]) = R.cr[i];
         }
-        if (s >= 1) prefetch(R, s - 1);
+        if constexpr (kSW) {
+            // unconditional, so that every pass through the loop issues the same loads (the
+            // last steps re-read block 0)
+            prefetch(R, s >= DEPTH ? s - DEPTH : 0);
+        } else {
+            if (s >= 1) prefetch(R, s - 1);
+        }
         __syncthreads();
+        if (kSW && s < 0) return;  // a padding step (the walk is a whole number of DEPTH steps)
         const float el = __expf(lam_end);
 #pragma unroll
         for (int q = 0; q < kTiles; ++q) {
-            const int nt = kNT * wave + q / 4, pt = q % 4;
+            const int nt = tile_nt(q), pt = tile_pt(q);
             f32x4 acc = G[q];
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] *= el;
@@ -201,13 +231,44 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4,
             G[q] = acc;
         }
     };
-    Rows R;
-    prefetch(R, nblk - 1);
-    for (int s = nblk - 1; s >= 0; --s) step(s, R);
+    // Steps s = nblk - 1 down to send + 1, a whole number of DEPTH steps: those below 0 pad
+    // the last pass (they stage re-read rows and wait at the barriers, nothing else), so
+    // that the loop body is the same on every pass.
+    const int send = nblk - 1 - ((nblk + DEPTH - 1) / DEPTH) * DEPTH;
+    if (store_wave) {
+        // the store wave: the same two barriers per block as the compute waves; at a chunk
+        // end it copies the gradient they staged before the first barrier out to the
+        // workspace, reading it before the second (after which it may be restaged).  A loop
+        // of its own, so that the compute waves' code never follows a store.
+        for (int s = nblk - 1; s > send; --s) {
+            __syncthreads();
+            if (s >= 0 && (s == nblk - 1 || (s + 1) % bpc == 0)) {
+                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<DstSmemSW &>(smw).gout);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(dst0 + static_cast<int64_t>(s / bpc) * PN);
+#pragma unroll 4
+                for (int i = 0; i < PN * 2 / 16 / 64; ++i) dst[64 * i + lane] = src[64 * i + lane];
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    Rows R[DEPTH];
+    if constexpr (kSW) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) prefetch(R[d], nblk - 1 - d >= 0 ? nblk - 1 - d : 0);
+        for (int s = nblk - 1; s > send; s -= DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) step(s - d, R[d]);
+        }
+    } else {
+        prefetch(R[0], nblk - 1);
+        for (int s = nblk - 1; s >= 0; --s) step(s, R[0]);
+    }
     if (a.dh0 != nullptr) {
 #pragma unroll
         for (int q = 0; q < kTiles; ++q) {
-            const int n = 16 * (kNT * wave + q / 4) + lq, p = 16 * (q % 4) + lr;
+            const int n = 16 * tile_nt(q) + lq, p = 16 * tile_pt(q) + lr;
             *reinterpret_cast<float4 *>(a.dh0 + static_cast<int64_t>(bh) * PN + p * kN + n) =
                 make_float4(G[q][0], G[q][1], G[q][2], G[q][3]);
         }
@@ -917,8 +978,8 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipEvent_t ev_begin, hipEvent_t e
     const int64_t nbh = a.Bsz * a.H;
     if (nbh >= 4 * static_cast<int64_t>(cus))
         ssd_bwd_dstate_kernel<4><<<static_cast<unsigned>(nbh), 256, 0, s>>>(a);
-    else
-        ssd_bwd_dstate_kernel<8><<<static_cast<unsigned>(nbh), 512, 0, s>>>(a);
+    else  // eight compute waves and the store wave
+        ssd_bwd_dstate_kernel<8><<<static_cast<unsigned>(nbh), 9 * 64, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nwg = a.Bsz * a.G * a.nchunks * (a.L / kLs);
