@@ -75,10 +75,13 @@ struct __align__(16) DstSmem {
     bf16_t EdY[kLs * kSY];   // [tok][p] = dy[tok][p] * exp(Lam_tok)
     float lam[2][kLs];
 };
-// The small-grid form also stages a chunk's exit gradient here for its store wave.
+// The small-grid form: the staged tiles and the prefix double-buffered by block parity, and
+// a chunk's exit gradient staged for the store wave (by chunk parity).
 struct __align__(16) DstSmemSW {
-    DstSmem s;
-    bf16_t gout[kP * kN];  // one chunk's gradient in the workspace's order
+    bf16_t C[2][kLs * kSC];
+    bf16_t EdY[2][kLs * kSY];
+    float lam[2][kLs];
+    bf16_t gout[2][kP * kN];  // chunk-exit gradients in the workspace's order
 };
 
 // NW waves per workgroup: 4 when the (batch, head) workgroups fill every CU four deep,
@@ -104,8 +107,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_d
     constexpr bool kSW = (NW == 8);  // a store wave
     constexpr int DEPTH = kSW ? 3 : 1;  // blocks of rows in flight
     typedef typename std::conditional<kSW, DstSmemSW, DstSmem>::type Smem;
-    __shared__ Smem smw;
-    DstSmem &sm = *reinterpret_cast<DstSmem *>(&smw);
+    __shared__ Smem sm;
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -157,66 +159,49 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_d
         const uint32_t nv = static_cast<uint32_t>(rem < kLs ? rem : kLs);
         const rsrc_t ry = make_rsrc(dy0 + s * sy, nv * toky);
         const rsrc_t rc = make_rsrc(C0 + s * sc, nv * tokc);
+        const rsrc_t rd = make_rsrc(dt0 + s * sd, nv * a.H * 4u);
+        R.dtr = 0.f;
+        // (the small-grid form uses dt a step before the rows, so it is loaded first there)
+        if (kSW && tid < kLs) R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
 #pragma unroll
         for (int i = 0; i < kYR; ++i) R.yr[i] = buf_ld_16b(ry, (yt0 + 8 * NW * i) * toky + yp0 * 2);
 #pragma unroll
         for (int i = 0; i < kCR; ++i) R.cr[i] = buf_ld_16b(rc, (ct0 + 4 * NW * i) * tokc + cn0 * 2);
-        R.dtr = 0.f;
-        if (tid < kLs) {
-            const rsrc_t rd = make_rsrc(dt0 + s * sd, nv * a.H * 4u);
-            R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
-        }
+        if (!kSW && tid < kLs) R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
     };
     const int nblk = static_cast<int>((T + kLs - 1) / kLs);
     const int bpc = static_cast<int>(a.L / kLs);  // blocks per chunk
     bf16_t *const dst0 = a.dstates + static_cast<int64_t>(bh) * a.nchunks * PN;
-    // one block of the reverse walk; R is refilled with block s - DEPTH once staged
-    auto step = [&](int s, Rows &R) {
-        const int buf = s & 1;
-        if (s >= 0 && (s == nblk - 1 || (s + 1) % bpc == 0)) {
-            // gradient on the state leaving chunk c (everything after it), stored by tile
-            // pairs in accumulator lane order (tiles q and q + kPT share a p-tile); the
-            // small-grid form puts it in LDS in the same order
-            bf16_t *dst;
-            if constexpr (kSW) dst = reinterpret_cast<DstSmemSW &>(smw).gout;
-            else dst = dst0 + static_cast<int64_t>(s / bpc) * PN;
+    // the gradient on the state leaving chunk c (everything after it) by tile pairs in
+    // accumulator lane order (tiles q and q + kPT share a p-tile)
+    auto put_exit_gradient = [&](bf16_t *dst) {
 #pragma unroll
-            for (int q = 0; q < kPT; ++q) {
-                const u16x4 lo = pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
-                const u16x4 hi = pack4(G[q + kPT][0], G[q + kPT][1], G[q + kPT][2], G[q + kPT][3]);
-                const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                *reinterpret_cast<u16x8 *>(dst + dstate_pair(np, tile_pt(q), lane)) = v;
-            }
+        for (int q = 0; q < kPT; ++q) {
+            const u16x4 lo = pack4(G[q][0], G[q][1], G[q][2], G[q][3]);
+            const u16x4 hi = pack4(G[q + kPT][0], G[q + kPT][1], G[q + kPT][2], G[q + kPT][3]);
+            const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<u16x8 *>(dst + dstate_pair(np, tile_pt(q), lane)) = v;
         }
-        if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(R.dtr * Ah);
-        __syncthreads();
-        const float *lam = sm.lam[buf];
-        const float lam_end = lam[kLs - 1];
-        {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    };
+    // dy rows scaled by exp(Lam) and C rows into the given tiles
+    auto stage = [&](const Rows &R, const float *lam, bf16_t *sC, bf16_t *sE) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-            for (int i = 0; i < kYR; ++i) {
-                const float e = __expf(lam[yt0 + 8 * NW * i]);
-                const u16x8 v = R.yr[i];
-                const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * e, bf16_to_f32(v[1]) * e),
-                                 pack2_bf16(bf16_to_f32(v[2]) * e, bf16_to_f32(v[3]) * e),
-                                 pack2_bf16(bf16_to_f32(v[4]) * e, bf16_to_f32(v[5]) * e),
-                                 pack2_bf16(bf16_to_f32(v[6]) * e, bf16_to_f32(v[7]) * e)};
-                *reinterpret_cast<u32x4 *>(&sm.EdY[(yt0 + 8 * NW * i) * kSY + yp0]) = w;
-            }
+        for (int i = 0; i < kYR; ++i) {
+            const float e = __expf(lam[yt0 + 8 * NW * i]);
+            const u16x8 v = R.yr[i];
+            const u32x4 w = {pack2_bf16(bf16_to_f32(v[0]) * e, bf16_to_f32(v[1]) * e),
+                             pack2_bf16(bf16_to_f32(v[2]) * e, bf16_to_f32(v[3]) * e),
+                             pack2_bf16(bf16_to_f32(v[4]) * e, bf16_to_f32(v[5]) * e),
+                             pack2_bf16(bf16_to_f32(v[6]) * e, bf16_to_f32(v[7]) * e)};
+            *reinterpret_cast<u32x4 *>(&sE[(yt0 + 8 * NW * i) * kSY + yp0]) = w;
+        }
 #pragma unroll
-            for (int i = 0; i < kCR; ++i)
-                *reinterpret_cast<u16x8 *>(&sm.C[(ct0 + 4 * NW * i) * kSC + cn0]) = R.cr[i];
-        }
-        if constexpr (kSW) {
-            // unconditional, so that every pass through the loop issues the same loads (the
-            // last steps re-read block 0)
-            prefetch(R, s >= DEPTH ? s - DEPTH : 0);
-        } else {
-            if (s >= 1) prefetch(R, s - 1);
-        }
-        __syncthreads();
-        if (kSW && s < 0) return;  // a padding step (the walk is a whole number of DEPTH steps)
+        for (int i = 0; i < kCR; ++i)
+            *reinterpret_cast<u16x8 *>(&sC[(ct0 + 4 * NW * i) * kSC + cn0]) = R.cr[i];
+    };
+    // dH^T = exp(Lam_63) dH^T + C^T (exp(Lam) dy) over the staged block
+    auto products = [&](const bf16_t *sC, const bf16_t *sE, float lam_end) {
         const float el = __expf(lam_end);
 #pragma unroll
         for (int q = 0; q < kTiles; ++q) {
@@ -226,44 +211,78 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_d
             for (int v = 0; v < 4; ++v) acc[v] *= el;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                acc = mfma(frag_tr(sm.C, kSC, 16 * nt, 32 * kk, lane),
-                           frag_tr(sm.EdY, kSY, 16 * pt, 32 * kk, lane), acc);
+                acc = mfma(frag_tr(sC, kSC, 16 * nt, 32 * kk, lane), frag_tr(sE, kSY, 16 * pt, 32 * kk, lane), acc);
             G[q] = acc;
         }
     };
-    // Steps s = nblk - 1 down to send + 1, a whole number of DEPTH steps: those below 0 pad
-    // the last pass (they stage re-read rows and wait at the barriers, nothing else), so
-    // that the loop body is the same on every pass.
-    const int send = nblk - 1 - ((nblk + DEPTH - 1) / DEPTH) * DEPTH;
-    if (store_wave) {
-        // the store wave: the same two barriers per block as the compute waves; at a chunk
-        // end it copies the gradient they staged before the first barrier out to the
-        // workspace, reading it before the second (after which it may be restaged).  A loop
-        // of its own, so that the compute waves' code never follows a store.
-        for (int s = nblk - 1; s > send; --s) {
+    auto chunk_end = [&](int s) { return s >= 0 && (s == nblk - 1 || (s + 1) % bpc == 0); };
+    if constexpr (!kSW) {
+        // two barriers per block: the prefix of block s, then its staged rows
+        auto step = [&](int s, Rows &R) {
+            const int buf = s & 1;
+            if (chunk_end(s)) put_exit_gradient(dst0 + static_cast<int64_t>(s / bpc) * PN);
+            if (wave == 0) sm.lam[buf][lane] = wave_prefix_sum(R.dtr * Ah);
             __syncthreads();
-            if (s >= 0 && (s == nblk - 1 || (s + 1) % bpc == 0)) {
-                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<DstSmemSW &>(smw).gout);
-                u32x4 *dst = reinterpret_cast<u32x4 *>(dst0 + static_cast<int64_t>(s / bpc) * PN);
+            stage(R, sm.lam[buf], sm.C, sm.EdY);
+            const float lam_end = sm.lam[buf][kLs - 1];
+            if (s >= 1) prefetch(R, s - 1);
+            __syncthreads();
+            products(sm.C, sm.EdY, lam_end);
+        };
+        Rows R;
+        prefetch(R, nblk - 1);
+        for (int s = nblk - 1; s >= 0; --s) step(s, R);
+    } else {
+        // One barrier per block.  Before it: block s's rows are staged into the tiles of its
+        // parity (the prefix Lam of block s was formed one step earlier), wave 0 forms block
+        // s - 1's prefix from the queued rows, and a chunk's exit gradient is put in LDS for
+        // the store wave; after it: the products of block s.  A tile pair, a prefix or a
+        // gradient buffer is rewritten two steps after the barrier that published it, after
+        // the next barrier, which every wave reaches only once done with it.
+        //
+        // Steps s = nblk - 1 down to send + 1, a whole number of DEPTH steps: those below 0
+        // pad the last pass (they stage re-read rows and wait at the barrier, nothing else),
+        // so that the loop body, and the loads it issues, are the same on every pass.
+        const int send = nblk - 1 - ((nblk + DEPTH - 1) / DEPTH) * DEPTH;
+        if (store_wave) {
+            // the store wave: the same barriers; at a chunk end it copies the gradient out to
+            // the workspace.  A loop of its own, so that the compute waves' code never
+            // follows a store.
+            __syncthreads();
+            for (int s = nblk - 1; s > send; --s) {
+                __syncthreads();
+                if (chunk_end(s)) {
+                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                    const u32x4 *src = reinterpret_cast<const u32x4 *>(sm.gout[(s / bpc) & 1]);
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(dst0 + static_cast<int64_t>(s / bpc) * PN);
 #pragma unroll 4
-                for (int i = 0; i < PN * 2 / 16 / 64; ++i) dst[64 * i + lane] = src[64 * i + lane];
+                    for (int i = 0; i < PN * 2 / 16 / 64; ++i) dst[64 * i + lane] = src[64 * i + lane];
+                }
             }
-            __syncthreads();
+            return;
         }
-        return;
-    }
-    Rows R[DEPTH];
-    if constexpr (kSW) {
+        // R refilled with block s - DEPTH once staged; Rn holds block s - 1
+        auto step = [&](int s, Rows &R, const Rows &Rn) {
+            const int buf = s & 1;
+            if (chunk_end(s)) put_exit_gradient(sm.gout[(s / bpc) & 1]);
+            stage(R, sm.lam[buf], sm.C[buf], sm.EdY[buf]);
+            const float lam_end = sm.lam[buf][kLs - 1];
+            if (wave == 0) sm.lam[buf ^ 1][lane] = wave_prefix_sum(Rn.dtr * Ah);
+            // unconditional, so that every pass issues the same loads (the last steps re-read
+            // block 0)
+            prefetch(R, s >= DEPTH ? s - DEPTH : 0);
+            __syncthreads();
+            if (s >= 0) products(sm.C[buf], sm.EdY[buf], lam_end);
+        };
+        Rows R[DEPTH];
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) prefetch(R[d], nblk - 1 - d >= 0 ? nblk - 1 - d : 0);
+        if (wave == 0) sm.lam[(nblk - 1) & 1][lane] = wave_prefix_sum(R[0].dtr * Ah);
+        __syncthreads();
         for (int s = nblk - 1; s > send; s -= DEPTH) {
 #pragma unroll
-            for (int d = 0; d < DEPTH; ++d) step(s - d, R[d]);
+            for (int d = 0; d < DEPTH; ++d) step(s - d, R[d], R[(d + 1) % DEPTH]);
         }
-    } else {
-        prefetch(R[0], nblk - 1);
-        for (int s = nblk - 1; s >= 0; --s) step(s, R[0]);
     }
     if (a.dh0 != nullptr) {
 #pragma unroll
