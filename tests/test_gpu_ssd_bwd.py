@@ -81,14 +81,19 @@ def test_backward_deterministic(ssm):
         assert torch.equal(g1[k], g2[k]), k
 
 
-def test_batch_slices_are_independent(ssm):
+@pytest.mark.parametrize("t,L", [(320, 128), (64, 64), (130, 64), (200, 256)])
+def test_batch_slices_are_independent(ssm, t, L):
     # Every (batch, head) is computed by its own workgroups, so each batch run alone gives
-    # the same bits as the batched run.  With 256 heads the batch-4 reverse pass fills an
-    # MI355X four deep and takes its 4-wave form, while a batch of 1 takes the 8-wave
-    # form: this also checks that the two forms agree bit for bit.  (dA and dD sum over
-    # the batch, so only their batch-summed values are compared, at tolerance.)
-    b, t, h, p, n, g, L = 4, 320, 256, 64, 128, 8, 128
-    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 41, dev, h0="randn", dh_final=True)
+    # the same bits as the batched run.  With 256 heads the batch-4 forward and reverse
+    # pass fill an MI355X two and four deep and take their batch forms, while a batch of 1
+    # takes the small-grid forms: this also checks that the forms agree bit for bit.  The
+    # shapes cover the small-grid reverse pass's edges: a walk that is not a whole number
+    # of its three-block passes (5, 3 and 4 blocks are padded by 1, 0 and 2 steps), one
+    # block, a chunk end at every block (chunk 64), several chunk ends and ragged last
+    # chunks.  (dA and dD sum over the batch, so only their batch-summed values are
+    # compared, at tolerance.)
+    b, h, p, n, g = 4, 256, 64, 128, 8
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 41 + t, dev, h0="randn", dh_final=True)
     assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
     y, hf, cs, gr = _run(ssm, pr, L)
     dA = torch.zeros_like(gr["dA"], dtype=torch.float64)
