@@ -75,13 +75,11 @@ struct __align__(16) DstSmem {
     bf16_t EdY[kLs * kSY];   // [tok][p] = dy[tok][p] * exp(Lam_tok)
     float lam[2][kLs];
 };
-// The small-grid form: the staged tiles and the prefix double-buffered by block parity, and
-// a chunk's exit gradient staged for the store wave (by chunk parity).
-struct __align__(16) DstSmemSW {
+// The small-grid form: the staged tiles and the prefix double-buffered by block parity.
+struct __align__(16) DstSmem2 {
     bf16_t C[2][kLs * kSC];
     bf16_t EdY[2][kLs * kSY];
     float lam[2][kLs];
-    bf16_t gout[2][kP * kN];  // chunk-exit gradients in the workspace's order
 };
 
 // NW waves per workgroup: 4 when the (batch, head) workgroups fill every CU four deep,
@@ -90,28 +88,22 @@ struct __align__(16) DstSmemSW {
 // and as many dy fragments as it has p-tiles; every tile sees the same MFMA sequence
 // either way, so the results do not depend on NW.
 //
-// With four workgroups per CU (NW = 4) the other workgroups cover each one's load latency:
-// the rows of one block are loaded ahead and the waves store the chunk-exit gradients
-// themselves.  The small-grid form (NW = 8), alone on its CU, keeps three blocks of rows in
-// flight, and its compute waves issue no stores: loads and stores share one completion
-// counter and complete out of order with respect to each other, so a wave with a store
-// issued after its pending loads can only wait for all of them, which would drain the row
-// queue at every chunk end.  The compute waves put a chunk's gradient in LDS instead, and a
-// ninth wave that issues no loads copies it out.
+// With four workgroups per CU (NW = 4) the other workgroups cover each one's load latency
+// and the rows of one block are loaded ahead.  The small-grid form (NW = 8), alone on its
+// CU, keeps three blocks of rows in flight and runs one barrier per block (kSmall below).
 template <int NW>
-__global__ void __launch_bounds__(NW == 8 ? 9 * 64 : NW * 64)
-__attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 2, NW == 4 ? 4 : 2))) ssd_bwd_dstate_kernel(SsdBwdArgs a) {
     static_assert(NW == 4 || NW == 8, "two n-tiles of four p-tiles per wave, or of two");
     constexpr int kTiles = 32 / NW;  // dH^T tiles per wave
     constexpr int kPT = kTiles / 2;  // p-tiles per wave (of n-tiles 2 np, 2 np + 1)
-    constexpr bool kSW = (NW == 8);  // a store wave
-    constexpr int DEPTH = kSW ? 3 : 1;  // blocks of rows in flight
-    typedef typename std::conditional<kSW, DstSmemSW, DstSmem>::type Smem;
+    constexpr bool kSmall = (NW == 8);
+    constexpr int DEPTH = kSmall ? 3 : 1;  // blocks of rows in flight
+    typedef typename std::conditional<kSmall, DstSmem2, DstSmem>::type Smem;
     __shared__ Smem sm;
     const int bh = xcd_remap(blockIdx.x, gridDim.x);
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const bool store_wave = kSW && wave == NW;  // uniform per wave
     const int lr = lane & 15, lq = (lane >> 4) * 4;
     const int64_t T = a.T;
     const float Ah = a.A[h];
@@ -128,7 +120,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_d
 #pragma unroll
     for (int q = 0; q < kTiles; ++q) {
         const int n = 16 * tile_nt(q) + lq, p = 16 * tile_pt(q) + lr;
-        if (a.dh_final != nullptr && !store_wave) {
+        if (a.dh_final != nullptr) {
             const float4 v = *reinterpret_cast<const float4 *>(a.dh_final + static_cast<int64_t>(bh) * PN + p * kN + n);
             G[q] = f32x4{v.x, v.y, v.z, v.w};
         } else {
@@ -162,12 +154,12 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_d
         const rsrc_t rd = make_rsrc(dt0 + s * sd, nv * a.H * 4u);
         R.dtr = 0.f;
         // (the small-grid form uses dt a step before the rows, so it is loaded first there)
-        if (kSW && tid < kLs) R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
+        if (kSmall && tid < kLs) R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
 #pragma unroll
         for (int i = 0; i < kYR; ++i) R.yr[i] = buf_ld_16b(ry, (yt0 + 8 * NW * i) * toky + yp0 * 2);
 #pragma unroll
         for (int i = 0; i < kCR; ++i) R.cr[i] = buf_ld_16b(rc, (ct0 + 4 * NW * i) * tokc + cn0 * 2);
-        if (!kSW && tid < kLs) R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
+        if (!kSmall && tid < kLs) R.dtr = buf_ld_f32(rd, static_cast<uint32_t>(tid) * a.H * 4u);
     };
     const int nblk = static_cast<int>((T + kLs - 1) / kLs);
     const int bpc = static_cast<int>(a.L / kLs);  // blocks per chunk
@@ -216,7 +208,7 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_d
         }
     };
     auto chunk_end = [&](int s) { return s >= 0 && (s == nblk - 1 || (s + 1) % bpc == 0); };
-    if constexpr (!kSW) {
+    if constexpr (!kSmall) {
         // two barriers per block: the prefix of block s, then its staged rows
         auto step = [&](int s, Rows &R) {
             const int buf = s & 1;
@@ -234,37 +226,23 @@ __attribute__((amdgpu_waves_per_eu(NW == 4 ? 4 : 3, NW == 4 ? 4 : 3))) ssd_bwd_d
         for (int s = nblk - 1; s >= 0; --s) step(s, R);
     } else {
         // One barrier per block.  Before it: block s's rows are staged into the tiles of its
-        // parity (the prefix Lam of block s was formed one step earlier), wave 0 forms block
-        // s - 1's prefix from the queued rows, and a chunk's exit gradient is put in LDS for
-        // the store wave; after it: the products of block s.  A tile pair, a prefix or a
-        // gradient buffer is rewritten two steps after the barrier that published it, after
-        // the next barrier, which every wave reaches only once done with it.
+        // parity (the prefix Lam of block s was formed one step earlier) and wave 0 forms
+        // block s - 1's prefix from the queued rows; after it: the products of block s.  A
+        // tile pair or a prefix is rewritten two steps after the barrier that published it,
+        // after the next barrier, which every wave reaches only once done with it.
         //
-        // Steps s = nblk - 1 down to send + 1, a whole number of DEPTH steps: those below 0
-        // pad the last pass (they stage re-read rows and wait at the barrier, nothing else),
-        // so that the loop body, and the loads it issues, are the same on every pass.
+        // The waits on the queued rows count exactly only if every path through the loop
+        // issues the same loads: with the last prefetches skipped, or a pass of the unrolled
+        // loop cut short, the compiler can no longer tell how many loads are still pending
+        // behind a block's rows and waits for all of them, which drains the queue.  So the
+        // prefetch is unconditional (the last steps re-read block 0) and the walk runs steps
+        // s = nblk - 1 down to send + 1, a whole number of DEPTH steps: those below 0 pad the
+        // last pass (they stage re-read rows and wait at the barrier, nothing else).
         const int send = nblk - 1 - ((nblk + DEPTH - 1) / DEPTH) * DEPTH;
-        if (store_wave) {
-            // the store wave: the same barriers; at a chunk end it copies the gradient out to
-            // the workspace.  A loop of its own, so that the compute waves' code never
-            // follows a store.
-            __syncthreads();
-            for (int s = nblk - 1; s > send; --s) {
-                __syncthreads();
-                if (chunk_end(s)) {
-                    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-                    const u32x4 *src = reinterpret_cast<const u32x4 *>(sm.gout[(s / bpc) & 1]);
-                    u32x4 *dst = reinterpret_cast<u32x4 *>(dst0 + static_cast<int64_t>(s / bpc) * PN);
-#pragma unroll 4
-                    for (int i = 0; i < PN * 2 / 16 / 64; ++i) dst[64 * i + lane] = src[64 * i + lane];
-                }
-            }
-            return;
-        }
         // R refilled with block s - DEPTH once staged; Rn holds block s - 1
         auto step = [&](int s, Rows &R, const Rows &Rn) {
             const int buf = s & 1;
-            if (chunk_end(s)) put_exit_gradient(sm.gout[(s / bpc) & 1]);
+            if (chunk_end(s)) put_exit_gradient(dst0 + static_cast<int64_t>(s / bpc) * PN);
             stage(R, sm.lam[buf], sm.C[buf], sm.EdY[buf]);
             const float lam_end = sm.lam[buf][kLs - 1];
             if (wave == 0) sm.lam[buf ^ 1][lane] = wave_prefix_sum(Rn.dtr * Ah);
@@ -997,8 +975,8 @@ hipError_t launch_ssd_bwd(const SsdBwdArgs &a, hipEvent_t ev_begin, hipEvent_t e
     const int64_t nbh = a.Bsz * a.H;
     if (nbh >= 4 * static_cast<int64_t>(cus))
         ssd_bwd_dstate_kernel<4><<<static_cast<unsigned>(nbh), 256, 0, s>>>(a);
-    else  // eight compute waves and the store wave
-        ssd_bwd_dstate_kernel<8><<<static_cast<unsigned>(nbh), 9 * 64, 0, s>>>(a);
+    else
+        ssd_bwd_dstate_kernel<8><<<static_cast<unsigned>(nbh), 512, 0, s>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nwg = a.Bsz * a.G * a.nchunks * (a.L / kLs);
