@@ -560,6 +560,47 @@ def long_context_rates(dev):
     return lc
 
 
+def fwd_inference_rates(dev):
+    """The chunked forward in inference form on the prefill workload: outputs and the
+    final state only, no chunk-boundary states saved (70,656 B per token at the head
+    shape: x, y, B, C, dt)."""
+    import statistics
+
+    import torch
+
+    from backward_mamba_ssd_amd import inputs, ssm
+
+    w = inputs.WORKLOADS["prefill_b4_t4096"]
+    pr = inputs.make_workload_problem(w, dev, with_dy=False)
+    b, t, h, p = pr["x"].shape
+    n = pr["B"].shape[3]
+    y = torch.empty_like(pr["x"])
+    hf = torch.empty((b, h, p, n), dtype=torch.float32, device=dev)
+
+    def run():
+        ssm.ssm_fwd_chunked(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], chunk=w.chunk,
+                            h_final=hf, chunk_states=None, y=y)
+
+    for _ in range(10):  # also brings the clocks up when the section runs alone
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(20)]
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev)
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    nbytes = (2 * H * P + 2 * H * P + 2 * 2 * G * N + 4 * H) * b * t + 4 * b * H * P * N
+    e = path_entry(fwd_flops_per_token(w) * b * t, nbytes, ms)
+    e["tokens_per_s"] = round(b * t / (ms * 1e-3), 1)
+    e["workload"] = w.name
+    del pr, y, hf
+    torch.cuda.empty_cache()
+    return e
+
+
 def copy_calibration(dev):
     """Three plain 1 GiB device-to-device copies: the known-size reference that scales
     the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of a profiled run."""
@@ -578,6 +619,7 @@ def copy_calibration(dev):
 
 
 SECTIONS = {
+    "fwd_inference": fwd_inference_rates,
     "decode": decode_rates,
     "dt_prep": dt_prep_rates,
     "draft_rollback": draft_rollback_rates,

@@ -133,3 +133,20 @@ def test_forward_at_the_ends_of_the_retention_range(ssm, case):
     assert_close("y", y, ref["y"], 2e-2)
     assert_close("h_final", hf, ref["h_final"], 2e-2)
     assert_close("chunk_states", cs, ref["chunk_states"], 2e-2)
+
+
+def test_inference_form_equals_training_form(ssm):
+    """Leaving out the saved chunk states (inference) or the final state changes no other
+    output: y and h_final are bit-identical to the call that saves everything."""
+    b, t, h, p, n, g = 2, 333, 8, 64, 128, 2
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 21, dev, h0="randn")
+    _assert_mfma(ssm, pr, 128)
+    args = (pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"])
+    y, hf, cs = ssm.ssm_fwd_chunked(*args, h0=pr["h0"], chunk=128)
+    y1, hf1, cs1 = ssm.ssm_fwd_chunked(*args, h0=pr["h0"], chunk=128, chunk_states=None)
+    y2, hf2, cs2 = ssm.ssm_fwd_chunked(*args, h0=pr["h0"], chunk=128, chunk_states=None,
+                                       h_final=None)
+    torch.cuda.synchronize()
+    assert cs1 is None and cs2 is None and hf2 is None
+    assert torch.equal(y1, y) and torch.equal(y2, y)
+    assert torch.equal(hf1, hf)
