@@ -203,3 +203,30 @@ def test_backward_at_the_ends_of_the_retention_range(ssm, case):
     torch.cuda.synchronize()
     for k in GRADS:
         assert_close(k, gr[k], ref[k], 2e-2)
+
+
+def test_sixty_four_heads_per_group(ssm):
+    # the widest group the MFMA backward takes: 64 heads share B and C, so the per-block
+    # kernel's head loop and its per-head A, D reads span a whole wave
+    b, t, h, p, n, g, L = 1, 200, 64, 64, 128, 1, 128
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 77, dev, h0="randn", dh_final=True)
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
+    _, _, _, gr = _run(ssm, pr, L)
+    ref = oracle.bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], pr["dy"],
+                     h0=pr["h0"], dh_final=pr["dh_final"])
+    torch.cuda.synchronize()
+    for k in GRADS:
+        assert_close(k, gr[k], ref[k], 2e-2)
+
+
+def test_no_tokens_at_the_mfma_shape(ssm):
+    # T = 0 at the MFMA head shape: the final state is the initial state, dh0 is
+    # dh_final, and the parameter gradients are zero
+    b, h, p, n, g = 2, 8, 64, 128, 2
+    pr = inputs.make_problem(b, 0, h, p, n, g, "bf16", 78, dev, h0="randn", dh_final=True)
+    y, hf, cs, gr = _run(ssm, pr, 256)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and cs.numel() == 0
+    assert torch.equal(hf, pr["h0"])
+    assert torch.equal(gr["dh0"], pr["dh_final"])
+    assert float(gr["dA"].abs().max()) == 0.0 and float(gr["dD"].abs().max()) == 0.0
