@@ -230,3 +230,22 @@ def test_no_tokens_at_the_mfma_shape(ssm):
     assert torch.equal(hf, pr["h0"])
     assert torch.equal(gr["dh0"], pr["dh_final"])
     assert float(gr["dA"].abs().max()) == 0.0 and float(gr["dD"].abs().max()) == 0.0
+
+
+def test_grids_that_are_not_a_multiple_of_the_xcd_count(ssm):
+    # 3 sequences x 6 heads in 3 groups: 18 forward and reverse-pass workgroups and 27
+    # per-block workgroups, none a multiple of 8, so the workgroup ids are used as they come
+    b, t, h, p, n, g, L = 3, 130, 6, 64, 128, 3, 64
+    pr = inputs.make_problem(b, t, h, p, n, g, "bf16", 79, dev, h0="randn", dh_final=True)
+    assert ssm.ssm_uses_mfma_path(ssm.dims_of(pr["x"], pr["B"], L), ssm.SSM_BF16)
+    y, hf, cs, gr = _run(ssm, pr, L)
+    rf = oracle.fwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], h0=pr["h0"], chunk=L,
+                    want_chunk_states=True)
+    rb = oracle.bwd(pr["x"], pr["B"], pr["C"], pr["dt"], pr["A"], pr["D"], pr["dy"],
+                    h0=pr["h0"], dh_final=pr["dh_final"])
+    torch.cuda.synchronize()
+    assert_close("y", y, rf["y"], 2e-2)
+    assert_close("h_final", hf, rf["h_final"], 2e-2)
+    assert_close("chunk_states", cs, rf["chunk_states"], 2e-2)
+    for k in GRADS:
+        assert_close(k, gr[k], rb[k], 2e-2)
